@@ -1,0 +1,283 @@
+"""Plain CPU oracle of the sigmoid-routed mixture-of-experts FFN (Kimi K2 / DeepSeek-V3 style).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or run this
+module: only the tests, the smoke check in ``__graft_entry__`` and the CPU-baseline leg
+of ``bench.py`` use it.  It shares no code with the HIP library and imports nothing
+from it; it takes plain numpy arrays (any float dtype) and computes in float64.
+
+Sources (the pages this follows; cited by page title and the part of the page):
+
+* "Kimi K2 · Transformer blocks" (atlas.klimoza.dev, MoE transformer block), the
+  mixture-of-experts equations:
+      z = x_ffn W_r ;  s = sigma(z) ;  E_sel_i = [ i in top_8(s + b) ] ;
+      G_i = 2.827 s_i E_sel_i / sum_j s_j E_sel_j ;
+      g = x W1 ; u = x W3 ; a = g sigma(g) ; h = a (.) u ; E_i = h W2 ;
+      y_routed = sum_{i=1..384} G_i E_i ; y_shared = same SwiGLU with the shared
+      expert's weights ; Delta_ffn = y_routed + y_shared,
+  and the table "Exact per-instance accounting" (MoE parameters 16,958,226,816).
+* "nnterp encyclopedia · kimi_k2", section "The mixture of experts" (selection on
+  sigmoid plus a selection bias, every expert a candidate, gates are the chosen
+  sigmoids without the bias, renormalised and multiplied by 2.827) and section
+  "Config" (384 experts, 8 per token, moe_intermediate_size 2048, one shared expert,
+  routed_scaling_factor 2.827, norm_topk_prob true, n_group = topk_group = 1).
+* "Kimi K3 · Latent up-projection", the printed moe_infer: count tokens per expert,
+  group the (token, slot) pairs by expert, run each expert on its group, put the
+  outputs back in slot order and take the weighted sum over the k slots in fp32.
+
+Readings where the pages are silent (each also listed in the design doc):
+
+* Weights are stored [out, in] (the K3 page states this for its projection); so
+  ``w_r`` is [E, d], ``w1``/``w3`` are [E, I, d], ``w2`` is [E, d, I].
+* Top-k tie-break: the lower expert index wins.
+* The selection is a floating-point decision, so it is taken in the precision the
+  kernel takes it in (fp32): z rounded to fp32, s = sigma(z) rounded to fp32, the
+  score s + b rounded to fp32.  All values (gates, FFN, sums) are float64.
+* The bias enters only the selection, added to sigma(z), never to z and never to G.
+* No epsilon in the renormalising denominator (the denominator is > 0).
+* RMSNorm (latent variant only): u / sqrt(mean(u^2) + eps) with unit gain.
+
+Parity pins: see tests/test_oracle_pins.py.  The output values themselves have no
+worked example on the pages ("parity unpinned" beyond the invariants and closed
+forms the pins check).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ALPHA_K2 = 2.827
+
+
+# ----------------------------------------------------------------------------- shapes
+def moe_param_shapes(d_model, n_experts, d_expert, d_shared, n_shared=1):
+    """Shapes of every learned array one MoE block holds, [out, in] storage.
+
+    "Kimi K2 · Transformer blocks", parameter table: the mixture of experts counts the
+    384 routed SwiGLU experts, the shared expert, the router matrix and the selection
+    bias (one value per expert).  Nothing else (no router bias term)."""
+    shapes = {
+        "w_r": (n_experts, d_model),
+        "b": (n_experts,),
+        "w1": (n_experts, d_expert, d_model),
+        "w3": (n_experts, d_expert, d_model),
+        "w2": (n_experts, d_model, d_expert),
+    }
+    if n_shared:
+        i_s = d_shared * n_shared
+        shapes.update({"ws1": (i_s, d_model), "ws3": (i_s, d_model), "ws2": (d_model, i_s)})
+    return shapes
+
+
+def moe_param_count(**kw):
+    return int(sum(math.prod(s) for s in moe_param_shapes(**kw).values()))
+
+
+# ------------------------------------------------------------------------ primitives
+def sigmoid(v):
+    """sigma(v) = 1 / (1 + exp(-v)), float64; the K2 page's s = sigma(z) and a = g sigma(g)."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    pos = v >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-v[pos]))
+    e = np.exp(v[~pos])            # stable form for negative arguments
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def silu(v):
+    """a = g sigma(g) (K2 page, expert equations; the config's hidden_act 'silu')."""
+    v = np.asarray(v, dtype=np.float64)
+    return v * sigmoid(v)
+
+
+def rmsnorm(u, eps=1e-6):
+    """RMSNorm with unit gain: u / sqrt(mean(u^2) + eps), per row (latent variant)."""
+    u = np.asarray(u, dtype=np.float64)
+    return u / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------- router
+def route(x, w_r, b, top_k, alpha=ALPHA_K2):
+    """Router: z = x W_r^T, s = sigma(z), top-k of (s + b), gates alpha * s / sum(s).
+
+    "Kimi K2 · Transformer blocks", MoE equations z, s, E_sel, G_i;
+    "nnterp encyclopedia · kimi_k2", "The mixture of experts" (bias only in the choice,
+    all 384 experts candidates since n_group = 1).
+
+    Returns a dict:
+      z        [T, E] float64 logits
+      s        [T, E] float64 sigmoid scores
+      score32  [T, E] float32 decision scores fl32(fl32(sigma(fl32(z))) + b)
+      topk_idx [T, k] int32   selected experts, descending score, ties to lower index
+      topk_w   [T, k] float64 gates G (same order)
+      gap      [T]    float64 score32 of the k-th pick minus that of the (k+1)-th
+                      (+inf when k == E): tokens with a tiny gap can flip under rounding
+    """
+    x = _f64(x)
+    w_r = _f64(w_r)
+    b = np.asarray(b, dtype=np.float32)
+    T = x.shape[0]
+    E = w_r.shape[0]
+    if not (1 <= top_k <= E):
+        raise ValueError("top_k must be in [1, E]")
+    z = x @ w_r.T                                  # library matmul as the GEMM step
+    s = sigmoid(z)
+    # decision precision: fp32, as the kernel takes it
+    z32 = z.astype(np.float32)
+    s32 = sigmoid(z32.astype(np.float64)).astype(np.float32)
+    score32 = (s32.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
+    # order experts by (score descending, index ascending)
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((idx, -score32.astype(np.float64)), axis=-1)
+    sel = order[:, :top_k].astype(np.int32)
+    if top_k < E:
+        kth = np.take_along_axis(score32, order[:, top_k - 1:top_k], axis=1)[:, 0]
+        nxt = np.take_along_axis(score32, order[:, top_k:top_k + 1], axis=1)[:, 0]
+        gap = kth.astype(np.float64) - nxt.astype(np.float64)
+    else:
+        gap = np.full(T, np.inf)
+    s_sel = np.take_along_axis(s, sel, axis=1)
+    den = s_sel.sum(axis=1, keepdims=True)
+    assert np.all(den > 0.0), "renormalising denominator must be positive"
+    gates = alpha * s_sel / den
+    return {"z": z, "s": s, "score32": score32, "topk_idx": sel, "topk_w": gates, "gap": gap}
+
+
+def gate_matrix(topk_idx, topk_w, n_experts):
+    """Dense G [T, E]: G_i on the selected experts, 0 elsewhere (the K2 page's G_i)."""
+    T = topk_idx.shape[0]
+    G = np.zeros((T, n_experts), dtype=np.float64)
+    np.put_along_axis(G, np.asarray(topk_idx, dtype=np.int64), _f64(topk_w), axis=1)
+    return G
+
+
+# --------------------------------------------------------------------------- permute
+def permute(topk_idx, n_experts):
+    """Group the T*k (token, slot) pairs by expert.
+
+    "Kimi K3 · Latent up-projection", moe_infer: tokens per expert, the flat slots sorted
+    by expert, each expert's rows a contiguous segment starting at the running sum.
+    Order inside a segment is not fixed by the page; the oracle's is token ascending.
+
+    Returns counts [E], offsets [E+1] (exclusive scan), perm [T*k] (perm[p] = t*k + slot
+    of the p-th grouped row) and inv [T*k] (inv[t*k + slot] = its grouped row).
+    """
+    flat = np.asarray(topk_idx, dtype=np.int64).reshape(-1)
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for e in flat:                                 # plain histogram
+        counts[e] += 1
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    for e in range(n_experts):                     # exclusive scan
+        offsets[e + 1] = offsets[e] + counts[e]
+    fill = offsets[:-1].copy()
+    perm = np.empty(flat.size, dtype=np.int64)
+    inv = np.empty(flat.size, dtype=np.int64)
+    for j, e in enumerate(flat):                   # stable scatter, token ascending
+        perm[fill[e]] = j
+        inv[j] = fill[e]
+        fill[e] += 1
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            perm.astype(np.int32), inv.astype(np.int32))
+
+
+# ------------------------------------------------------------------------------- FFN
+def swiglu(x_rows, w1, w3, w2):
+    """One SwiGLU expert on a set of rows: g = x W1, u = x W3, a = g sigma(g), h = a u,
+    E = h W2 ("Kimi K2 · Transformer blocks", expert and shared-expert equations).
+    Weights [out, in]; float64 throughout."""
+    x_rows = _f64(x_rows)
+    g = x_rows @ _f64(w1).T
+    u = x_rows @ _f64(w3).T
+    h = silu(g) * u
+    return h @ _f64(w2).T
+
+
+def _expert_getter(w1, w3, w2):
+    return lambda e: (w1[e], w3[e], w2[e])
+
+
+def moe_dense(x, w_r, b, w1, w3, w2, ws1, ws3, ws2, top_k, alpha=ALPHA_K2):
+    """Delta_ffn by the page's dense definition: every expert runs on every token and
+    y_routed = sum over all E experts (ascending) of G_i E_i; small inputs only.
+    Returns dict with route outputs, y_routed, y_shared, out (all float64)."""
+    r = route(x, w_r, b, top_k, alpha)
+    E = _f64(w_r).shape[0]
+    G = gate_matrix(r["topk_idx"], r["topk_w"], E)
+    y_r = np.zeros((x.shape[0], np.shape(w2)[1]), dtype=np.float64)
+    for e in range(E):
+        y_r = y_r + G[:, e:e + 1] * swiglu(x, w1[e], w3[e], w2[e])
+    y_s = swiglu(x, ws1, ws3, ws2) if ws1 is not None else np.zeros_like(y_r)
+    return dict(r, y_routed=y_r, y_shared=y_s, out=y_r + y_s)
+
+
+def moe_sparse(x, w_r, b, top_k, alpha=ALPHA_K2, *, get_expert=None, w1=None, w3=None,
+               w2=None, shared=None, tokens=None, routing=None):
+    """Delta_ffn computed only through the k selected experts of each token.
+
+    Follows the grouping of the K3 page's moe_infer (rows grouped by expert, each
+    expert run once on its rows, outputs put back per slot) and the K2 page's sum
+    y_routed = sum_i G_i E_i taken over the selected experts in ascending expert order.
+
+    get_expert(e) -> (w1_e, w3_e, w2_e) lets a caller hand over one expert at a time
+    (large shapes); shared = (ws1, ws3, ws2) or None.  tokens: optional list of token
+    rows to evaluate (sampled check); routing: a precomputed route() result.
+    """
+    if get_expert is None:
+        get_expert = _expert_getter(w1, w3, w2)
+    r = routing if routing is not None else route(x, w_r, b, top_k, alpha)
+    x = np.asarray(x)
+    T = x.shape[0]
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    sel = r["topk_idx"][rows]
+    gates = r["topk_w"][rows]
+    # group the (row, slot) pairs by expert
+    by_expert: dict[int, list[tuple[int, int]]] = {}
+    for i in range(rows.size):
+        for j in range(sel.shape[1]):
+            by_expert.setdefault(int(sel[i, j]), []).append((i, j))
+    per_slot: dict[tuple[int, int], np.ndarray] = {}
+    for e in sorted(by_expert):
+        pairs = by_expert[e]
+        w1e, w3e, w2e = get_expert(e)
+        out_e = swiglu(x[rows[[i for i, _ in pairs]]], w1e, w3e, w2e)
+        for n, pr in enumerate(pairs):
+            per_slot[pr] = out_e[n]
+    d = next(iter(per_slot.values())).shape[0] if per_slot else _f64(w_r).shape[1]
+    y_r = np.zeros((rows.size, d), dtype=np.float64)
+    for i in range(rows.size):
+        for j in np.argsort(sel[i], kind="stable"):          # ascending expert index
+            y_r[i] = y_r[i] + gates[i, j] * per_slot[(i, int(j))]
+    if shared is not None:
+        y_s = swiglu(x[rows], *shared)
+    else:
+        y_s = np.zeros_like(y_r)
+    return dict(r, rows=rows, y_routed=y_r, y_shared=y_s, out=y_r + y_s)
+
+
+# ------------------------------------------------------------------ latent variant
+def moe_latent(x, w_r, b, w_down, w1, w3, w2, w_up, ws1, ws3, ws2, top_k,
+               alpha=ALPHA_K2, eps=1e-6, tokens=None, get_expert=None):
+    """Latent mixture of experts ("Kimi K3 · Latent up-projection", the printed forward):
+    the router scores the full-width input; the input is projected down to the latent
+    width; the selected latent experts run and are gate-weighted and summed; the sum is
+    RMS-normalised and projected back up (y_routed = u_hat W_up); the shared expert
+    runs on the full-width input and is added."""
+    r = route(x, w_r, b, top_k, alpha)
+    x64 = _f64(x)
+    rows = np.arange(x64.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    lat = x64[rows] @ _f64(w_down).T
+    if get_expert is None:
+        get_expert = _expert_getter(w1, w3, w2)
+    sub = {k: v[rows] for k, v in r.items() if isinstance(v, np.ndarray) and v.shape[:1] == (x64.shape[0],)}
+    sparse = moe_sparse(lat, w_r, b, top_k, alpha, get_expert=get_expert, shared=None,
+                        routing=sub)
+    u_hat = rmsnorm(sparse["y_routed"], eps)
+    y_r = u_hat @ _f64(w_up).T
+    y_s = swiglu(x64[rows], ws1, ws3, ws2)
+    return dict(r, rows=rows, latent=lat, y_latent=sparse["y_routed"], y_routed=y_r,
+                y_shared=y_s, out=y_r + y_s)
