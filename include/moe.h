@@ -1,0 +1,151 @@
+/*
+ * moe.h — C ABI of the sigmoid-routed mixture-of-experts FFN layer for MI355X (gfx950).
+ *
+ * One layer of the Kimi K2 / DeepSeek-V3 mixture of experts, as the equations of
+ * "Kimi K2 · Transformer blocks" (MoE transformer block, "Mixture of experts") give it:
+ *
+ *   z = x W_r^T                       router logits            [T, E]
+ *   s = sigmoid(z)                    scores
+ *   sel(t) = top_k(s + b)             selection on biased scores (bias only here)
+ *   G_i = alpha * s_i / sum_{j in sel} s_j   on sel(t), 0 elsewhere (alpha = 2.827 on K2)
+ *   E_i = (silu(x W1_i^T) * (x W3_i^T)) W2_i^T   SwiGLU expert
+ *   y_routed = sum_i G_i E_i ;  y_shared = same SwiGLU with the shared expert's weights
+ *   out = y_routed + y_shared
+ *
+ * and the routing notes of "nnterp encyclopedia · kimi_k2" ("The mixture of experts":
+ * every expert a candidate, gates are the chosen sigmoids without the bias, renormalised
+ * and scaled so they sum to alpha at every token).
+ *
+ * Conventions for every entry point
+ *   - All array pointers are DEVICE pointers; `dims` is a host pointer.  bf16 arrays are
+ *     passed as uint16_t bit patterns (bfloat16, round-to-nearest-even).
+ *   - Matrices are row-major and stored [out, in] (the input dimension contiguous):
+ *       x      [T, d]       bf16        w_router [E, d]    fp32     bias [E] fp32
+ *       w1, w3 [E, I, d]    bf16        w2       [E, d, I] bf16
+ *       ws1, ws3 [Is, d]    bf16        ws2      [d, Is]   bf16     (shared expert)
+ *   - Row p of the "grouped" order: the T*k (token, slot) pairs sorted by expert, expert 0
+ *     first; inside an expert's segment tokens ascend.  Slot id = t*k + slot.
+ *   - The caller owns all memory.  The library allocates nothing, keeps no state between
+ *     calls and never synchronises the host; all work is queued on `stream` (a
+ *     hipStream_t; NULL = the default stream).  Concurrent calls need their own workspace.
+ *   - Every output is fully overwritten.  tokens == 0 is a valid no-op.
+ *   - Errors are status codes, checked on the host BEFORE anything is launched:
+ *       MOE_EINVAL       null / misaligned (16 B) pointer, impossible dims
+ *       MOE_EUNSUPPORTED dims this build does not handle (d, I not multiples of 64,
+ *                        top_k > 8, E > 1024, Is not 0 or I)
+ *       MOE_EWORKSPACE   ws_bytes smaller than moe_workspace_bytes()
+ *       MOE_EHIP         a kernel launch failed (device faults surface at the caller's
+ *                        next synchronisation, as usual for asynchronous work)
+ *   - Deterministic: the same inputs give bit-identical outputs (no float atomics).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layer shape.  K2: d_model 7168, n_experts 384, top_k 8, d_expert 2048, d_shared 2048,
+ * routed_scale 2.827 ("nnterp encyclopedia · kimi_k2", section "Config"). */
+typedef struct moe_dims {
+  int64_t tokens;      /* T >= 0 (batch x positions flattened: the layer is per token) */
+  int32_t d_model;     /* d, multiple of 64 */
+  int32_t n_experts;   /* E in [1, 1024] */
+  int32_t top_k;       /* k in [1, min(8, E)] */
+  int32_t d_expert;    /* I, multiple of 64 */
+  int32_t d_shared;    /* Is: 0 (no shared expert) or equal to d_expert */
+  float routed_scale;  /* alpha, finite */
+} moe_dims;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,
+  MOE_EUNSUPPORTED = 2,
+  MOE_EWORKSPACE = 3,
+  MOE_EHIP = 4
+} moe_status;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(int status);
+
+/* Bytes of device workspace every entry point below accepts for these dims (one size
+ * serves them all).  Host only; launches nothing. */
+moe_status moe_workspace_bytes(const moe_dims* dims, size_t* bytes);
+
+/* Router ("Kimi K2 · Transformer blocks", MoE equations z, s, E_sel, G_i).
+ *   topk_idx [T, k] int32  chosen experts per token, descending biased score, ties to
+ *                          the lower expert index
+ *   topk_w   [T, k] fp32   gates alpha * s / sum(s over the chosen), same order
+ *   logits   [T, E] fp32   z, or NULL (then kept in the workspace)
+ * z is accumulated in fp32 from the bf16 x and fp32 w_router; the selection compares
+ * fp32 scores fl(sigmoid(z) + b). */
+moe_status moe_route(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Token permutation ("Kimi K3 · Latent up-projection", moe_infer: count tokens per
+ * expert, group the slots by expert, each expert's rows a contiguous segment).
+ *   counts   [E]    int32  rows per expert
+ *   offsets  [E+1]  int32  exclusive scan of counts (offsets[E] = number of valid slots)
+ *   perm_rows[T*k]  int32  perm_rows[p] = slot id (t*k + slot) of grouped row p
+ *   inv_perm [T*k]  int32  inv_perm[t*k + slot] = its grouped row
+ * Entries of topk_idx outside [0, E), or repeating an earlier slot of the same token,
+ * are dropped: not counted, inv_perm = -1, and the tail perm_rows[offsets[E]..T*k) = -1.
+ */
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_rows, int32_t* inv_perm, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Expert gate/up projections with the SwiGLU product fused in the epilogue
+ * ("Kimi K2 · Transformer blocks", g = x W1, u = x W3, a = g sigma(g), h = a (.) u).
+ *   h [(T*k + Ts), I] bf16: rows 0..T*k-1 in grouped order (row p reads token
+ *     perm_rows[p] / k of x through expert e with offsets[e] <= p < offsets[e+1]), then,
+ *     if the shared expert is present (d_shared > 0, ws1/ws3 non-NULL), Ts = T rows of
+ *     the shared expert for tokens 0..T-1.  Rows p >= offsets[E] of the routed block are
+ *     left untouched.  g, u are fp32 accumulations of bf16 products; h is rounded to bf16. */
+moe_status moe_expert_gate_up(const moe_dims* dims, const uint16_t* x, const int32_t* perm_rows,
+                              const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                              const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Expert down projections ("Kimi K2 · Transformer blocks", E_i = h W2; y_shared = h W2).
+ *   h as produced by moe_expert_gate_up;
+ *   y_routed [T*k, d] bf16 grouped order (rows >= offsets[E] untouched);
+ *   y_shared [T, d]   bf16 (NULL iff no shared expert).  fp32 accumulation, bf16 store. */
+moe_status moe_expert_down(const moe_dims* dims, const uint16_t* h, const int32_t* offsets,
+                           const uint16_t* w2, const uint16_t* ws2, uint16_t* y_routed,
+                           uint16_t* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_expert_gate_up followed by moe_expert_down, h kept in the workspace. */
+moe_status moe_expert_ffn(const moe_dims* dims, const uint16_t* x, const int32_t* perm_rows,
+                          const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                          const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
+                          const uint16_t* ws2, uint16_t* y_routed, uint16_t* y_shared,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine plus shared expert ("Kimi K2 · Transformer blocks", y_routed =
+ * sum_i G_i E_i and Delta_ffn = y_routed + y_shared; the fp32 weighted sum over the k
+ * slots of "Kimi K3 · Latent up-projection", moe_infer):
+ *   out[t] = bf16( sum_{slot} topk_w[t, slot] * y_routed[inv_perm[t*k + slot]] + y_shared[t] )
+ * summed in fp32 in slot order, one rounding to bf16.  inv_perm = -1 slots add nothing;
+ * y_shared may be NULL. */
+moe_status moe_combine(const moe_dims* dims, const uint16_t* y_routed, const int32_t* inv_perm,
+                       const float* topk_w, const uint16_t* y_shared, uint16_t* out,
+                       void* stream);
+
+/* The whole layer: route, permute, gate/up, down, combine; out [T, d] bf16.
+ * Shared expert used iff d_shared > 0 (then ws1, ws3, ws2 must be non-NULL). */
+moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                       const float* bias, const uint16_t* w1, const uint16_t* w3,
+                       const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
+                       const uint16_t* ws2, uint16_t* out, void* ws, size_t ws_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

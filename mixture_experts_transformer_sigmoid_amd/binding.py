@@ -1,0 +1,160 @@
+"""Thin ctypes binding of libmoe (include/moe.h): argument marshalling only.
+
+Every function has the C entry point's name and argument order; tensors are passed as
+device pointers, the stream defaults to torch's current stream.  All arithmetic runs
+in the library's HIP kernels; there is no fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+
+# every exported symbol of include/moe.h
+EXPORTS = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
+           "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_combine",
+           "moe_forward")
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("d_model", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_expert", ctypes.c_int32), ("d_shared", ctypes.c_int32),
+                ("routed_scale", ctypes.c_float)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_S = ctypes.c_size_t
+
+
+def lib():
+    """Load libmoe.so (after torch, so both share one HIP runtime).  Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmoe.so not built ({LIB_PATH}); run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    st = ctypes.c_int
+    D = ctypes.POINTER(MoeDims)
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_status_str.argtypes = [ctypes.c_int]
+    sig = {
+        "moe_workspace_bytes": [D, ctypes.POINTER(ctypes.c_size_t)],
+        "moe_route": [D, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+        "moe_permute": [D, _P, _P, _P, _P, _P, _P, _S, _P],
+        "moe_expert_gate_up": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+        "moe_expert_down": [D, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+        "moe_expert_ffn": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+        "moe_combine": [D, _P, _P, _P, _P, _P, _P],
+        "moe_forward": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.restype = st
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def _check(rc):
+    if rc != MOE_OK:
+        raise MoeError(rc, status_str(rc))
+
+
+def moe_dims(tokens, d_model, n_experts, top_k, d_expert, d_shared, routed_scale=2.827):
+    return MoeDims(int(tokens), int(d_model), int(n_experts), int(top_k), int(d_expert),
+                   int(d_shared), float(routed_scale))
+
+
+def dims_for(cfg: dict, tokens=None) -> MoeDims:
+    """moe_dims from a config dict (keys as in synth_inputs.CONFIGS)."""
+    return moe_dims(cfg["tokens"] if tokens is None else tokens, cfg["d_model"], cfg["n_experts"],
+                    cfg["top_k"], cfg["d_expert"], cfg["d_shared"], cfg.get("routed_scale", 2.827))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def moe_workspace_bytes(dims: MoeDims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def workspace(dims: MoeDims, device="cuda") -> torch.Tensor:
+    """A device buffer of moe_workspace_bytes(dims) bytes (torch owns the memory)."""
+    return torch.empty(max(moe_workspace_bytes(dims), 256), dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
+
+
+def moe_route(dims, x, w_router, bias, topk_idx, topk_w, logits=None, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_idx),
+                           _ptr(topk_w), _ptr(logits), wp, wn, _stream(stream)))
+
+
+def moe_permute(dims, topk_idx, counts, offsets, perm_rows, inv_perm, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_permute(ctypes.byref(dims), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                             _ptr(perm_rows), _ptr(inv_perm), wp, wn, _stream(stream)))
+
+
+def moe_expert_gate_up(dims, x, perm_rows, offsets, w1, w3, ws1, ws3, h, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_expert_gate_up(ctypes.byref(dims), _ptr(x), _ptr(perm_rows), _ptr(offsets),
+                                    _ptr(w1), _ptr(w3), _ptr(ws1), _ptr(ws3), _ptr(h), wp, wn,
+                                    _stream(stream)))
+
+
+def moe_expert_down(dims, h, offsets, w2, ws2, y_routed, y_shared, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_expert_down(ctypes.byref(dims), _ptr(h), _ptr(offsets), _ptr(w2), _ptr(ws2),
+                                 _ptr(y_routed), _ptr(y_shared), wp, wn, _stream(stream)))
+
+
+def moe_expert_ffn(dims, x, perm_rows, offsets, w1, w3, w2, ws1, ws3, ws2, y_routed, y_shared, ws,
+                   stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_expert_ffn(ctypes.byref(dims), _ptr(x), _ptr(perm_rows), _ptr(offsets),
+                                _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2),
+                                _ptr(y_routed), _ptr(y_shared), wp, wn, _stream(stream)))
+
+
+def moe_combine(dims, y_routed, inv_perm, topk_w, y_shared, out, stream=None):
+    _check(lib().moe_combine(ctypes.byref(dims), _ptr(y_routed), _ptr(inv_perm), _ptr(topk_w),
+                             _ptr(y_shared), _ptr(out), _stream(stream)))
+
+
+def moe_forward(dims, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_forward(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w1),
+                             _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out), wp,
+                             wn, _stream(stream)))

@@ -1,0 +1,91 @@
+// Device helpers and launcher declarations shared by the HIP sources of libmoe.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 16x16x32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 1024;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// C(16x16, fp32) += A(16x32) * B(32x16), bf16 operands.
+// Lane l supplies row (l & 15) of A and column (l & 15) of B, each with the 8
+// consecutive k values 8*(l >> 4) .. +7; it receives C rows 4*(l >> 4) .. +3 of column
+// (l & 15).  Any k assignment works as long as A and B use the same one.
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+}  // namespace moe
+
+// ---------------------------------------------------------------- launchers (host)
+// Each returns hipSuccess or the launch error; arguments are pre-validated by moe_abi.
+namespace moe {
+
+struct Tile {
+  int32_t group;      // expert index, or E for the shared expert
+  int32_t row_begin;  // first row (grouped order; shared rows start at T*k)
+  int32_t row_end;    // one past the last row
+  int32_t pad;
+};
+
+hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
+                         int E, int k, float alpha, float* logits, int32_t* topk_idx,
+                         float* topk_w, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* hist,
+                          int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm,
+                          int32_t* inv, hipStream_t s);
+int64_t permute_blocks(int64_t T);
+
+struct FfnShape {
+  int64_t T;    // tokens
+  int d;        // model width
+  int E;        // routed experts
+  int k;        // slots per token
+  int I;        // expert intermediate width
+  bool shared;  // shared expert present (Is == I)
+};
+
+int64_t ffn_max_tiles(const FfnShape& sh);
+
+hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
+                          const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                          const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, Tile* tiles,
+                          int32_t* ntiles, hipStream_t s);
+
+hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
+                       const uint16_t* w2, const uint16_t* ws2, uint16_t* y_routed,
+                       uint16_t* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* y_routed, const int32_t* inv, const float* topk_w,
+                          const uint16_t* y_shared, uint16_t* out, int64_t T, int d, int k,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,284 @@
+// C ABI of libmoe: argument checks, workspace layout and the launch sequence.
+// Every check runs on the host before the first launch; nothing here synchronises.
+#include <math.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace {
+
+using moe::FfnShape;
+using moe::Tile;
+
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool aligned(const void* p, size_t a) { return p != nullptr && ((uintptr_t)p % a) == 0; }
+
+bool has_shared(const moe_dims& d) { return d.d_shared > 0; }
+
+moe_status check_dims(const moe_dims* dp) {
+  if (dp == nullptr) return MOE_EINVAL;
+  const moe_dims& d = *dp;
+  if (d.tokens < 0 || d.d_model <= 0 || d.n_experts <= 0 || d.top_k <= 0 || d.d_expert <= 0 ||
+      d.d_shared < 0)
+    return MOE_EINVAL;
+  if (d.top_k > d.n_experts) return MOE_EINVAL;
+  if (!isfinite(d.routed_scale)) return MOE_EINVAL;
+  if (d.top_k > moe::kMaxTopK || d.n_experts > moe::kMaxExperts) return MOE_EUNSUPPORTED;
+  if (d.d_model % 64 != 0 || d.d_expert % 64 != 0) return MOE_EUNSUPPORTED;
+  if (d.d_shared != 0 && d.d_shared != d.d_expert) return MOE_EUNSUPPORTED;
+  // grouped rows (T*k routed + T shared) are indexed with int32
+  if (d.tokens > (int64_t)(INT32_MAX / 2) / (d.top_k + 1)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t z, idx, w, counts, offsets, perm, inv, hist, base, tiles, ntiles, h, y, total;
+};
+
+Layout layout(const moe_dims& d) {
+  const size_t T = (size_t)d.tokens, E = (size_t)d.n_experts, k = (size_t)d.top_k;
+  const size_t slots = T * k;
+  const size_t rows = slots + (has_shared(d) ? T : 0);
+  const size_t nb = (size_t)moe::permute_blocks(d.tokens);
+  FfnShape sh{d.tokens, d.d_model, d.n_experts, d.top_k, d.d_expert, has_shared(d)};
+  const size_t max_tiles = (size_t)moe::ffn_max_tiles(sh);
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L.z = take(T * E * 4);
+  L.idx = take(slots * 4);
+  L.w = take(slots * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(slots * 4);
+  L.inv = take(slots * 4);
+  L.hist = take(nb * E * 4);
+  L.base = take(nb * E * 4);
+  L.tiles = take(max_tiles * sizeof(Tile));
+  L.ntiles = take(4);
+  L.h = take(rows * (size_t)d.d_expert * 2);
+  L.y = take(rows * (size_t)d.d_model * 2);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status check_ws(const moe_dims& d, const void* ws, size_t ws_bytes) {
+  if (!aligned(ws, kWsAlign)) return MOE_EINVAL;
+  if (ws_bytes < layout(d).total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+FfnShape ffn_shape(const moe_dims& d) {
+  return FfnShape{d.tokens, d.d_model, d.n_experts, d.top_k, d.d_expert, has_shared(d)};
+}
+
+#define MOE_TRY(expr)                 \
+  do {                                \
+    const moe_status st_ = (expr);    \
+    if (st_ != MOE_OK) return st_;    \
+  } while (0)
+
+#define MOE_NEED(cond)                  \
+  do {                                  \
+    if (!(cond)) return MOE_EINVAL;     \
+  } while (0)
+
+moe_status route_impl(const moe_dims& d, const uint16_t* x, const float* w_r, const float* b,
+                      int32_t* idx, float* w, float* logits, hipStream_t s) {
+  return hip_status(moe::launch_router(x, w_r, b, d.tokens, d.d_model, d.n_experts, d.top_k,
+                                       d.routed_scale, logits, idx, w, s));
+}
+
+moe_status permute_impl(const moe_dims& d, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* inv, void* ws, hipStream_t s) {
+  const Layout L = layout(d);
+  return hip_status(moe::launch_permute(idx, d.tokens, d.n_experts, d.top_k,
+                                        at<int32_t>(ws, L.hist), at<int32_t>(ws, L.base), counts,
+                                        offsets, perm, inv, s));
+}
+
+moe_status gate_up_impl(const moe_dims& d, const uint16_t* x, const int32_t* perm,
+                        const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                        const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, void* ws,
+                        hipStream_t s) {
+  const Layout L = layout(d);
+  return hip_status(moe::launch_gate_up(ffn_shape(d), x, perm, offsets, w1, w3, ws1, ws3, h,
+                                        at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles), s));
+}
+
+moe_status down_impl(const moe_dims& d, const uint16_t* h, const int32_t* offsets,
+                     const uint16_t* w2, const uint16_t* ws2, uint16_t* y_routed,
+                     uint16_t* y_shared, void* ws, hipStream_t s) {
+  const Layout L = layout(d);
+  return hip_status(moe::launch_down(ffn_shape(d), h, offsets, w2, ws2, y_routed, y_shared,
+                                     at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles), s));
+}
+
+moe_status combine_impl(const moe_dims& d, const uint16_t* y_routed, const int32_t* inv,
+                        const float* w, const uint16_t* y_shared, uint16_t* out, hipStream_t s) {
+  return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, out, d.tokens, d.d_model,
+                                        d.top_k, s));
+}
+
+bool shared_ptrs_ok(const moe_dims& d, const void* a, const void* b) {
+  return has_shared(d) ? (aligned(a, 16) && aligned(b, 16)) : true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument (null or misaligned pointer, bad dims)";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: dims not handled by this build";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace smaller than moe_workspace_bytes()";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch error";
+    default: return "unknown moe_status";
+  }
+}
+
+moe_status moe_workspace_bytes(const moe_dims* dims, size_t* bytes) {
+  MOE_TRY(check_dims(dims));
+  MOE_NEED(bytes != nullptr);
+  *bytes = layout(*dims).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                     size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x, 16) && aligned(w_router, 16) && aligned(bias, 4));
+  MOE_NEED(aligned(topk_idx, 4) && aligned(topk_w, 4));
+  if (logits == nullptr) {
+    MOE_TRY(check_ws(d, ws, ws_bytes));
+    logits = at<float>(ws, layout(d).z);
+  } else {
+    MOE_NEED(aligned(logits, 4));
+  }
+  (void)hipGetLastError();
+  return route_impl(d, x, w_router, bias, topk_idx, topk_w, logits, (hipStream_t)stream);
+}
+
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_rows, int32_t* inv_perm, void* ws,
+                       size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  MOE_NEED(aligned(counts, 4) && aligned(offsets, 4));
+  if (d.tokens > 0) MOE_NEED(aligned(topk_idx, 4) && aligned(perm_rows, 4) && aligned(inv_perm, 4));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  (void)hipGetLastError();
+  return permute_impl(d, topk_idx, counts, offsets, perm_rows, inv_perm, ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_gate_up(const moe_dims* dims, const uint16_t* x, const int32_t* perm_rows,
+                              const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                              const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, void* ws,
+                              size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x, 16) && aligned(perm_rows, 4) && aligned(offsets, 4));
+  MOE_NEED(aligned(w1, 16) && aligned(w3, 16) && aligned(h, 16));
+  MOE_NEED(shared_ptrs_ok(d, ws1, ws3));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  (void)hipGetLastError();
+  return gate_up_impl(d, x, perm_rows, offsets, w1, w3, ws1, ws3, h, ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_down(const moe_dims* dims, const uint16_t* h, const int32_t* offsets,
+                           const uint16_t* w2, const uint16_t* ws2, uint16_t* y_routed,
+                           uint16_t* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(h, 16) && aligned(offsets, 4) && aligned(w2, 16) && aligned(y_routed, 16));
+  MOE_NEED(shared_ptrs_ok(d, ws2, y_shared));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  (void)hipGetLastError();
+  return down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn(const moe_dims* dims, const uint16_t* x, const int32_t* perm_rows,
+                          const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                          const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
+                          const uint16_t* ws2, uint16_t* y_routed, uint16_t* y_shared, void* ws,
+                          size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x, 16) && aligned(perm_rows, 4) && aligned(offsets, 4));
+  MOE_NEED(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(y_routed, 16));
+  MOE_NEED(shared_ptrs_ok(d, ws1, ws3) && shared_ptrs_ok(d, ws2, y_shared));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  (void)hipGetLastError();
+  const hipStream_t s = (hipStream_t)stream;
+  uint16_t* h = at<uint16_t>(ws, layout(d).h);
+  MOE_TRY(gate_up_impl(d, x, perm_rows, offsets, w1, w3, ws1, ws3, h, ws, s));
+  return down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s);
+}
+
+moe_status moe_combine(const moe_dims* dims, const uint16_t* y_routed, const int32_t* inv_perm,
+                       const float* topk_w, const uint16_t* y_shared, uint16_t* out,
+                       void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(y_routed, 16) && aligned(inv_perm, 4) && aligned(topk_w, 4) && aligned(out, 16));
+  if (y_shared != nullptr) MOE_NEED(aligned(y_shared, 16));
+  (void)hipGetLastError();
+  return combine_impl(d, y_routed, inv_perm, topk_w, y_shared, out, (hipStream_t)stream);
+}
+
+moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                       const float* bias, const uint16_t* w1, const uint16_t* w3,
+                       const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
+                       const uint16_t* ws2, uint16_t* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x, 16) && aligned(w_router, 16) && aligned(bias, 4));
+  MOE_NEED(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(out, 16));
+  if (has_shared(d)) MOE_NEED(aligned(ws1, 16) && aligned(ws3, 16) && aligned(ws2, 16));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  (void)hipGetLastError();
+  const hipStream_t s = (hipStream_t)stream;
+  const Layout L = layout(d);
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* w = at<float>(ws, L.w);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  uint16_t* y_routed = at<uint16_t>(ws, L.y);
+  uint16_t* y_shared =
+      has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
+  MOE_TRY(route_impl(d, x, w_router, bias, idx, w, at<float>(ws, L.z), s));
+  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s));
+  MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s));
+  MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s));
+  return combine_impl(d, y_routed, inv, w, y_shared, out, s);
+}
+
+}  // extern "C"

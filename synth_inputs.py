@@ -90,30 +90,43 @@ def bias(cfg, device, seed=0):
     raise ValueError(kind)
 
 
-def make_inputs(cfg, device="cpu", seed=0, shared=True):
-    """Return the layer's inputs for a config dict (or a CONFIGS name)."""
+def make_weights(cfg, device="cpu", seed=0, shared=True):
+    """The layer's learned arrays (router, bias excluded) for a config dict or name."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
-    T, d, E = cfg["tokens"], cfg["d_model"], cfg["n_experts"]
+    d, E = cfg["d_model"], cfg["n_experts"]
     I, Is = cfg["d_expert"], cfg["d_shared"]
     L = cfg.get("d_latent")
     w = L if L else d                       # the width the routed experts read
-    inp = {
-        "x": normal((T, d), 1.0, torch.bfloat16, device, seed, TID["x"]),
+    out = {
         "w_r": normal((E, d), 1.0 / math.sqrt(d), torch.float32, device, seed, TID["w_r"]),
-        "b": bias(cfg, device, seed),
         "w1": _stacked(E, (I, w), 1.0 / math.sqrt(w), device, seed, TID["w1"]),
         "w3": _stacked(E, (I, w), 1.0 / math.sqrt(w), device, seed, TID["w3"]),
         "w2": _stacked(E, (w, I), 1.0 / math.sqrt(I), device, seed, TID["w2"]),
     }
     if shared and Is:
-        inp["ws1"] = normal((Is, d), 1.0 / math.sqrt(d), torch.bfloat16, device, seed, TID["ws1"])
-        inp["ws3"] = normal((Is, d), 1.0 / math.sqrt(d), torch.bfloat16, device, seed, TID["ws3"])
-        inp["ws2"] = normal((d, Is), 1.0 / math.sqrt(Is), torch.bfloat16, device, seed, TID["ws2"])
+        out["ws1"] = normal((Is, d), 1.0 / math.sqrt(d), torch.bfloat16, device, seed, TID["ws1"])
+        out["ws3"] = normal((Is, d), 1.0 / math.sqrt(d), torch.bfloat16, device, seed, TID["ws3"])
+        out["ws2"] = normal((d, Is), 1.0 / math.sqrt(Is), torch.bfloat16, device, seed, TID["ws2"])
     if L:
-        inp["w_down"] = normal((L, d), 1.0 / math.sqrt(d), torch.bfloat16, device, seed, TID["w_down"])
-        inp["w_up"] = normal((d, L), 1.0 / math.sqrt(L), torch.bfloat16, device, seed, TID["w_up"])
-    return inp
+        out["w_down"] = normal((L, d), 1.0 / math.sqrt(d), torch.bfloat16, device, seed, TID["w_down"])
+        out["w_up"] = normal((d, L), 1.0 / math.sqrt(L), torch.bfloat16, device, seed, TID["w_up"])
+    return out
+
+
+def make_activations(cfg, device="cpu", seed=0):
+    """The token batch x and the selection bias b for a config dict or name."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    return {"x": normal((cfg["tokens"], cfg["d_model"]), 1.0, torch.bfloat16, device, seed, TID["x"]),
+            "b": bias(cfg, device, seed)}
+
+
+def make_inputs(cfg, device="cpu", seed=0, shared=True):
+    """All inputs of the layer for a config dict (or a CONFIGS name)."""
+    out = make_weights(cfg, device, seed, shared)
+    out.update(make_activations(cfg, device, seed))
+    return out
 
 
 def with_overrides(name, **kw):

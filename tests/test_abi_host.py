@@ -1,0 +1,115 @@
+"""Host-side checks of libmoe's C ABI (no GPU): the library loads, exports every entry
+point include/moe.h declares, and rejects bad arguments before launching anything.
+
+Every call here is built to fail a host-side check, so no kernel is ever queued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_transformer_sigmoid_amd as M
+from mixture_experts_transformer_sigmoid_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = M.lib()
+    names = _declared()
+    assert "moe_forward" in names and "moe_route" in names and len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_status_strings():
+    for code in range(5):
+        assert M.status_str(code).startswith("MOE_")
+    assert "unknown" in M.status_str(99)
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(B.MoeDims) == 32
+    assert B.MoeDims.routed_scale.offset == 28
+
+
+def _k2(T=128):
+    return M.moe_dims(T, 7168, 384, 8, 2048, 2048, 2.827)
+
+
+def test_workspace_bytes_grow_with_tokens():
+    a = M.moe_workspace_bytes(_k2(128))
+    b = M.moe_workspace_bytes(_k2(8192))
+    assert 0 < a < b
+    # holds at least the h and y buffers of the grouped rows
+    assert b >= 8192 * 9 * (2048 + 7168) * 2
+    assert M.moe_workspace_bytes(_k2(0)) > 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(top_k=9), M.MOE_EUNSUPPORTED),
+    (dict(top_k=0), M.MOE_EINVAL),
+    (dict(n_experts=4, top_k=8), M.MOE_EINVAL),
+    (dict(d_model=7000), M.MOE_EUNSUPPORTED),
+    (dict(d_expert=100), M.MOE_EUNSUPPORTED),
+    (dict(d_shared=1024), M.MOE_EUNSUPPORTED),
+    (dict(n_experts=2000), M.MOE_EUNSUPPORTED),
+    (dict(tokens=-1), M.MOE_EINVAL),
+    (dict(routed_scale=float("nan")), M.MOE_EINVAL),
+    (dict(tokens=1 << 40), M.MOE_EUNSUPPORTED),
+])
+def test_bad_dims_rejected(bad, code):
+    kw = dict(tokens=128, d_model=7168, n_experts=384, top_k=8, d_expert=2048, d_shared=2048,
+              routed_scale=2.827)
+    kw.update(bad)
+    d = M.moe_dims(**kw)
+    n = ctypes.c_size_t(0)
+    assert M.lib().moe_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == code
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_null_and_misaligned_pointers_rejected():
+    L = M.lib()
+    d = _k2()
+    P = _fake(0x100000)          # 16-byte aligned, never dereferenced: every call fails first
+    Q = _fake(0x100002)          # misaligned
+    ws_need = M.moe_workspace_bytes(d)
+    # null x
+    assert L.moe_forward(ctypes.byref(d), None, P, P, P, P, P, P, P, P, P, P, ws_need, None) == M.MOE_EINVAL
+    # misaligned weight
+    assert L.moe_forward(ctypes.byref(d), P, P, P, Q, P, P, P, P, P, P, P, ws_need, None) == M.MOE_EINVAL
+    # workspace too small
+    assert L.moe_forward(ctypes.byref(d), P, P, P, P, P, P, P, P, P, P, P, ws_need - 1, None) == M.MOE_EWORKSPACE
+    # workspace misaligned
+    assert L.moe_forward(ctypes.byref(d), P, P, P, P, P, P, P, P, P, P, _fake(0x100010), ws_need, None) == M.MOE_EINVAL
+    # shared expert declared but missing
+    assert L.moe_expert_down(ctypes.byref(d), P, P, P, None, P, P, P, ws_need, None) == M.MOE_EINVAL
+    # route without logits needs the workspace
+    assert L.moe_route(ctypes.byref(d), P, P, P, P, P, None, None, 0, None) == M.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(d), P, P, P, P, P, None, P, 16, None) == M.MOE_EWORKSPACE
+    # null dims
+    assert L.moe_combine(None, P, P, P, P, P, None) == M.MOE_EINVAL
+
+
+def test_zero_tokens_is_a_noop():
+    L = M.lib()
+    d = _k2(0)
+    assert L.moe_forward(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
+                         None, None, 0, None) == M.MOE_OK
+    assert L.moe_combine(ctypes.byref(d), None, None, None, None, None, None) == M.MOE_OK
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_workspace_bytes(M.moe_dims(1, 7168, 384, 9, 2048, 2048))
+    assert ei.value.status == M.MOE_EUNSUPPORTED

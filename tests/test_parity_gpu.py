@@ -1,0 +1,360 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle, on seeded inputs.
+
+Contract (per entry point):
+  routing   topk_idx equal as per-token sets, bit-exact, except tokens whose k-th/(k+1)-th
+            fp32 score gap is below 1e-6 (reported); gates within 1e-5; logits within 1e-5
+  permute   counts, offsets, perm_rows, inv_perm bit-exact against the oracle's permute of
+            the same topk_idx
+  output    max |out_gpu - out_oracle| <= 2e-2 * RMS(out_oracle) over the compared tokens
+            (bf16 output, fp32 accumulation; the oracle is float64)
+Small configs compare every token; the K2-shape configs check routing and permutation on
+every token and the output on a seeded sample of tokens the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_transformer_sigmoid_amd as M
+import synth_inputs as S
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+GAP = 1e-6
+TOL = 2e-2
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def to_dev(inp):
+    return {k: v.to(DEV) for k, v in inp.items()}
+
+
+def run_split(cfg, inp, dims=None):
+    """Every entry point in turn, each output pre-filled with a sentinel."""
+    dims = dims or M.dims_for(cfg)
+    T, E, k = dims.tokens, dims.n_experts, dims.top_k
+    d, I = dims.d_model, dims.d_expert
+    shared = dims.d_shared > 0
+    ws = M.workspace(dims)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    idx = torch.full((T, k), -7, **i32)
+    w = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    z = torch.full((T, E), float("nan"), dtype=torch.float32, device=DEV)
+    M.moe_route(dims, inp["x"], inp["w_r"], inp["b"], idx, w, z, ws)
+    counts = torch.full((E,), -7, **i32)
+    offsets = torch.full((E + 1,), -7, **i32)
+    perm = torch.full((T * k,), -7, **i32)
+    inv = torch.full((T * k,), -7, **i32)
+    M.moe_permute(dims, idx, counts, offsets, perm, inv, ws)
+    rows = T * k + (T if shared else 0)
+    h = torch.full((rows, I), float("nan"), dtype=torch.bfloat16, device=DEV)
+    M.moe_expert_gate_up(dims, inp["x"], perm, offsets, inp["w1"], inp["w3"], inp.get("ws1"),
+                         inp.get("ws3"), h, ws)
+    y_r = torch.full((T * k, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y_s = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device=DEV) if shared else None
+    M.moe_expert_down(dims, h, offsets, inp["w2"], inp.get("ws2"), y_r, y_s, ws)
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    M.moe_combine(dims, y_r, inv, w, y_s, out)
+    torch.cuda.synchronize()
+    return dict(idx=idx, w=w, z=z, counts=counts, offsets=offsets, perm=perm, inv=inv, h=h,
+                y_r=y_r, y_s=y_s, out=out, dims=dims)
+
+
+def run_forward(cfg, inp, dims=None):
+    dims = dims or M.dims_for(cfg)
+    ws = M.workspace(dims)
+    out = torch.full((dims.tokens, dims.d_model), float("nan"), dtype=torch.bfloat16, device=DEV)
+    M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
+                  inp.get("ws1"), inp.get("ws3"), inp.get("ws2"), out, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_route(inp, dims):
+    return O.route(f64(inp["x"]), f64(inp["w_r"]), inp["b"].cpu().numpy(), dims.top_k,
+                   dims.routed_scale)
+
+
+def check_routing(g, ref, dims, ztol=1e-5):
+    """Bit-exact expert sets outside the near-tie window; gates and logits in tolerance."""
+    keep = ref["gap"] >= GAP
+    idx = g["idx"].cpu().numpy()
+    assert idx.min() >= 0 and idx.max() < dims.n_experts
+    gi = np.sort(idx, axis=1)
+    oi = np.sort(ref["topk_idx"], axis=1)
+    bad = np.nonzero(np.any(gi != oi, axis=1) & keep)[0]
+    assert bad.size == 0, f"routing differs on {bad.size} tokens, e.g. {bad[:5]}"
+    # gates, matched by expert
+    gw = g["w"].cpu().numpy().astype(np.float64)
+    og = np.take_along_axis(ref["topk_w"], np.argsort(ref["topk_idx"], axis=1), axis=1)
+    gg = np.take_along_axis(gw, np.argsort(idx, axis=1), axis=1)
+    dg = np.abs(gg - og)[keep]
+    assert dg.size == 0 or dg.max() <= 1e-5, dg.max()
+    np.testing.assert_allclose(gw.sum(axis=1), dims.routed_scale, rtol=0, atol=1e-5)
+    # slot order: descending biased score
+    sc = np.take_along_axis(ref["score32"].astype(np.float64), idx.astype(np.int64), axis=1)
+    assert np.all(np.diff(sc, axis=1)[keep] <= 1e-6)
+    if g.get("z") is not None:
+        dz = np.abs(f64(g["z"]) - ref["z"]).max()
+        assert dz <= ztol, dz
+    return int((~keep).sum())
+
+
+def check_permute(g, dims):
+    """Bit-exact against the oracle's permutation of the GPU's own topk_idx."""
+    counts, offsets, perm, inv = O.permute(g["idx"].cpu().numpy(), dims.n_experts)
+    np.testing.assert_array_equal(g["counts"].cpu().numpy(), counts)
+    np.testing.assert_array_equal(g["offsets"].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(g["perm"].cpu().numpy(), perm)
+    np.testing.assert_array_equal(g["inv"].cpu().numpy(), inv)
+
+
+def check_out(got, want, what="out"):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = np.abs(got - want)
+    rms = np.sqrt(np.mean(want ** 2))
+    say(f"  {what}: max|err| {err.max():.3e}  tol {TOL * rms:.3e}  (rms {rms:.3e})")
+    assert err.max() <= TOL * rms, (err.max(), TOL * rms, np.unravel_index(err.argmax(), err.shape))
+
+
+def expert_getter(inp):
+    return lambda e: (f64(inp["w1"][e]), f64(inp["w3"][e]), f64(inp["w2"][e]))
+
+
+def shared_of(inp):
+    return (f64(inp["ws1"]), f64(inp["ws3"]), f64(inp["ws2"])) if "ws1" in inp else None
+
+
+def full_check(cfg, inp, dims=None, sample=None, intermediates=False, seed=0):
+    dims = dims or M.dims_for(cfg)
+    say(f"case T={dims.tokens} d={dims.d_model} E={dims.n_experts} k={dims.top_k} "
+        f"I={dims.d_expert} Is={dims.d_shared} alpha={dims.routed_scale}")
+    g = run_split(cfg, inp, dims)
+    ref = oracle_route(inp, dims)
+    n_ex = check_routing(g, ref, dims)
+    say(f"  routing ok; near-tie tokens excluded: {n_ex}")
+    check_permute(g, dims)
+    say("  permutation bit-exact")
+    T = dims.tokens
+    keep = ref["gap"] >= GAP
+    if sample is None:
+        toks = np.arange(T)
+    else:
+        rng = np.random.default_rng(seed)
+        toks = np.sort(rng.choice(T, size=min(sample, T), replace=False))
+    toks = toks[keep[toks]]
+    o = O.moe_sparse(f64(inp["x"]), None, None, dims.top_k, dims.routed_scale,
+                     get_expert=expert_getter(inp), shared=shared_of(inp), tokens=toks,
+                     routing=ref)
+    check_out(f64(g["out"])[toks], o["out"])
+    if intermediates:
+        # y_shared and the unweighted expert rows of the sampled tokens
+        if dims.d_shared:
+            check_out(f64(g["y_s"])[toks], o["y_shared"], "y_shared")
+        inv = g["inv"].cpu().numpy().reshape(T, dims.top_k)
+        idx = g["idx"].cpu().numpy()
+        yr = f64(g["y_r"])
+        got, want = [], []
+        for t in toks[:16]:
+            for s in range(dims.top_k):
+                e = int(idx[t, s])
+                w1, w3, w2 = expert_getter(inp)(e)
+                want.append(O.swiglu(f64(inp["x"])[t:t + 1], w1, w3, w2)[0])
+                got.append(yr[inv[t, s]])
+        check_out(np.stack(got), np.stack(want), "y_routed rows")
+    fw = run_forward(cfg, inp, dims)
+    assert torch.equal(fw.view(torch.int16), g["out"].view(torch.int16)), "forward != split path"
+    return g, ref
+
+
+# ------------------------------------------------------------------ small configs
+def test_tiny_config():
+    cfg = S.CONFIGS["tiny"]
+    inp = to_dev(S.make_inputs(cfg, "cpu"))
+    g, ref = full_check(cfg, inp, intermediates=True)
+    # h rows against the oracle's SwiGLU hidden layer
+    dims = g["dims"]
+    x = f64(inp["x"])
+    perm = g["perm"].cpu().numpy()
+    offs = g["offsets"].cpu().numpy()
+    h = f64(g["h"])
+    want = np.empty_like(h[: dims.tokens * dims.top_k])
+    for e in range(dims.n_experts):
+        for p in range(offs[e], offs[e + 1]):
+            t = perm[p] // dims.top_k
+            want[p] = O.silu(x[t] @ f64(inp["w1"][e]).T) * (x[t] @ f64(inp["w3"][e]).T)
+    check_out(h[: dims.tokens * dims.top_k], want, "h (routed)")
+    ws = O.silu(x @ f64(inp["ws1"]).T) * (x @ f64(inp["ws3"]).T)
+    check_out(h[dims.tokens * dims.top_k:], ws, "h (shared)")
+
+
+def test_deterministic_repeat():
+    cfg = S.CONFIGS["tiny"]
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=3))
+    a = run_forward(cfg, inp)
+    b = run_forward(cfg, inp)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_ragged_shapes(T):
+    # N not a multiple of the 128-wide n-block, ragged token counts
+    cfg = dict(tokens=T, d_model=320, n_experts=24, top_k=3, d_expert=192, d_shared=192,
+               routed_scale=2.827, bias="uniform")
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=T))
+    full_check(cfg, inp, intermediates=True)
+
+
+def test_no_shared_expert():
+    cfg = S.with_overrides("tiny", d_shared=0)
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=5))
+    assert "ws1" not in inp
+    full_check(cfg, inp)
+
+
+def test_all_tokens_to_the_same_experts():
+    cfg = S.with_overrides("tiny", tokens=300)
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=6))
+    b = torch.zeros(cfg["n_experts"])
+    b[:2] = 10.0
+    inp["b"] = b.to(DEV)
+    g, _ = full_check(cfg, inp)
+    c = g["counts"].cpu().numpy()
+    assert c[0] == 300 and c[1] == 300 and c[2:].sum() == 0
+
+
+def test_alpha_zero_gives_shared_only():
+    cfg = S.with_overrides("tiny", routed_scale=0.0)
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=7))
+    g = run_split(cfg, inp)
+    assert torch.equal(g["out"].view(torch.int16), g["y_s"].view(torch.int16))
+    assert torch.count_nonzero(g["w"]) == 0
+
+
+def test_w2_zero_gives_shared_only():
+    cfg = S.CONFIGS["tiny"]
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=8))
+    inp["w2"] = torch.zeros_like(inp["w2"])
+    g = run_split(cfg, inp)
+    assert torch.equal(g["out"].view(torch.int16), g["y_s"].view(torch.int16))
+    full_check(cfg, inp)
+
+
+def test_k_equals_e():
+    cfg = dict(tokens=50, d_model=128, n_experts=8, top_k=8, d_expert=64, d_shared=64,
+               routed_scale=2.827, bias="uniform")
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=9))
+    g, _ = full_check(cfg, inp)
+    assert np.all(g["counts"].cpu().numpy() == 50)
+
+
+def test_single_expert():
+    cfg = dict(tokens=20, d_model=64, n_experts=1, top_k=1, d_expert=64, d_shared=64,
+               routed_scale=2.827, bias="uniform")
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=10))
+    g, _ = full_check(cfg, inp)
+    np.testing.assert_allclose(g["w"].cpu().numpy(), 2.827, rtol=1e-6)
+
+
+def test_tie_break_lower_index():
+    cfg = S.with_overrides("tiny", top_k=1)
+    inp = S.make_inputs(cfg, "cpu", seed=11)
+    inp["w_r"][5] = inp["w_r"][3]
+    inp["b"][3] = 10.0
+    inp["b"][5] = 10.0
+    inp = to_dev(inp)
+    g = run_split(cfg, inp)
+    assert torch.all(g["idx"] == 3)
+
+
+def test_permute_drops_invalid_entries():
+    cfg = S.CONFIGS["tiny"]
+    dims = M.dims_for(cfg, tokens=6)
+    idx = torch.tensor([[0, 1], [2, 2], [-1, 3], [16, 4], [5, 6], [7, 7]], dtype=torch.int32,
+                       device=DEV)
+    E, T, k = 16, 6, 2
+    ws = M.workspace(dims)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    perm = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    inv = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    M.moe_permute(dims, idx, counts, offsets, perm, inv, ws)
+    torch.cuda.synchronize()
+    inv_h = inv.cpu().numpy()
+    dropped = [3, 4, 6, 11]          # duplicate, out of range (-1, 16), duplicate
+    assert all(inv_h[j] == -1 for j in dropped)
+    valid = [j for j in range(T * k) if j not in dropped]
+    flat = idx.cpu().numpy().reshape(-1)
+    want_counts = np.bincount(flat[valid], minlength=E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), want_counts)
+    assert offsets.cpu().numpy()[-1] == len(valid)
+    p = perm.cpu().numpy()
+    assert np.all(p[len(valid):] == -1)
+    np.testing.assert_array_equal(p[:len(valid)], np.array(valid)[np.argsort(flat[valid], kind="stable")])
+
+
+def test_zero_tokens_leaves_output_alone():
+    cfg = S.CONFIGS["tiny"]
+    inp = to_dev(S.make_inputs(cfg, "cpu"))
+    dims = M.dims_for(cfg, tokens=0)
+    out = torch.full((4, cfg["d_model"]), 1.5, dtype=torch.bfloat16, device=DEV)
+    M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
+                  inp["ws1"], inp["ws3"], inp["ws2"], out, M.workspace(dims))
+    torch.cuda.synchronize()
+    assert torch.all(out == 1.5)
+
+
+def test_workspace_too_small_rejected_on_device():
+    cfg = S.CONFIGS["tiny"]
+    inp = to_dev(S.make_inputs(cfg, "cpu"))
+    dims = M.dims_for(cfg)
+    ws = torch.empty(M.moe_workspace_bytes(dims) - 256, dtype=torch.uint8, device=DEV)
+    out = torch.empty(cfg["tokens"], cfg["d_model"], dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
+                      inp["ws1"], inp["ws3"], inp["ws2"], out, ws)
+    assert ei.value.status == M.MOE_EWORKSPACE
+
+
+# ------------------------------------------------------------------ K2 shape
+@pytest.fixture(scope="module")
+def k2_weights():
+    say("generating K2-shape weights on the GPU (384 experts, d 7168, I 2048)")
+    w = S.make_weights("k2_decode", DEV)
+    torch.cuda.synchronize()
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+def _k2_case(name, k2_weights, sample):
+    cfg = S.CONFIGS[name]
+    inp = dict(k2_weights)
+    inp.update(S.make_activations(cfg, DEV))
+    g, ref = full_check(cfg, inp, sample=sample, intermediates=True)
+    active = int((g["counts"] > 0).sum())
+    say(f"  {name}: active experts {active}, max rows/expert {int(g['counts'].max())}")
+    return g
+
+
+def test_k2_decode_128(k2_weights):
+    _k2_case("k2_decode", k2_weights, sample=16)
+
+
+def test_k2_prefill_8192(k2_weights):
+    _k2_case("k2_prefill", k2_weights, sample=8)
+
+
+def test_k2_skewed_4096(k2_weights):
+    g = _k2_case("k2_skew", k2_weights, sample=8)
+    c = g["counts"].cpu().numpy()
+    assert (c == 0).sum() > 100          # many idle experts
