@@ -1,0 +1,234 @@
+"""Throughput of the K2-shape MoE FFN layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload k2_decode|k2_prefill]
+
+A step is one moe_forward over the batch: router, top-k and gates, permutation,
+gate/up GEMM with SwiGLU, down GEMM, combine with the shared expert.  Inputs (seeded,
+synthetic, K2 shape: d 7168, 384 experts, top-8, I 2048, one shared expert, bf16
+weights, fp32 router) are resident in HBM before the timed region.  Prints one JSON
+line: whole-layer tokens/s for the main workload (128-token decode by default), the
+roofline of the dominant kernel (the gate/up grouped GEMM) timed with HIP events on
+the stream it runs on, the 8192-token prefill figure, and the CPU oracle timed on a
+bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "K2 MoE-layer tokens/s (128 & 8192 tok, bf16); % of HBM / MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="k2_decode", choices=["k2_decode", "k2_prefill"])
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token figure")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=12, help="tokens in the oracle sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg, active, T):
+    """Bytes and flops of one layer pass and of one gate/up launch (each weight of an
+    active expert counted once; activations read/written once)."""
+    d, I, Is, E, k = cfg["d_model"], cfg["d_expert"], cfg["d_shared"], cfg["n_experts"], cfg["top_k"]
+    expert_w = 3 * d * I * 2                      # bytes of one expert's W1, W3, W2 (bf16)
+    rows = T * k + (T if Is else 0)
+    layer_bytes = (active * expert_w + (3 * d * Is * 2 if Is else 0) + E * d * 4 + E * 4
+                   + T * d * 2 + T * d * 2)
+    layer_flops = 2 * 3 * d * I * T * k + (2 * 3 * d * Is * T if Is else 0)
+    gateup_units = active + (1 if Is else 0)        # experts whose W1, W3 stream through
+    gateup_bytes = gateup_units * 2 * d * I * 2 + T * d * 2 + rows * I * 2
+    gateup_flops = 2 * 2 * d * I * rows
+    return dict(layer_bytes=layer_bytes, layer_flops=layer_flops, gateup_bytes=gateup_bytes,
+                gateup_flops=gateup_flops, gateup_units=gateup_units)
+
+
+def time_forward(M, torch, dims, inp, out, ws, steps, warmup):
+    for _ in range(warmup):
+        M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
+                      inp["ws1"], inp["ws3"], inp["ws2"], out, ws)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
+                      inp["ws1"], inp["ws3"], inp["ws2"], out, ws)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    return t0.elapsed_time(t1) / steps, wall
+
+
+def split_state(M, torch, dims, inp, ws):
+    """Route and permute once: the gate/up GEMM's inputs."""
+    T, E, k = dims.tokens, dims.n_experts, dims.top_k
+    dev = inp["x"].device
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    M.moe_route(dims, inp["x"], inp["w_r"], inp["b"], idx, w, None, ws)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    M.moe_permute(dims, idx, counts, offsets, perm, inv, ws)
+    torch.cuda.synchronize()
+    return dict(idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv)
+
+
+def time_gate_up(M, torch, dims, inp, st, ws, steps, warmup):
+    """Average duration of one moe_expert_gate_up call (tile-list kernel + GEMM kernel),
+    HIP events on the current stream, which is the stream the kernels run on."""
+    T, k = dims.tokens, dims.top_k
+    h = torch.empty(T * k + T, dims.d_expert, dtype=torch.bfloat16, device=inp["x"].device)
+
+    def call():
+        M.moe_expert_gate_up(dims, inp["x"], st["perm"], st["offsets"], inp["w1"], inp["w3"],
+                             inp["ws1"], inp["ws3"], h, ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def cpu_baseline(torch, S, cfg, inp, n_tok):
+    """The oracle as it stands on a bounded sample: route + sparse FFN for n_tok tokens of
+    the batch, weights pre-staged on the host (bf16), timed on the host cores."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+    T = cfg["tokens"]
+    toks = np.sort(np.random.default_rng(0).choice(T, size=min(n_tok, T), replace=False))
+    x = inp["x"][toks].to("cpu", torch.float64).numpy()
+    w_r = inp["w_r"].to("cpu", torch.float64).numpy()
+    b = inp["b"].cpu().numpy()
+    r = O.route(x, w_r, b, cfg["top_k"], cfg["routed_scale"])
+    need = sorted(set(int(e) for e in r["topk_idx"].reshape(-1)))
+    host = {e: (inp["w1"][e].cpu(), inp["w3"][e].cpu(), inp["w2"][e].cpu()) for e in need}
+    shared_h = (inp["ws1"].cpu(), inp["ws3"].cpu(), inp["ws2"].cpu())
+
+    def get(e):
+        return tuple(t.to(torch.float64).numpy() for t in host[e])
+    t = time.perf_counter()
+    r = O.route(x, w_r, b, cfg["top_k"], cfg["routed_scale"])
+    O.moe_sparse(x, w_r, b, cfg["top_k"], cfg["routed_scale"], get_expert=get,
+                 shared=tuple(s.to(torch.float64).numpy() for s in shared_h), routing=r)
+    el = time.perf_counter() - t
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [torch.get_num_threads()])
+    return {"value": len(toks) / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(toks)} of the {T} tokens (route + {len(need)} experts + shared, "
+                      f"float64 numpy, {el:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the layer is measured on one GPU; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_transformer_sigmoid_amd as M
+    import synth_inputs as S
+
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS[args.workload]
+    log("generating K2-shape weights on the GPU")
+    weights = S.make_weights(cfg, dev)
+    inp = dict(weights)
+    inp.update(S.make_activations(cfg, dev))
+    dims = M.dims_for(cfg)
+    T = cfg["tokens"]
+    ws = M.workspace(dims, dev)
+    out = torch.empty(T, cfg["d_model"], dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    log(f"timing moe_forward, {args.workload}, T={T}")
+    ms, wall = time_forward(M, torch, dims, inp, out, ws, args.steps, args.warmup)
+    st = split_state(M, torch, dims, inp, ws)
+    active = int((st["counts"] > 0).sum())
+    alg = algorithmic(cfg, active, T)
+    gu_ms = time_gate_up(M, torch, dims, inp, st, ws, args.steps, args.warmup)
+    gu_gbs = alg["gateup_bytes"] / (gu_ms * 1e-3) / 1e9
+    layer_gbs = alg["layer_bytes"] / (ms * 1e-3) / 1e9
+    layer_tfs = alg["layer_flops"] / (ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: one MoE FFN layer, T={T} tokens, d=7168, "
+                               "384 experts top-8 (x2.827), I=2048, 1 shared expert, bf16 "
+                               "weights/activations, fp32 router and accumulation",
+                   "tokens": T, "active_experts": active},
+        "roofline": {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "ffn_skinny_kernel<gate/up> (+ its tile-list launch)",
+                     "ms_per_launch": gu_ms, "bytes_per_launch": alg["gateup_bytes"]},
+        "layer": {"hbm_gbs": layer_gbs, "hbm_frac": layer_gbs / HBM_PEAK_GBS,
+                  "mfma_tflops": layer_tfs, "mfma_frac": layer_tfs / MFMA_BF16_PEAK_TFLOPS,
+                  "algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"]},
+    }
+    log(f"{args.workload}: {ms:.3f} ms/step, {res['value']:.0f} tok/s, layer {layer_gbs:.0f} GB/s, "
+        f"gate/up {gu_ms:.3f} ms = {gu_gbs:.0f} GB/s")
+
+    if not args.no_prefill and args.workload != "k2_prefill":
+        pcfg = S.CONFIGS["k2_prefill"]
+        pin = dict(weights)
+        pin.update(S.make_activations(pcfg, dev))
+        pdims = M.dims_for(pcfg)
+        del ws
+        pws = M.workspace(pdims, dev)
+        pout = torch.empty(pcfg["tokens"], pcfg["d_model"], dtype=torch.bfloat16, device=dev)
+        log("timing moe_forward, k2_prefill, T=8192")
+        psteps = max(3, min(args.steps, 10))
+        pms, _ = time_forward(M, torch, pdims, pin, pout, pws, psteps, 1)
+        pst = split_state(M, torch, pdims, pin, pws)
+        pact = int((pst["counts"] > 0).sum())
+        palg = algorithmic(pcfg, pact, pcfg["tokens"])
+        ptf = palg["layer_flops"] / (pms * 1e-3) / 1e12
+        pgb = palg["layer_bytes"] / (pms * 1e-3) / 1e9
+        res["prefill"] = {"workload": "k2_prefill: T=8192 (4 x 2048), same layer", "steps": psteps,
+                          "ms_per_step": pms, "tokens_per_s": pcfg["tokens"] / (pms * 1e-3),
+                          "mfma_tflops": ptf, "mfma_frac": ptf / MFMA_BF16_PEAK_TFLOPS,
+                          "hbm_gbs": pgb, "hbm_frac": pgb / HBM_PEAK_GBS, "active_experts": pact}
+        log(f"prefill: {pms:.3f} ms/step, {res['prefill']['tokens_per_s']:.0f} tok/s, "
+            f"{ptf:.0f} TFLOP/s ({100 * ptf / MFMA_BF16_PEAK_TFLOPS:.1f}% MFMA)")
+        del pws, pin
+
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_sample} tokens")
+        res["cpu_baseline"] = cpu_baseline(torch, S, cfg, inp, args.cpu_sample)
+        log(f"cpu oracle: {res['cpu_baseline']['value']:.2f} tok/s on {res['cpu_baseline']['cores']} threads")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

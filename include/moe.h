@@ -113,27 +113,29 @@ moe_status moe_expert_gate_up(const moe_dims* dims, const uint16_t* x, const int
 
 /* Expert down projections ("Kimi K2 · Transformer blocks", E_i = h W2; y_shared = h W2).
  *   h as produced by moe_expert_gate_up;
- *   y_routed [T*k, d] bf16 grouped order (rows >= offsets[E] untouched);
- *   y_shared [T, d]   bf16 (NULL iff no shared expert).  fp32 accumulation, bf16 store. */
+ *   y_routed [T*k, d] fp32 grouped order (rows >= offsets[E] untouched);
+ *   y_shared [T, d]   fp32 (NULL iff no shared expert).  fp32 accumulation; the expert
+ *   outputs stay fp32 so that the layer output is rounded to bf16 only once. */
 moe_status moe_expert_down(const moe_dims* dims, const uint16_t* h, const int32_t* offsets,
-                           const uint16_t* w2, const uint16_t* ws2, uint16_t* y_routed,
-                           uint16_t* y_shared, void* ws, size_t ws_bytes, void* stream);
+                           const uint16_t* w2, const uint16_t* ws2, float* y_routed,
+                           float* y_shared, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_expert_gate_up followed by moe_expert_down, h kept in the workspace. */
 moe_status moe_expert_ffn(const moe_dims* dims, const uint16_t* x, const int32_t* perm_rows,
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                           const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
-                          const uint16_t* ws2, uint16_t* y_routed, uint16_t* y_shared,
+                          const uint16_t* ws2, float* y_routed, float* y_shared,
                           void* ws, size_t ws_bytes, void* stream);
 
 /* Weighted combine plus shared expert ("Kimi K2 · Transformer blocks", y_routed =
  * sum_i G_i E_i and Delta_ffn = y_routed + y_shared; the fp32 weighted sum over the k
  * slots of "Kimi K3 · Latent up-projection", moe_infer):
  *   out[t] = bf16( sum_{slot} topk_w[t, slot] * y_routed[inv_perm[t*k + slot]] + y_shared[t] )
- * summed in fp32 in slot order, one rounding to bf16.  inv_perm = -1 slots add nothing;
+ * with y_routed [T*k, d] and y_shared [T, d] fp32, summed in fp32 in slot order, one
+ * rounding to bf16.  inv_perm = -1 slots add nothing;
  * y_shared may be NULL. */
-moe_status moe_combine(const moe_dims* dims, const uint16_t* y_routed, const int32_t* inv_perm,
-                       const float* topk_w, const uint16_t* y_shared, uint16_t* out,
+moe_status moe_combine(const moe_dims* dims, const float* y_routed, const int32_t* inv_perm,
+                       const float* topk_w, const float* y_shared, uint16_t* out,
                        void* stream);
 
 /* The whole layer: route, permute, gate/up, down, combine; out [T, d] bf16.

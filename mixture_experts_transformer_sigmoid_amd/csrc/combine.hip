@@ -3,7 +3,8 @@
 // y_shared; the weighted sum over the k slots in fp32 as in the moe_infer of
 // "Kimi K3 · Latent up-projection".  fp32 accumulation in slot order, one bf16 rounding.
 //
-// Each thread owns 8 consecutive features of one token (16-byte loads and stores);
+// Each thread owns 8 consecutive features of one token (32-byte fp32 loads, one 16-byte
+// bf16 store);
 // a token's k expert rows are gathered through inv_perm.
 #include "common.h"
 
@@ -13,46 +14,44 @@ namespace {
 constexpr int kCombineThreads = 256;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    const uint16_t* __restrict__ y_routed, const int32_t* __restrict__ inv,
-    const float* __restrict__ topk_w, const uint16_t* __restrict__ y_shared,
+    const float* __restrict__ y_routed, const int32_t* __restrict__ inv,
+    const float* __restrict__ topk_w, const float* __restrict__ y_shared,
     uint16_t* __restrict__ out, int64_t T, int d, int k) {
   const int nchunk = (d / 8 + kCombineThreads - 1) / kCombineThreads;
   const int64_t t = blockIdx.x / nchunk;
   const int c = ((int)(blockIdx.x % nchunk) * kCombineThreads + threadIdx.x) * 8;
   if (t >= T || c >= d) return;
   const int64_t slots = T * k;
-  float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < k; ++s) {
     const int32_t p = inv[t * k + s];
     if (p < 0 || p >= slots) continue;
     const float w = topk_w[t * k + s];
-    const u32x4_t v = load16(y_routed + (int64_t)p * d + c);
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y_routed + (int64_t)p * d + c);
+    const f32x4_t a = src[0], b = src[1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(w, bf16_to_f32(v[i] & 0xffffu), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(w, bf16_to_f32(v[i] >> 16), acc[2 * i + 1]);
+      lo[i] = fmaf(w, a[i], lo[i]);
+      hi[i] = fmaf(w, b[i], hi[i]);
     }
   }
   if (y_shared != nullptr) {
-    const u32x4_t v = load16(y_shared + t * d + c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += bf16_to_f32(v[i] & 0xffffu);
-      acc[2 * i + 1] += bf16_to_f32(v[i] >> 16);
-    }
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y_shared + t * d + c);
+    lo += src[0];
+    hi += src[1];
   }
   u32x4_t o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
+  o[0] = f32_to_bf16(lo[0]) | (f32_to_bf16(lo[1]) << 16);
+  o[1] = f32_to_bf16(lo[2]) | (f32_to_bf16(lo[3]) << 16);
+  o[2] = f32_to_bf16(hi[0]) | (f32_to_bf16(hi[1]) << 16);
+  o[3] = f32_to_bf16(hi[2]) | (f32_to_bf16(hi[3]) << 16);
   *reinterpret_cast<u32x4_t*>(out + t * d + c) = o;
 }
 
 }  // namespace
 
-hipError_t launch_combine(const uint16_t* y_routed, const int32_t* inv, const float* topk_w,
-                          const uint16_t* y_shared, uint16_t* out, int64_t T, int d, int k,
+hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float* topk_w,
+                          const float* y_shared, uint16_t* out, int64_t T, int d, int k,
                           hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int64_t nchunk = (d / 8 + kCombineThreads - 1) / kCombineThreads;

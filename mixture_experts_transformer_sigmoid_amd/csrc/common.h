@@ -52,7 +52,9 @@ struct Tile {
   int32_t group;      // expert index, or E for the shared expert
   int32_t row_begin;  // first row (grouped order; shared rows start at T*k)
   int32_t row_end;    // one past the last row
-  int32_t pad;
+  int32_t first;      // index of the group's first tile in the list
+  int32_t count;      // number of tiles of the group
+  int32_t pad[3];
 };
 
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
@@ -81,11 +83,11 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
                           int32_t* ntiles, hipStream_t s);
 
 hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
-                       const uint16_t* w2, const uint16_t* ws2, uint16_t* y_routed,
-                       uint16_t* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s);
+                       const uint16_t* w2, const uint16_t* ws2, float* y_routed,
+                       float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s);
 
-hipError_t launch_combine(const uint16_t* y_routed, const int32_t* inv, const float* topk_w,
-                          const uint16_t* y_shared, uint16_t* out, int64_t T, int d, int k,
+hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float* topk_w,
+                          const float* y_shared, uint16_t* out, int64_t T, int d, int k,
                           hipStream_t s);
 
 }  // namespace moe

@@ -64,7 +64,7 @@ Layout layout(const moe_dims& d) {
   L.tiles = take(max_tiles * sizeof(Tile));
   L.ntiles = take(4);
   L.h = take(rows * (size_t)d.d_expert * 2);
-  L.y = take(rows * (size_t)d.d_model * 2);
+  L.y = take(rows * (size_t)d.d_model * 4);
   L.total = off;
   return L;
 }
@@ -121,15 +121,15 @@ moe_status gate_up_impl(const moe_dims& d, const uint16_t* x, const int32_t* per
 }
 
 moe_status down_impl(const moe_dims& d, const uint16_t* h, const int32_t* offsets,
-                     const uint16_t* w2, const uint16_t* ws2, uint16_t* y_routed,
-                     uint16_t* y_shared, void* ws, hipStream_t s) {
+                     const uint16_t* w2, const uint16_t* ws2, float* y_routed,
+                     float* y_shared, void* ws, hipStream_t s) {
   const Layout L = layout(d);
   return hip_status(moe::launch_down(ffn_shape(d), h, offsets, w2, ws2, y_routed, y_shared,
                                      at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles), s));
 }
 
-moe_status combine_impl(const moe_dims& d, const uint16_t* y_routed, const int32_t* inv,
-                        const float* w, const uint16_t* y_shared, uint16_t* out, hipStream_t s) {
+moe_status combine_impl(const moe_dims& d, const float* y_routed, const int32_t* inv,
+                        const float* w, const float* y_shared, uint16_t* out, hipStream_t s) {
   return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, out, d.tokens, d.d_model,
                                         d.top_k, s));
 }
@@ -206,8 +206,8 @@ moe_status moe_expert_gate_up(const moe_dims* dims, const uint16_t* x, const int
 }
 
 moe_status moe_expert_down(const moe_dims* dims, const uint16_t* h, const int32_t* offsets,
-                           const uint16_t* w2, const uint16_t* ws2, uint16_t* y_routed,
-                           uint16_t* y_shared, void* ws, size_t ws_bytes, void* stream) {
+                           const uint16_t* w2, const uint16_t* ws2, float* y_routed,
+                           float* y_shared, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(dims));
   const moe_dims& d = *dims;
   if (d.tokens == 0) return MOE_OK;
@@ -221,7 +221,7 @@ moe_status moe_expert_down(const moe_dims* dims, const uint16_t* h, const int32_
 moe_status moe_expert_ffn(const moe_dims* dims, const uint16_t* x, const int32_t* perm_rows,
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                           const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
-                          const uint16_t* ws2, uint16_t* y_routed, uint16_t* y_shared, void* ws,
+                          const uint16_t* ws2, float* y_routed, float* y_shared, void* ws,
                           size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(dims));
   const moe_dims& d = *dims;
@@ -237,8 +237,8 @@ moe_status moe_expert_ffn(const moe_dims* dims, const uint16_t* x, const int32_t
   return down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s);
 }
 
-moe_status moe_combine(const moe_dims* dims, const uint16_t* y_routed, const int32_t* inv_perm,
-                       const float* topk_w, const uint16_t* y_shared, uint16_t* out,
+moe_status moe_combine(const moe_dims* dims, const float* y_routed, const int32_t* inv_perm,
+                       const float* topk_w, const float* y_shared, uint16_t* out,
                        void* stream) {
   MOE_TRY(check_dims(dims));
   const moe_dims& d = *dims;
@@ -271,9 +271,8 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
   int32_t* perm = at<int32_t>(ws, L.perm);
   int32_t* inv = at<int32_t>(ws, L.inv);
   uint16_t* h = at<uint16_t>(ws, L.h);
-  uint16_t* y_routed = at<uint16_t>(ws, L.y);
-  uint16_t* y_shared =
-      has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
+  float* y_routed = at<float>(ws, L.y);
+  float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
   MOE_TRY(route_impl(d, x, w_router, bias, idx, w, at<float>(ws, L.z), s));
   MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s));
   MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s));
