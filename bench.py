@@ -24,8 +24,67 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "K2 MoE-layer tokens/s (128 & 8192 tok, bf16); % of HBM / MFMA peak"
+# the gate/up kernel each workload runs (decode: a few rows per expert; prefill: many)
+GATEUP_KERNEL = {"k2_decode": "ffn_skinny_kernel<2, 8, true>", "k2_prefill": "ffn_stream_kernel<true>"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_transformer_sigmoid_amd", "csrc", f)
+                  for f in ("ffn.hip", "common.h")]
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def write_traffic(fetch_csv, write_csv):
+    """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of a
+    --copy-calibration run into profiles/hbm_traffic.json: bytes per launch per kernel,
+    each counter scaled by what it reads for the 1 GiB calibration copy."""
+    import csv
+    import collections
+    out = {"source_sha256": kernel_source_hash(), "kernels": {}, "scale": {}}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        scale = (COPY_BYTES / 1024) / copy
+        out["scale"][counter] = scale
+        per = collections.defaultdict(list)
+        for r in rows:
+            if "copyBuffer" in r["Kernel_Name"]:
+                continue
+            per[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024 * scale)
+        for k, v in per.items():
+            key = "read_bytes" if counter == "FETCH_SIZE" else "write_bytes"
+            out["kernels"].setdefault(k, {})[key] = sum(v) / len(v)
+            out["kernels"][k]["launches"] = len(v)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1))
+
+
+def traffic_for(kernel_substr):
+    """HBM bytes per launch of a kernel from the committed counter summary, or None when it
+    is missing or the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    for name, v in t["kernels"].items():
+        if kernel_substr in name and "read_bytes" in v and "write_bytes" in v:
+            return v["read_bytes"] + v["write_bytes"]
+    return None
 
 
 def parse():
@@ -36,7 +95,12 @@ def parse():
     ap.add_argument("--workload", default="k2_decode", choices=["k2_decode", "k2_prefill"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=12, help="tokens in the oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="tokens in the oracle sample")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two --pmc counter CSVs and exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device-to-device copy (a plain copy kernel of known size "
+                         "for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -148,6 +212,9 @@ def cpu_baseline(torch, S, cfg, inp, n_tok):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the layer is measured on one GPU; see DESIGN.md for how it would shard)",
@@ -175,6 +242,14 @@ def main():
     st = split_state(M, torch, dims, inp, ws)
     active = int((st["counts"] > 0).sum())
     alg = algorithmic(cfg, active, T)
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {1 << 30} bytes read, {1 << 30} bytes written")
+        del src, dst
     gu_ms = time_gate_up(M, torch, dims, inp, st, ws, args.steps, args.warmup)
     gu_gbs = alg["gateup_bytes"] / (gu_ms * 1e-3) / 1e9
     layer_gbs = alg["layer_bytes"] / (ms * 1e-3) / 1e9
@@ -189,8 +264,9 @@ def main():
                                "weights/activations, fp32 router and accumulation",
                    "tokens": T, "active_experts": active},
         "roofline": {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "ffn_skinny_kernel<gate/up> (+ its tile-list launch)",
+                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic_for(GATEUP_KERNEL[args.workload]),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "kernel": GATEUP_KERNEL[args.workload] + " (+ its tile-list launch)",
                      "ms_per_launch": gu_ms, "bytes_per_launch": alg["gateup_bytes"]},
         "layer": {"hbm_gbs": layer_gbs, "hbm_frac": layer_gbs / HBM_PEAK_GBS,
                   "mfma_tflops": layer_tfs, "mfma_frac": layer_tfs / MFMA_BF16_PEAK_TFLOPS,

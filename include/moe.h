@@ -32,7 +32,8 @@
  *   - Errors are status codes, checked on the host BEFORE anything is launched:
  *       MOE_EINVAL       null / misaligned (16 B) pointer, impossible dims
  *       MOE_EUNSUPPORTED dims this build does not handle (d, I not multiples of 64,
- *                        top_k > 8, E > 1024, Is not 0 or I)
+ *                        top_k > 8, E > 1024, Is not 0 or I, x or one weight matrix
+ *                        of 4 GiB or more)
  *       MOE_EWORKSPACE   ws_bytes smaller than moe_workspace_bytes()
  *       MOE_EHIP         a kernel launch failed (device faults surface at the caller's
  *                        next synchronisation, as usual for asynchronous work)
@@ -79,9 +80,11 @@ moe_status moe_workspace_bytes(const moe_dims* dims, size_t* bytes);
  *   topk_idx [T, k] int32  chosen experts per token, descending biased score, ties to
  *                          the lower expert index
  *   topk_w   [T, k] fp32   gates alpha * s / sum(s over the chosen), same order
- *   logits   [T, E] fp32   z, or NULL (then kept in the workspace)
- * z is accumulated in fp32 from the bf16 x and fp32 w_router; the selection compares
- * fp32 scores fl(sigmoid(z) + b). */
+ *   logits   [T, E] fp32   z, or NULL (not written)
+ *   ws                     workspace (required)
+ * z keeps fp32 accuracy: w_router is split exactly into three bf16 parts whose products
+ * with the bf16 x are exact; their sums (fp32 accumulation) are added in fp64 and
+ * rounded to fp32.  The selection compares fp32 scores fl(sigmoid(z) + b). */
 moe_status moe_route(const moe_dims* dims, const uint16_t* x, const float* w_router,
                      const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
                      void* ws, size_t ws_bytes, void* stream);

@@ -32,6 +32,19 @@ __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Raw buffer resource over [base, base + bytes): loads take a 32-bit per-lane byte offset
+// and a wave-uniform byte offset, so the address costs one VGPR; reads past `bytes`
+// return zeros instead of faulting.  Word 3 is the gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                           uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // C(16x16, fp32) += A(16x32) * B(32x16), bf16 operands.
 // Lane l supplies row (l & 15) of A and column (l & 15) of B, each with the 8
 // consecutive k values 8*(l >> 4) .. +7; it receives C rows 4*(l >> 4) .. +3 of column
@@ -41,6 +54,17 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
 }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations, then meets
+// the other waves.  Unlike __syncthreads() it does not drain the wave's outstanding
+// global loads (on CDNA a release fence waits for vmcnt(0)), so register prefetches of
+// later k-steps stay in flight across it.  Only for kernels whose waves share data
+// through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 }  // namespace moe
 
@@ -57,8 +81,10 @@ struct Tile {
   int32_t pad[3];
 };
 
+// Router: w_split [3E, d] bf16 and z_part [T, 3E] fp32 are workspace; logits may be null.
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
-                         int E, int k, float alpha, float* logits, int32_t* topk_idx,
+                         int E, int k, float alpha, uint16_t* w_split, float* z_part,
+                         Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,
                          float* topk_w, hipStream_t s);
 
 hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* hist,
@@ -76,6 +102,10 @@ struct FfnShape {
 };
 
 int64_t ffn_max_tiles(const FfnShape& sh);
+
+// C[rows, N] (fp32) = A[rows, K] . W[N, K]^T with the grouped-GEMM kernels (one group).
+hipError_t launch_dense_f32(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
+                            float* C, Tile* tiles, int32_t* ntiles, hipStream_t s);
 
 hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,

@@ -16,9 +16,10 @@
 // each XCD walks one contiguous run of items and an expert's weight and activation
 // reuse stays inside one L2.
 //
-// Two kernels: "skinny" for row tiles of <= 16 rows (decode: a few tokens per expert),
-// a pure weight stream from HBM straight into MFMA registers; "wide" for 128-row tiles
-// (prefill), LDS-tiled with a three-deep register prefetch of the next k-chunks.
+// Two kernels, both streaming weights from HBM straight into MFMA registers: "skinny"
+// for row tiles of <= 16 rows (decode: a few tokens per expert), activations from L2;
+// "stream" for 256-row tiles (prefill), activations staged in LDS and shared by the
+// workgroup's waves.
 #include "common.h"
 
 namespace moe {
@@ -39,6 +40,7 @@ struct FfnArgs {
   const int32_t* ntiles;
   int32_t k;              // slots per token (gate/up gather: token = slot / k)
   int32_t N, K, E;
+  int64_t a_rows;         // rows of A (gate/up: tokens of x)
 };
 
 // ------------------------------------------------------------------ tile list
@@ -247,171 +249,234 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
   }
 }
 
-// --------------------------------------------------------------- wide GEMM
-// 128-row tiles.  Four waves as 2 (rows) x 2 (features); each wave owns a 64-row x
-// BN/2-feature block (per weight matrix).  K is walked in 64-wide chunks staged in LDS
-// (row pitch 144 B: 16 B of padding make the MFMA operand reads and the chunk writes
-// bank-conflict free).  Global loads for chunk kt+3 are issued while chunk kt is being
-// multiplied, through a ring of three register sets, and chunk kt+1 is written to the
-// other LDS buffer at the end of the step: one barrier per chunk.  16-row fragments
-// past the tile's last row skip their MFMAs (a wave-uniform branch), so a 108-row
-// expert costs 112 rows of MFMA work, not 128.
-template <int BN, bool GATEUP>
-__global__ __launch_bounds__(256, 2) void ffn_wide_kernel(const FfnArgs a) {
-  constexpr int BM = 128, BK = 64;
-  constexpr int PITCH = BK + 8;                       // bf16 elements per LDS row
-  constexpr int WROWS = GATEUP ? 2 * BN : BN;         // weight rows staged per chunk
-  constexpr int NCA = BM * 8 / 256;                   // 16-byte pieces per thread: acts
-  constexpr int NCW = WROWS * 8 / 256;                // 16-byte pieces per thread: weights
-  constexpr int NC = NCA + NCW;
-  constexpr int STAGE = (BM + WROWS) * PITCH;         // bf16 elements per LDS stage
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
-  static_assert(NCA * 256 == BM * 8 && NCW * 256 == WROWS * 8, "tile / thread mismatch");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+// ------------------------------------------------------------- stream GEMM
+// 256-row tiles (prefill: an expert's rows usually fit one tile, so its weights leave HBM
+// once).  Eight waves, each owning all of the tile's rows (16 row fragments) x 32 outputs
+// (gate/up: 16 features of W1 and the same 16 of W3; down: 32 features), so no two waves
+// load the same weights.  Weights stream from HBM straight into MFMA registers, the same
+// operand layout as the skinny kernel, through a ring of six k-step register sets: five
+// k-steps (10 KiB per wave, 80 KiB per CU) are in flight while one is multiplied.  The
+// tile's activation rows are staged in LDS in 64-wide k-chunks (row pitch 144 B:
+// conflict-free MFMA reads and chunk writes), double-buffered, with one LDS-only barrier
+// per chunk (it does not drain the weight loads in flight).  Activation fragments are
+// read from LDS two at a time, one group ahead of the four MFMAs that use them.
+// The main loop is straight-line code: it is instantiated for 4, 8, 12 or 16 live row
+// fragments (the tile's rows rounded up to 64: rows past the end cost at most three
+// fragments of MFMAs), prefetch indices are clamped instead of guarded, and three chunks
+// are unrolled per iteration so the register ring is indexed statically.  Branches inside
+// the loop would make the compiler's wait-count analysis conservative at every join and
+// wait for the prefetched loads too.
+struct StreamCtx {
+  __amdgpu_buffer_rsrc_t w1;   // matrix of weight fragment 0 (and 1 unless gate/up)
+  __amdgpu_buffer_rsrc_t w3;   // gate/up: matrix of weight fragment 1
+  __amdgpu_buffer_rsrc_t act;  // activation rows (x, or the tile's rows of h)
+  uint32_t woff[2];            // byte offset of the lane's row and k lane-group, per fragment
+  uint32_t aoff[4];            // byte offset of each activation piece (row start + chunk)
+  int adst;                    // LDS offset (elements) of the first activation piece; piece
+                               // i sits 64 i rows further
+  int nks, nc;                 // k-steps (32) and chunks (64)
+};
+
+template <bool GATEUP, int NL>
+__device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
+                                            f32x4_t (&acc)[16][2]) {
+  constexpr int BM = 256, BK = 64, PITCH = BK + 8, NW = 2, NA = 4;
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int nks = c_.nks, nc = c_.nc;
+  u32x4_t W0[NW], W1[NW], W2[NW], W3[NW], W4[NW], W5[NW], AR[NA];
+
+  auto load_w = [&](u32x4_t* S, int ks) {
+    const uint32_t kb = (uint32_t)(ks < nks ? ks : nks - 1) * 64;  // past the end: re-read
+    S[0] = bload16(c_.w1, c_.woff[0], kb);
+    S[1] = bload16(GATEUP ? c_.w3 : c_.w1, c_.woff[1], kb);
+  };
+  auto load_a = [&](int c) {
+    const uint32_t cb = (uint32_t)(c < nc ? c : nc - 1) * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) AR[i] = bload16(c_.act, c_.aoff[i], cb);
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      *reinterpret_cast<u32x4_t*>(lds + buf * BM * PITCH + c_.adst + i * 64 * PITCH) = AR[i];
+  };
+  auto mma_step = [&](int buf, int kk, const u32x4_t* S) {
+    constexpr int GS = 2;                     // fragments per read group
+    const uint16_t* As = lds + buf * BM * PITCH + kk * 32 + q * 8 + r * PITCH;
+    u32x4_t G0[GS], G1[GS];
+#pragma unroll
+    for (int j = 0; j < GS; ++j) G0[j] = *reinterpret_cast<const u32x4_t*>(As + 16 * j * PITCH);
+#pragma unroll
+    for (int g = 0; g < NL / GS; ++g) {
+      u32x4_t* cur = (g & 1) ? G1 : G0;
+      u32x4_t* nxt = (g & 1) ? G0 : G1;
+      if (g + 1 < NL / GS) {
+#pragma unroll
+        for (int j = 0; j < GS; ++j)
+          nxt[j] = *reinterpret_cast<const u32x4_t*>(As + 16 * (GS * (g + 1) + j) * PITCH);
+      }
+#pragma unroll
+      for (int j = 0; j < GS; ++j) {
+        acc[GS * g + j][0] = mfma16x16x32(S[0], cur[j], acc[GS * g + j][0]);
+        acc[GS * g + j][1] = mfma16x16x32(S[1], cur[j], acc[GS * g + j][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // one k-step: refill the slot freed by the previous step, then multiply this one
+  auto kstep = [&](int buf, int kk, const u32x4_t* use, u32x4_t* fill, int ks_fill) {
+    load_w(fill, ks_fill);
+    mma_step(buf, kk, use);
+  };
+  // chunk c+1's activations (in AR) go to the other LDS buffer; AR then loads chunk c+2
+  auto next_chunk = [&](int c) {
+    store_a((c + 1) & 1);
+    load_a(c + 2);
+    lds_barrier();
+  };
+
+  load_a(0);
+  load_w(W0, 0);
+  load_w(W1, 1);
+  load_w(W2, 2);
+  load_w(W3, 3);
+  load_w(W4, 4);
+  store_a(0);
+  load_a(1);
+  lds_barrier();
+  int c = 0;
+  // at the top of an iteration W0..W4 hold k-steps 2c .. 2c+4 and W5 is free
+  for (; c + 3 <= nc; c += 3) {
+    const int k0 = 2 * c;
+    kstep(c & 1, 0, W0, W5, k0 + 5);
+    kstep(c & 1, 1, W1, W0, k0 + 6);
+    next_chunk(c);
+    kstep((c + 1) & 1, 0, W2, W1, k0 + 7);
+    kstep((c + 1) & 1, 1, W3, W2, k0 + 8);
+    next_chunk(c + 1);
+    kstep((c + 2) & 1, 0, W4, W3, k0 + 9);
+    kstep((c + 2) & 1, 1, W5, W4, k0 + 10);
+    next_chunk(c + 2);
+  }
+  if (c < nc) {
+    const int k0 = 2 * c;
+    kstep(c & 1, 0, W0, W5, k0 + 5);
+    kstep(c & 1, 1, W1, W0, k0 + 6);
+    next_chunk(c);
+    if (c + 1 < nc) {
+      kstep((c + 1) & 1, 0, W2, W1, k0 + 7);
+      kstep((c + 1) & 1, 1, W3, W2, k0 + 8);
+      next_chunk(c + 1);
+    }
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(512, 1) void ffn_stream_kernel(const FfnArgs a) {
+  constexpr int BM = 256, BK = 64, PITCH = BK + 8;
+  constexpr int FM = BM / 16;                 // row fragments (every wave has all rows)
+  constexpr int NW = 2;                       // weight fragments per wave per k-step
+  constexpr int FEAT_WAVE = GATEUP ? 16 : 32; // features of N per wave
+  constexpr int FEAT = 8 * FEAT_WAVE;         // features of N per workgroup
+  constexpr int NT = 512;                     // threads
+  constexpr int NA = BM * BK / 8 / NT;        // 16-byte activation pieces per thread (4)
+  static_assert(NA == 4 && FM == 16, "stream tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * PITCH];
 
   Tile tile;
   int nb;
-  if (!map_work(a, (a.N + BN - 1) / BN, tile, nb)) return;
+  if (!map_work(a, (a.N + FEAT - 1) / FEAT, tile, nb)) return;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, q = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
   const int K = a.K, N = a.N;
-  const int n_base = nb * BN;
   const int nrows = tile.row_end - tile.row_begin;
+  const int n_wave = nb * FEAT + wave * FEAT_WAVE;
 
   const bool is_shared = tile.group >= a.E;
   const int64_t wofs = (int64_t)tile.group * N * K;
   const uint16_t* W1 = is_shared ? a.S1 : a.B1 + wofs;
   const uint16_t* W3 = GATEUP ? (is_shared ? a.S3 : a.B3 + wofs) : nullptr;
 
-  // this thread's 16-byte pieces of a stage: row (tid >> 3) + 32 i, chunk tid & 7
-  const int prow = tid >> 3, pch = tid & 7;
-  const uint16_t* src[NC];
-  int dst[NC];
+  StreamCtx ctx;
+  // one weight matrix is N*K*2 < 2^32 bytes (checked on the host)
+  const uint32_t wbytes = (uint32_t)N * (uint32_t)K * 2u;
+  ctx.w1 = buffer_rsrc(W1, wbytes);
+  ctx.w3 = buffer_rsrc(GATEUP ? W3 : W1, wbytes);
+  // gate/up gathers rows of x (T*K*2 < 2^32 bytes, checked on the host); down reads the
+  // tile's own contiguous rows of h
+  const uint16_t* abase = GATEUP ? a.A : a.A + (int64_t)tile.row_begin * K;
+  const uint32_t abytes = GATEUP ? (uint32_t)(a.a_rows * K * 2) : (uint32_t)nrows * K * 2u;
+  ctx.act = buffer_rsrc(abase, abytes);
+  // weight fragment f: gate/up: f = 0 -> W1 rows, f = 1 -> the same rows of W3;
+  // down: 16 rows each
 #pragma unroll
-  for (int i = 0; i < NCA; ++i) {
-    const int m = prow + 32 * i;
+  for (int f = 0; f < NW; ++f) {
+    int n = n_wave + (GATEUP ? 0 : 16 * f) + r;
+    if (n > N - 1) n = N - 1;
+    ctx.woff[f] = ((uint32_t)n * (uint32_t)K + q * 8) * 2u;
+  }
+  // activation pieces of this thread: row (tid >> 3) + 64 i, 16-byte chunk tid & 7
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int m = (tid >> 3) + (NT / 8) * i;
     int64_t p = tile.row_begin + m;
     if (p >= tile.row_end) p = tile.row_end - 1;
-    src[i] = act_row(a, GATEUP, p) + pch * 8;
-    dst[i] = m * PITCH + pch * 8;
+    ctx.aoff[i] = (uint32_t)(act_row(a, GATEUP, p) - abase) * 2u + (tid & 7) * 16;
   }
-#pragma unroll
-  for (int i = 0; i < NCW; ++i) {
-    const int wr = prow + 32 * i;
-    const bool second = GATEUP && wr >= BN;
-    int n = n_base + (second ? wr - BN : wr);
-    if (n > N - 1) n = N - 1;
-    src[NCA + i] = (second ? W3 : W1) + (int64_t)n * K + pch * 8;
-    dst[NCA + i] = (BM + wr) * PITCH + pch * 8;
-  }
+  ctx.adst = (tid >> 3) * PITCH + (tid & 7) * 8;
+  ctx.nks = K / 32;
+  ctx.nc = K / BK;
 
-  f32x4_t acc1[FM][FN], acc3[FM][FN];
+  f32x4_t acc[FM][NW];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      acc1[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      acc3[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  bool live[FM];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) live[i] = wm * WM + 16 * i < nrows;
+    for (int f = 0; f < NW; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
-  u32x4_t R0[NC], R1[NC], R2[NC];
-
-#define WIDE_ISSUE(R, kt)                                            \
-  _Pragma("unroll") for (int c = 0; c < NC; ++c) R[c] = load16(src[c] + (int64_t)(kt) * BK);
-#define WIDE_COMMIT(R, buf)                                          \
-  _Pragma("unroll") for (int c = 0; c < NC; ++c)                    \
-      *reinterpret_cast<u32x4_t*>(lds + (buf) * STAGE + dst[c]) = R[c];
-
-  auto compute = [&](int buf) {
-    const uint16_t* As = lds + buf * STAGE;
-    const uint16_t* Ws = As + BM * PITCH;
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      u32x4_t af[FM], w1f[FN], w3f[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const u32x4_t*>(As + (wm * WM + 16 * i + r) * PITCH + ks * 32 + q * 8);
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        w1f[f] = *reinterpret_cast<const u32x4_t*>(Ws + (wn * WN + 16 * f + r) * PITCH + ks * 32 + q * 8);
-        if (GATEUP)
-          w3f[f] = *reinterpret_cast<const u32x4_t*>(Ws + (BN + wn * WN + 16 * f + r) * PITCH + ks * 32 + q * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        if (!live[i]) continue;
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          acc1[i][f] = mfma16x16x32(w1f[f], af[i], acc1[i][f]);
-          if (GATEUP) acc3[i][f] = mfma16x16x32(w3f[f], af[i], acc3[i][f]);
-        }
-      }
-    }
-  };
-
-#define WIDE_STEP(kt, Rfree, Rnext)                                  \
-  {                                                                  \
-    if ((kt) + 3 < nk) { WIDE_ISSUE(Rfree, (kt) + 3) }               \
-    compute((kt) & 1);                                               \
-    if ((kt) + 1 < nk) { WIDE_COMMIT(Rnext, ((kt) + 1) & 1) }        \
-    __syncthreads();                                                 \
+  const int ngroups = (nrows + 63) / 64;      // workgroup-uniform, 1..4
+  switch (ngroups) {
+    case 1: stream_loop<GATEUP, 4>(ctx, lds, acc); break;
+    case 2: stream_loop<GATEUP, 8>(ctx, lds, acc); break;
+    case 3: stream_loop<GATEUP, 12>(ctx, lds, acc); break;
+    default: stream_loop<GATEUP, 16>(ctx, lds, acc); break;
   }
 
-  WIDE_ISSUE(R0, 0)
-  if (nk > 1) { WIDE_ISSUE(R1, 1) }
-  if (nk > 2) { WIDE_ISSUE(R2, 2) }
-  WIDE_COMMIT(R0, 0)
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 3) {
-    WIDE_STEP(kt, R0, R1)
-    if (kt + 1 < nk) WIDE_STEP(kt + 1, R1, R2)
-    if (kt + 2 < nk) WIDE_STEP(kt + 2, R2, R0)
-  }
-#undef WIDE_STEP
-#undef WIDE_COMMIT
-#undef WIDE_ISSUE
-
-  // epilogue: fragment (i, f) of this lane = row wm*WM + 16 i + r, features
-  // n_base + wn*WN + 16 f + 4 q .. +3
+  // epilogue: acc[i][f] of this lane = tile row 16 i + r, features 4 q .. 4 q + 3 of
+  // weight fragment f
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = wm * WM + 16 * i + r;
+    const int m = 16 * i + r;
     if (m >= nrows) continue;
     const int64_t p = tile.row_begin + m;
+    if (GATEUP) {
+      const int nn = n_wave + 4 * q;
+      if (nn < N) store_gateup(a.C + p * N + nn, acc[i][0], acc[i][1]);
+    } else {
+      float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int nn = n_base + wn * WN + 16 * f + 4 * q;
-      if (nn >= N) continue;
-      if (GATEUP) {
-        store_gateup(a.C + p * N + nn, acc1[i][f], acc3[i][f]);
-      } else {
-        float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
-        *reinterpret_cast<f32x4_t*>(yrow + nn) = acc1[i][f];
+      for (int f = 0; f < NW; ++f) {
+        const int nn = n_wave + 16 * f + 4 * q;
+        if (nn < N) *reinterpret_cast<f32x4_t*>(yrow + nn) = acc[i][f];
       }
     }
   }
 }
 
 constexpr int kSkinnyBM = 16;
-constexpr int kWideBM = 128;
+constexpr int kStreamBM = 256;
 constexpr int kSkinnyNF = 2;       // skinny: 4 waves x 2 fragments = 128 features per block
 constexpr int kSkinnyKU = 8;       // skinny: k-steps (of 32) per batch of loads
-constexpr int kWideBNGateUp = 64;  // wide: features per block (x2 weight matrices)
-constexpr int kWideBNDown = 128;
+constexpr int kStreamBNGateUp = 128;  // stream: features of N per block (x2 weight matrices)
+constexpr int kStreamBNDown = 256;
 
 int64_t max_tiles_for(const FfnShape& sh, int BM) {
   // sum_e ceil(c_e / BM) <= (T*k) / BM + E, plus the shared expert's ceil(T / BM)
   return sh.T * sh.k / BM + sh.E + (sh.shared ? (sh.T + BM - 1) / BM : 0) + 1;
 }
 
-// Average rows per routed expert decides the kernel: a few (decode) -> skinny stream;
-// many (prefill) -> wide LDS-tiled kernel.
+// Average rows per routed expert decides the kernel: a few (decode) -> skinny kernel;
+// many (prefill) -> 128-row stream kernel.
 bool use_wide(const FfnShape& sh) { return sh.T * sh.k > (int64_t)16 * sh.E; }
 
 hipError_t tiles_launch(const FfnShape& sh, const int32_t* offsets, int BM, Tile* tiles,
@@ -431,16 +496,46 @@ dim3 grid_for(const FfnShape& sh, int BM, int BN, int N) {
 
 int64_t ffn_max_tiles(const FfnShape& sh) { return max_tiles_for(sh, kSkinnyBM); }
 
+hipError_t launch_dense_f32(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
+                            float* C, Tile* tiles, int32_t* ntiles, hipStream_t s) {
+  // one group (the "shared" slot of the tile list) whose rows are all the rows of A
+  const FfnShape sh{rows, K, 0, 0, N, true};
+  const bool wide = rows > 512;
+  const int BM = wide ? kStreamBM : kSkinnyBM;
+  hipError_t err = tiles_launch(sh, nullptr, BM, tiles, ntiles, s);
+  if (err != hipSuccess) return err;
+  FfnArgs a{};
+  a.A = A;
+  a.a_rows = rows;
+  a.routed_rows = 0;
+  a.S1 = W;
+  a.Ys = C;
+  a.tiles = tiles;
+  a.ntiles = ntiles;
+  a.k = 1;
+  a.N = N;
+  a.K = K;
+  a.E = 0;
+  if (wide)
+    hipLaunchKernelGGL(ffn_stream_kernel<false>, grid_for(sh, BM, kStreamBNDown, N), dim3(512), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, false>), grid_for(sh, BM, 64, N),
+                       dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                           const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, Tile* tiles,
                           int32_t* ntiles, hipStream_t s) {
   const bool wide = use_wide(sh);
-  const int BM = wide ? kWideBM : kSkinnyBM;
+  const int BM = wide ? kStreamBM : kSkinnyBM;
   hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
   if (err != hipSuccess) return err;
   FfnArgs a{};
   a.A = x;
+  a.a_rows = sh.T;
   a.perm = perm;
   a.routed_rows = sh.T * sh.k;
   a.B1 = w1;
@@ -455,8 +550,8 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   a.K = sh.d;
   a.E = sh.E;
   if (wide)
-    hipLaunchKernelGGL((ffn_wide_kernel<kWideBNGateUp, true>),
-                       grid_for(sh, BM, kWideBNGateUp, a.N), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(ffn_stream_kernel<true>, grid_for(sh, BM, kStreamBNGateUp, a.N), dim3(512),
+                       0, s, a);
   else
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, true>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
@@ -467,11 +562,12 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
                        const uint16_t* w2, const uint16_t* ws2, float* y_routed,
                        float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s) {
   const bool wide = use_wide(sh);
-  const int BM = wide ? kWideBM : kSkinnyBM;
+  const int BM = wide ? kStreamBM : kSkinnyBM;
   hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
   if (err != hipSuccess) return err;
   FfnArgs a{};
   a.A = h;
+  a.a_rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
   a.perm = nullptr;
   a.routed_rows = sh.T * sh.k;
   a.B1 = w2;
@@ -487,8 +583,8 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.K = sh.I;
   a.E = sh.E;
   if (wide)
-    hipLaunchKernelGGL((ffn_wide_kernel<kWideBNDown, false>),
-                       grid_for(sh, BM, kWideBNDown, a.N), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(ffn_stream_kernel<false>, grid_for(sh, BM, kStreamBNDown, a.N), dim3(512),
+                       0, s, a);
   else
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, false>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);

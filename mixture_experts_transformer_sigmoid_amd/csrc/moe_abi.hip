@@ -31,11 +31,18 @@ moe_status check_dims(const moe_dims* dp) {
   if (d.d_shared != 0 && d.d_shared != d.d_expert) return MOE_EUNSUPPORTED;
   // grouped rows (T*k routed + T shared) are indexed with int32
   if (d.tokens > (int64_t)(INT32_MAX / 2) / (d.top_k + 1)) return MOE_EUNSUPPORTED;
+  // the GEMM kernels address x, one expert's weight matrix and the split router matrix
+  // through 32-bit byte offsets
+  const uint64_t lim = (uint64_t)UINT32_MAX;
+  if ((uint64_t)d.tokens * d.d_model * 2 > lim) return MOE_EUNSUPPORTED;
+  if ((uint64_t)d.d_model * d.d_expert * 2 > lim) return MOE_EUNSUPPORTED;
+  if ((uint64_t)3 * d.n_experts * d.d_model * 2 > lim) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
 struct Layout {
-  size_t z, idx, w, counts, offsets, perm, inv, hist, base, tiles, ntiles, h, y, total;
+  size_t zpart, wsplit, idx, w, counts, offsets, perm, inv, hist, base, tiles, ntiles, h, y,
+      total;
 };
 
 Layout layout(const moe_dims& d) {
@@ -52,7 +59,8 @@ Layout layout(const moe_dims& d) {
     off += align_up(bytes);
     return o;
   };
-  L.z = take(T * E * 4);
+  L.zpart = take(T * 3 * E * 4);
+  L.wsplit = take(3 * E * (size_t)d.d_model * 2);
   L.idx = take(slots * 4);
   L.w = take(slots * 4);
   L.counts = take(E * 4);
@@ -98,9 +106,12 @@ FfnShape ffn_shape(const moe_dims& d) {
   } while (0)
 
 moe_status route_impl(const moe_dims& d, const uint16_t* x, const float* w_r, const float* b,
-                      int32_t* idx, float* w, float* logits, hipStream_t s) {
+                      int32_t* idx, float* w, float* logits, void* ws, hipStream_t s) {
+  const Layout L = layout(d);
   return hip_status(moe::launch_router(x, w_r, b, d.tokens, d.d_model, d.n_experts, d.top_k,
-                                       d.routed_scale, logits, idx, w, s));
+                                       d.routed_scale, at<uint16_t>(ws, L.wsplit),
+                                       at<float>(ws, L.zpart), at<Tile>(ws, L.tiles),
+                                       at<int32_t>(ws, L.ntiles), logits, idx, w, s));
 }
 
 moe_status permute_impl(const moe_dims& d, const int32_t* idx, int32_t* counts, int32_t* offsets,
@@ -168,14 +179,10 @@ moe_status moe_route(const moe_dims* dims, const uint16_t* x, const float* w_rou
   if (d.tokens == 0) return MOE_OK;
   MOE_NEED(aligned(x, 16) && aligned(w_router, 16) && aligned(bias, 4));
   MOE_NEED(aligned(topk_idx, 4) && aligned(topk_w, 4));
-  if (logits == nullptr) {
-    MOE_TRY(check_ws(d, ws, ws_bytes));
-    logits = at<float>(ws, layout(d).z);
-  } else {
-    MOE_NEED(aligned(logits, 4));
-  }
+  if (logits != nullptr) MOE_NEED(aligned(logits, 4));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
   (void)hipGetLastError();
-  return route_impl(d, x, w_router, bias, topk_idx, topk_w, logits, (hipStream_t)stream);
+  return route_impl(d, x, w_router, bias, topk_idx, topk_w, logits, ws, (hipStream_t)stream);
 }
 
 moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* counts,
@@ -273,7 +280,7 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
   uint16_t* h = at<uint16_t>(ws, L.h);
   float* y_routed = at<float>(ws, L.y);
   float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
-  MOE_TRY(route_impl(d, x, w_router, bias, idx, w, at<float>(ws, L.z), s));
+  MOE_TRY(route_impl(d, x, w_router, bias, idx, w, nullptr, ws, s));
   MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s));
   MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s));
   MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s));

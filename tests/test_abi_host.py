@@ -64,6 +64,7 @@ def test_workspace_bytes_grow_with_tokens():
     (dict(tokens=-1), M.MOE_EINVAL),
     (dict(routed_scale=float("nan")), M.MOE_EINVAL),
     (dict(tokens=1 << 40), M.MOE_EUNSUPPORTED),
+    (dict(tokens=300_000), M.MOE_EUNSUPPORTED),          # x would need 4 GiB or more
 ])
 def test_bad_dims_rejected(bad, code):
     kw = dict(tokens=128, d_model=7168, n_experts=384, top_k=8, d_expert=2048, d_shared=2048,
