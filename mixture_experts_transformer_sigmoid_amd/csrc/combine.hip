@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kCombineThreads = 256;
 
+template <int KMAX>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ y_routed, const int32_t* __restrict__ inv,
     const float* __restrict__ topk_w, const float* __restrict__ y_shared,
@@ -22,17 +23,39 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int c = ((int)(blockIdx.x % nchunk) * kCombineThreads + threadIdx.x) * 8;
   if (t >= T || c >= d) return;
   const int64_t slots = T * k;
+  // all slot indices and weights first, then every row load in flight together
+  int32_t p[KMAX];
+  float w[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    p[s] = -1;
+    w[s] = 0.0f;
+    if (s < k) {
+      p[s] = inv[t * k + s];
+      w[s] = topk_w[t * k + s];
+    }
+  }
+  f32x4_t ra[KMAX], rb[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (p[s] >= 0 && p[s] < slots) {
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y_routed + (int64_t)p[s] * d + c);
+      ra[s] = src[0];
+      rb[s] = src[1];
+    } else {
+      ra[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      rb[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      w[s] = 0.0f;
+    }
+  }
   f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < k; ++s) {
-    const int32_t p = inv[t * k + s];
-    if (p < 0 || p >= slots) continue;
-    const float w = topk_w[t * k + s];
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y_routed + (int64_t)p * d + c);
-    const f32x4_t a = src[0], b = src[1];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (s >= k) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lo[i] = fmaf(w, a[i], lo[i]);
-      hi[i] = fmaf(w, b[i], hi[i]);
+      lo[i] = fmaf(w[s], ra[s][i], lo[i]);
+      hi[i] = fmaf(w[s], rb[s][i], hi[i]);
     }
   }
   if (y_shared != nullptr) {
@@ -56,8 +79,8 @@ hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float
   if (T <= 0) return hipSuccess;
   const int64_t nchunk = (d / 8 + kCombineThreads - 1) / kCombineThreads;
   dim3 grid((unsigned)(nchunk * T));
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, y_routed, inv, topk_w,
-                     y_shared, out, T, d, k);
+  hipLaunchKernelGGL(combine_kernel<kMaxTopK>, grid, dim3(kCombineThreads), 0, s, y_routed, inv,
+                     topk_w, y_shared, out, T, d, k);
   return hipGetLastError();
 }
 

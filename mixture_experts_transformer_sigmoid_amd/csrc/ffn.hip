@@ -256,31 +256,48 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
 // load the same weights.  Weights stream from HBM straight into MFMA registers, the same
 // operand layout as the skinny kernel, through a ring of six k-step register sets: five
 // k-steps (10 KiB per wave, 80 KiB per CU) are in flight while one is multiplied.  The
-// tile's activation rows are staged in LDS in 64-wide k-chunks (row pitch 144 B:
-// conflict-free MFMA reads and chunk writes), double-buffered, with one LDS-only barrier
-// per chunk (it does not drain the weight loads in flight).  Activation fragments are
-// read from LDS two at a time, one group ahead of the four MFMAs that use them.
+// tile's activation rows are staged in LDS in 64-wide k-chunks, double-buffered, with one
+// LDS-only barrier per chunk (it does not drain the weight loads in flight).  Within a
+// buffer the 16-byte pieces are stored k-chunk-major with the row index XOR-swizzled by
+// the chunk (slot = c * 256 + (m ^ 2c)), so the 16 lanes of an MFMA operand read (16 rows,
+// one chunk) and of a chunk write (2 rows x 8 chunks) touch 16 distinct bank groups.  Activation fragments are
+// read from LDS one at a time, one fragment ahead of the two MFMAs that use it.
 // The main loop is straight-line code: it is instantiated for 4, 8, 12 or 16 live row
 // fragments (the tile's rows rounded up to 64: rows past the end cost at most three
-// fragments of MFMAs), prefetch indices are clamped instead of guarded, and three chunks
+// fragments of MFMAs; finer steps measured slower, the extra copies of the loop crowd the
+// instruction cache), prefetch indices are clamped instead of guarded, and three chunks
 // are unrolled per iteration so the register ring is indexed statically.  Branches inside
 // the loop would make the compiler's wait-count analysis conservative at every join and
 // wait for the prefetched loads too.
+// Tuning constants of the stream kernel, measured on MI355X at the K2 prefill shape
+// (gate/up, ms): 64-row granules 6.33 vs 128-row 6.95 vs none 6.60; read groups of 1
+// fragment 6.33, 2: 6.34, 4: 6.88; without the scheduling barrier 8.40.
+#ifndef MOE_STREAM_NL_STEP
+#define MOE_STREAM_NL_STEP 4      // live row fragments are rounded up to this multiple
+#endif
+#ifndef MOE_STREAM_GS
+#define MOE_STREAM_GS 1           // activation fragments read from LDS per group
+#endif
+#ifndef MOE_STREAM_SCHED_BARRIER
+#define MOE_STREAM_SCHED_BARRIER 1  // keep reads one group ahead of their MFMAs
+#endif
+
 struct StreamCtx {
   __amdgpu_buffer_rsrc_t w1;   // matrix of weight fragment 0 (and 1 unless gate/up)
   __amdgpu_buffer_rsrc_t w3;   // gate/up: matrix of weight fragment 1
   __amdgpu_buffer_rsrc_t act;  // activation rows (x, or the tile's rows of h)
   uint32_t woff[2];            // byte offset of the lane's row and k lane-group, per fragment
   uint32_t aoff[4];            // byte offset of each activation piece (row start + chunk)
-  int adst;                    // LDS offset (elements) of the first activation piece; piece
-                               // i sits 64 i rows further
+  int adst;                    // LDS offset (elements) of the first activation piece; the
+                               // XOR touches bits 1..3 of the row only, so piece i (row
+                               // + 64 i) sits 64 i slots further
   int nks, nc;                 // k-steps (32) and chunks (64)
 };
 
 template <bool GATEUP, int NL>
 __device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
                                             f32x4_t (&acc)[16][2]) {
-  constexpr int BM = 256, BK = 64, PITCH = BK + 8, NW = 2, NA = 4;
+  constexpr int BM = 256, BK = 64, NW = 2, NA = 4;
   const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const int nks = c_.nks, nc = c_.nc;
   u32x4_t W0[NW], W1[NW], W2[NW], W3[NW], W4[NW], W5[NW], AR[NA];
@@ -298,14 +315,17 @@ __device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      *reinterpret_cast<u32x4_t*>(lds + buf * BM * PITCH + c_.adst + i * 64 * PITCH) = AR[i];
+      *reinterpret_cast<u32x4_t*>(lds + buf * BM * BK + c_.adst + i * 64 * 8) = AR[i];
   };
+  // slot of (row m, 8-element k-chunk c) = c * BM + (m ^ 2c): a lane's fragment read is
+  // row 16 i + r of chunk c = 4 kk + q, i.e. slot c * BM + 16 i + (r ^ 2c)
   auto mma_step = [&](int buf, int kk, const u32x4_t* S) {
-    constexpr int GS = 2;                     // fragments per read group
-    const uint16_t* As = lds + buf * BM * PITCH + kk * 32 + q * 8 + r * PITCH;
+    constexpr int GS = MOE_STREAM_GS;         // fragments per read group
+    const int c = 4 * kk + q;
+    const uint16_t* As = lds + buf * BM * BK + (c * BM + (r ^ (2 * c))) * 8;
     u32x4_t G0[GS], G1[GS];
 #pragma unroll
-    for (int j = 0; j < GS; ++j) G0[j] = *reinterpret_cast<const u32x4_t*>(As + 16 * j * PITCH);
+    for (int j = 0; j < GS; ++j) G0[j] = *reinterpret_cast<const u32x4_t*>(As + 16 * j * 8);
 #pragma unroll
     for (int g = 0; g < NL / GS; ++g) {
       u32x4_t* cur = (g & 1) ? G1 : G0;
@@ -313,14 +333,14 @@ __device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
       if (g + 1 < NL / GS) {
 #pragma unroll
         for (int j = 0; j < GS; ++j)
-          nxt[j] = *reinterpret_cast<const u32x4_t*>(As + 16 * (GS * (g + 1) + j) * PITCH);
+          nxt[j] = *reinterpret_cast<const u32x4_t*>(As + 16 * (GS * (g + 1) + j) * 8);
       }
 #pragma unroll
       for (int j = 0; j < GS; ++j) {
         acc[GS * g + j][0] = mfma16x16x32(S[0], cur[j], acc[GS * g + j][0]);
         acc[GS * g + j][1] = mfma16x16x32(S[1], cur[j], acc[GS * g + j][1]);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (MOE_STREAM_SCHED_BARRIER) __builtin_amdgcn_sched_barrier(0);
     }
   };
   // one k-step: refill the slot freed by the previous step, then multiply this one
@@ -371,9 +391,23 @@ __device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
   }
 }
 
+// stream_loop instantiated for the smallest multiple of STEP fragments >= nfrag
+template <bool GATEUP, int STEP, int NL = STEP>
+__device__ __forceinline__ void stream_dispatch(int nfrag, const StreamCtx& ctx, uint16_t* lds,
+                                                f32x4_t (&acc)[16][2]) {
+  if constexpr (NL >= 16) {
+    stream_loop<GATEUP, 16>(ctx, lds, acc);
+  } else {
+    if (nfrag <= NL)
+      stream_loop<GATEUP, NL>(ctx, lds, acc);
+    else
+      stream_dispatch<GATEUP, STEP, NL + STEP>(nfrag, ctx, lds, acc);
+  }
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(512, 1) void ffn_stream_kernel(const FfnArgs a) {
-  constexpr int BM = 256, BK = 64, PITCH = BK + 8;
+  constexpr int BM = 256, BK = 64;
   constexpr int FM = BM / 16;                 // row fragments (every wave has all rows)
   constexpr int NW = 2;                       // weight fragments per wave per k-step
   constexpr int FEAT_WAVE = GATEUP ? 16 : 32; // features of N per wave
@@ -381,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void ffn_stream_kernel(const FfnArgs a) {
   constexpr int NT = 512;                     // threads
   constexpr int NA = BM * BK / 8 / NT;        // 16-byte activation pieces per thread (4)
   static_assert(NA == 4 && FM == 16, "stream tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * BK];
 
   Tile tile;
   int nb;
@@ -424,7 +458,7 @@ __global__ __launch_bounds__(512, 1) void ffn_stream_kernel(const FfnArgs a) {
     if (p >= tile.row_end) p = tile.row_end - 1;
     ctx.aoff[i] = (uint32_t)(act_row(a, GATEUP, p) - abase) * 2u + (tid & 7) * 16;
   }
-  ctx.adst = (tid >> 3) * PITCH + (tid & 7) * 8;
+  ctx.adst = ((tid & 7) * BM + ((tid >> 3) ^ (2 * (tid & 7)))) * 8;
   ctx.nks = K / 32;
   ctx.nc = K / BK;
 
@@ -434,13 +468,9 @@ __global__ __launch_bounds__(512, 1) void ffn_stream_kernel(const FfnArgs a) {
 #pragma unroll
     for (int f = 0; f < NW; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int ngroups = (nrows + 63) / 64;      // workgroup-uniform, 1..4
-  switch (ngroups) {
-    case 1: stream_loop<GATEUP, 4>(ctx, lds, acc); break;
-    case 2: stream_loop<GATEUP, 8>(ctx, lds, acc); break;
-    case 3: stream_loop<GATEUP, 12>(ctx, lds, acc); break;
-    default: stream_loop<GATEUP, 16>(ctx, lds, acc); break;
-  }
+  // live row fragments rounded up to a multiple of MOE_STREAM_NL_STEP (workgroup-uniform)
+  const int nfrag = (nrows + 15) / 16;
+  stream_dispatch<GATEUP, MOE_STREAM_NL_STEP>(nfrag, ctx, lds, acc);
 
   // epilogue: acc[i][f] of this lane = tile row 16 i + r, features 4 q .. 4 q + 3 of
   // weight fragment f
