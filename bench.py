@@ -95,6 +95,7 @@ def parse():
     ap.add_argument("--workload", default="k2_decode", choices=["k2_decode", "k2_prefill"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-latent", action="store_true", help="skip the latent-MoE figure")
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens in the oracle sample")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two --pmc counter CSVs and exit")
@@ -178,6 +179,44 @@ def time_gate_up(M, torch, dims, inp, st, ws, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
+
+
+def time_latent(M, torch, S, dev, steps):
+    """moe_forward_latent at the latent-MoE shape: T=4096, d=7168, L=3584, 384 experts."""
+    cfg = S.CONFIGS["latent"]
+    inp = S.make_inputs(cfg, dev)
+    dims = M.dims_for(cfg)
+    L, T, d, I, Is, E, k = (cfg["d_latent"], cfg["tokens"], cfg["d_model"], cfg["d_expert"],
+                            cfg["d_shared"], cfg["n_experts"], cfg["top_k"])
+    ws = M.latent_workspace(dims, L, dev)
+    out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+
+    def call():
+        M.moe_forward_latent(dims, L, inp["x"], inp["w_r"], inp["b"], inp["w_down"], inp["w1"],
+                             inp["w3"], inp["w2"], inp["w_up"], inp["ws1"], inp["ws3"], inp["ws2"],
+                             out, ws)
+    call()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    # every routed expert is active at this batch (checked by the parity test's counts)
+    byts = (E * 3 * L * I * 2 + 2 * d * L * 2 + 3 * d * Is * 2 + E * d * 4 + E * 4
+            + T * d * 2 + T * d * 2)
+    flops = 2 * T * d * L * 2 + 2 * 3 * L * I * T * k + 2 * 3 * d * Is * T
+    del inp, ws
+    torch.cuda.empty_cache()
+    return {"workload": "latent MoE: T=4096, d=7168, latent 3584, 384 experts top-8, I=2048, "
+                        "RMSNorm, up-projection, shared expert on 7168",
+            "steps": steps, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "hbm_gbs": byts / (ms * 1e-3) / 1e9, "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
 def cpu_baseline(torch, S, cfg, inp, n_tok):
@@ -303,6 +342,18 @@ def main():
         log(f"timing the CPU oracle on {args.cpu_sample} tokens")
         res["cpu_baseline"] = cpu_baseline(torch, S, cfg, inp, args.cpu_sample)
         log(f"cpu oracle: {res['cpu_baseline']['value']:.2f} tok/s on {res['cpu_baseline']['cores']} threads")
+    if not args.no_latent:
+        # latent variant (experts on a 3584-wide latent), 4096 tokens; its own weights
+        del weights
+        for key in list(inp):
+            del inp[key]
+        torch.cuda.empty_cache()
+        lres = time_latent(M, torch, S, dev, max(3, min(args.steps, 10)))
+        res["latent"] = lres
+        log(f"latent: {lres['ms_per_step']:.3f} ms/step, {lres['tokens_per_s']:.0f} tok/s, "
+            f"{lres['hbm_gbs']:.0f} GB/s, {lres['mfma_tflops']:.0f} TFLOP/s")
+        inp = None
+
     print(json.dumps(res), flush=True)
 
 

@@ -149,6 +149,24 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
                        const uint16_t* ws2, uint16_t* out, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* Latent mixture of experts ("Kimi K3 · Latent up-projection": the router scores the
+ * full-width input; the input is projected down to the latent width; the routed experts
+ * run on the latent; their gate-weighted sum is RMS-normalised and projected back up; the
+ * shared expert runs on the full-width input and is added):
+ *   z, s, sel, G as in moe_route on x;  l = x W_down^T  [T, L] (bf16);
+ *   u = sum_i G_i E_i(l) (experts on width L);  u_hat = u / sqrt(mean(u^2) + 1e-6)
+ *   (unit gain);  out = bf16(u_hat W_up^T + y_shared(x))
+ *   w_down [L, d] bf16; w1, w3 [E, I, L]; w2 [E, L, I]; w_up [d, L] bf16; shared expert
+ *   [Is, d] / [d, Is] on the full width; out [T, d] bf16.  d_latent: multiple of 64,
+ *   at most 8192.  Workspace from moe_latent_workspace_bytes. */
+moe_status moe_latent_workspace_bytes(const moe_dims* dims, int32_t d_latent, size_t* bytes);
+moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint16_t* x,
+                              const float* w_router, const float* bias, const uint16_t* w_down,
+                              const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                              const uint16_t* w_up, const uint16_t* ws1, const uint16_t* ws3,
+                              const uint16_t* ws2, uint16_t* out, void* ws, size_t ws_bytes,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

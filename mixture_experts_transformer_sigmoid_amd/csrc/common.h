@@ -103,9 +103,12 @@ struct FfnShape {
 
 int64_t ffn_max_tiles(const FfnShape& sh);
 
-// C[rows, N] (fp32) = A[rows, K] . W[N, K]^T with the grouped-GEMM kernels (one group).
-hipError_t launch_dense_f32(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
-                            float* C, Tile* tiles, int32_t* ntiles, hipStream_t s);
+// Dense C[rows, N] = A[rows, K] . W[N, K]^T with the grouped-GEMM kernels (one group):
+// fp32 into Cf; bf16 into Cb; or bf16(C + R) into Cb with R [rows, N] fp32.
+enum class DenseOut { kF32, kBF16, kAddBF16 };
+hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
+                        DenseOut mode, float* Cf, uint16_t* Cb, const float* R, Tile* tiles,
+                        int32_t* ntiles, hipStream_t s);
 
 hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
@@ -119,5 +122,11 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
 hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float* topk_w,
                           const float* y_shared, uint16_t* out, int64_t T, int d, int k,
                           hipStream_t s);
+
+// out[t] = bf16(RMSNorm(sum_slot topk_w * y_routed[inv])) over L features (L <= 8192).
+hipError_t launch_combine_rmsnorm(const float* y_routed, const int32_t* inv, const float* topk_w,
+                                  uint16_t* out, int64_t T, int L, int k, float eps,
+                                  hipStream_t s);
+constexpr int kMaxLatent = 8192;
 
 }  // namespace moe

@@ -25,6 +25,14 @@
 namespace moe {
 namespace {
 
+// Epilogue of a GEMM launch.
+enum Epi : int {
+  kSwiGLU = 0,   // two weight matrices (W1, W3): h = bf16(silu(g) * u) into C
+  kF32 = 1,      // fp32 rows into Y (grouped rows) or Ys (the last group's rows)
+  kBF16 = 2,     // bf16 rows into C
+  kAddBF16 = 3,  // bf16(acc + R[row]) into C, R fp32 with the same layout
+};
+
 struct FfnArgs {
   const uint16_t* A;      // gate/up: x [T, K]; down: h [rows, K]
   const int32_t* perm;    // gate/up: slot id of each grouped row
@@ -41,6 +49,7 @@ struct FfnArgs {
   int32_t k;              // slots per token (gate/up gather: token = slot / k)
   int32_t N, K, E;
   int64_t a_rows;         // rows of A (gate/up: tokens of x)
+  const float* R;         // kAddBF16: fp32 rows added before the bf16 store
 };
 
 // ------------------------------------------------------------------ tile list
@@ -148,6 +157,25 @@ __device__ __forceinline__ void store_gateup(uint16_t* dst, f32x4_t g, f32x4_t u
   *reinterpret_cast<u32x2_t*>(dst) = packed;
 }
 
+// Store four consecutive outputs (features nn .. nn+3) of grouped row p.
+template <int EPI>
+__device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x4_t v,
+                                       f32x4_t u) {
+  const int N = a.N;
+  if (EPI == kSwiGLU) {
+    store_gateup(a.C + p * N + nn, v, u);
+  } else if (EPI == kF32) {
+    float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
+    *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
+  } else {
+    if (EPI == kAddBF16) v += *reinterpret_cast<const f32x4_t*>(a.R + p * N + nn);
+    u32x2_t packed;
+    packed[0] = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    packed[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<u32x2_t*>(a.C + p * N + nn) = packed;
+  }
+}
+
 // ------------------------------------------------------------- skinny GEMM
 // Each wave owns NF 16-row strips of the weight matrix (two strips, W1 and W3, per
 // fragment for gate/up) and runs them against the tile's <= 16 activation rows over the
@@ -162,8 +190,9 @@ __device__ __forceinline__ void store_gateup(uint16_t* dst, f32x4_t g, f32x4_t u
 // activations as the B operand (16 rows), so a lane ends up with four consecutive
 // output features of one row and stores them with one 8-byte (bf16) or 16-byte (fp32)
 // write.
-template <int NF, int KU, bool GATEUP>
+template <int NF, int KU, int EPI>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
+  constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int BN = 4 * 16 * NF;
   Tile tile;
   int nb;
@@ -232,20 +261,10 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
   }
 
   if (!row_ok) return;
-  if (GATEUP) {
-    uint16_t* crow = a.C + p * N;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int nn = n0 + 16 * f + 4 * q;
-      if (nn < N) store_gateup(crow + nn, acc1[f], acc3[f]);
-    }
-  } else {
-    float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int nn = n0 + 16 * f + 4 * q;
-      if (nn < N) *reinterpret_cast<f32x4_t*>(yrow + nn) = acc1[f];
-    }
+  for (int f = 0; f < NF; ++f) {
+    const int nn = n0 + 16 * f + 4 * q;
+    if (nn < N) store4<EPI>(a, p, nn, acc1[f], acc3[f]);
   }
 }
 
@@ -294,9 +313,10 @@ struct StreamCtx {
   int nks, nc;                 // k-steps (32) and chunks (64)
 };
 
-template <bool GATEUP, int NL>
+template <int EPI, int NL>
 __device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
                                             f32x4_t (&acc)[16][2]) {
+  constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int BM = 256, BK = 64, NW = 2, NA = 4;
   const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const int nks = c_.nks, nc = c_.nc;
@@ -392,21 +412,22 @@ __device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
 }
 
 // stream_loop instantiated for the smallest multiple of STEP fragments >= nfrag
-template <bool GATEUP, int STEP, int NL = STEP>
+template <int EPI, int STEP, int NL = STEP>
 __device__ __forceinline__ void stream_dispatch(int nfrag, const StreamCtx& ctx, uint16_t* lds,
                                                 f32x4_t (&acc)[16][2]) {
   if constexpr (NL >= 16) {
-    stream_loop<GATEUP, 16>(ctx, lds, acc);
+    stream_loop<EPI, 16>(ctx, lds, acc);
   } else {
     if (nfrag <= NL)
-      stream_loop<GATEUP, NL>(ctx, lds, acc);
+      stream_loop<EPI, NL>(ctx, lds, acc);
     else
-      stream_dispatch<GATEUP, STEP, NL + STEP>(nfrag, ctx, lds, acc);
+      stream_dispatch<EPI, STEP, NL + STEP>(nfrag, ctx, lds, acc);
   }
 }
 
-template <bool GATEUP>
+template <int EPI>
 __global__ __launch_bounds__(512, 1) void ffn_stream_kernel(const FfnArgs a) {
+  constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int BM = 256, BK = 64;
   constexpr int FM = BM / 16;                 // row fragments (every wave has all rows)
   constexpr int NW = 2;                       // weight fragments per wave per k-step
@@ -470,7 +491,7 @@ __global__ __launch_bounds__(512, 1) void ffn_stream_kernel(const FfnArgs a) {
 
   // live row fragments rounded up to a multiple of MOE_STREAM_NL_STEP (workgroup-uniform)
   const int nfrag = (nrows + 15) / 16;
-  stream_dispatch<GATEUP, MOE_STREAM_NL_STEP>(nfrag, ctx, lds, acc);
+  stream_dispatch<EPI, MOE_STREAM_NL_STEP>(nfrag, ctx, lds, acc);
 
   // epilogue: acc[i][f] of this lane = tile row 16 i + r, features 4 q .. 4 q + 3 of
   // weight fragment f
@@ -481,13 +502,12 @@ __global__ __launch_bounds__(512, 1) void ffn_stream_kernel(const FfnArgs a) {
     const int64_t p = tile.row_begin + m;
     if (GATEUP) {
       const int nn = n_wave + 4 * q;
-      if (nn < N) store_gateup(a.C + p * N + nn, acc[i][0], acc[i][1]);
+      if (nn < N) store4<EPI>(a, p, nn, acc[i][0], acc[i][1]);
     } else {
-      float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
 #pragma unroll
       for (int f = 0; f < NW; ++f) {
         const int nn = n_wave + 16 * f + 4 * q;
-        if (nn < N) *reinterpret_cast<f32x4_t*>(yrow + nn) = acc[i][f];
+        if (nn < N) store4<EPI>(a, p, nn, acc[i][f], acc[i][f]);
       }
     }
   }
@@ -505,9 +525,13 @@ int64_t max_tiles_for(const FfnShape& sh, int BM) {
   return sh.T * sh.k / BM + sh.E + (sh.shared ? (sh.T + BM - 1) / BM : 0) + 1;
 }
 
-// Average rows per routed expert decides the kernel: a few (decode) -> skinny kernel;
-// many (prefill) -> 128-row stream kernel.
-bool use_wide(const FfnShape& sh) { return sh.T * sh.k > (int64_t)16 * sh.E; }
+// Average rows per group (routed experts plus the shared expert) decides the kernel: a
+// few (decode) -> skinny kernel; many (prefill) -> 256-row stream kernel.
+bool use_wide(const FfnShape& sh) {
+  const int64_t rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
+  const int64_t groups = sh.E + (sh.shared ? 1 : 0);
+  return rows > (int64_t)16 * groups;
+}
 
 hipError_t tiles_launch(const FfnShape& sh, const int32_t* offsets, int BM, Tile* tiles,
                         int32_t* ntiles, hipStream_t s) {
@@ -526,8 +550,9 @@ dim3 grid_for(const FfnShape& sh, int BM, int BN, int N) {
 
 int64_t ffn_max_tiles(const FfnShape& sh) { return max_tiles_for(sh, kSkinnyBM); }
 
-hipError_t launch_dense_f32(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
-                            float* C, Tile* tiles, int32_t* ntiles, hipStream_t s) {
+hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
+                        DenseOut mode, float* Cf, uint16_t* Cb, const float* R, Tile* tiles,
+                        int32_t* ntiles, hipStream_t s) {
   // one group (the "shared" slot of the tile list) whose rows are all the rows of A
   const FfnShape sh{rows, K, 0, 0, N, true};
   const bool wide = rows > 512;
@@ -539,19 +564,31 @@ hipError_t launch_dense_f32(const uint16_t* A, int64_t rows, int K, const uint16
   a.a_rows = rows;
   a.routed_rows = 0;
   a.S1 = W;
-  a.Ys = C;
+  a.Ys = Cf;
+  a.C = Cb;
+  a.R = R;
   a.tiles = tiles;
   a.ntiles = ntiles;
   a.k = 1;
   a.N = N;
   a.K = K;
   a.E = 0;
-  if (wide)
-    hipLaunchKernelGGL(ffn_stream_kernel<false>, grid_for(sh, BM, kStreamBNDown, N), dim3(512), 0,
-                       s, a);
-  else
-    hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, false>), grid_for(sh, BM, 64, N),
-                       dim3(256), 0, s, a);
+  const dim3 gs = grid_for(sh, BM, kStreamBNDown, N), gk = grid_for(sh, BM, 64, N),
+             gk2 = grid_for(sh, BM, 128, N);
+  switch (mode) {
+    case DenseOut::kF32:
+      if (wide) hipLaunchKernelGGL(ffn_stream_kernel<kF32>, gs, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, kF32>), gk, dim3(256), 0, s, a);
+      break;
+    case DenseOut::kBF16:
+      if (wide) hipLaunchKernelGGL(ffn_stream_kernel<kBF16>, gs, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kBF16>), gk2, dim3(256), 0, s, a);
+      break;
+    case DenseOut::kAddBF16:
+      if (wide) hipLaunchKernelGGL(ffn_stream_kernel<kAddBF16>, gs, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kAddBF16>), gk2, dim3(256), 0, s, a);
+      break;
+  }
   return hipGetLastError();
 }
 
@@ -580,10 +617,10 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   a.K = sh.d;
   a.E = sh.E;
   if (wide)
-    hipLaunchKernelGGL(ffn_stream_kernel<true>, grid_for(sh, BM, kStreamBNGateUp, a.N), dim3(512),
+    hipLaunchKernelGGL(ffn_stream_kernel<kSwiGLU>, grid_for(sh, BM, kStreamBNGateUp, a.N), dim3(512),
                        0, s, a);
   else
-    hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, true>),
+    hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kSwiGLU>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -613,10 +650,10 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.K = sh.I;
   a.E = sh.E;
   if (wide)
-    hipLaunchKernelGGL(ffn_stream_kernel<false>, grid_for(sh, BM, kStreamBNDown, a.N), dim3(512),
+    hipLaunchKernelGGL(ffn_stream_kernel<kF32>, grid_for(sh, BM, kStreamBNDown, a.N), dim3(512),
                        0, s, a);
   else
-    hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, false>),
+    hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -149,6 +149,59 @@ bool shared_ptrs_ok(const moe_dims& d, const void* a, const void* b) {
   return has_shared(d) ? (aligned(a, 16) && aligned(b, 16)) : true;
 }
 
+// ------------------------------------------------------------------- latent variant
+moe_status check_latent(const moe_dims* dims, int32_t L) {
+  MOE_TRY(check_dims(dims));
+  if (L <= 0) return MOE_EINVAL;
+  if (L % 64 != 0 || L > moe::kMaxLatent) return MOE_EUNSUPPORTED;
+  const uint64_t lim = (uint64_t)UINT32_MAX;
+  if ((uint64_t)dims->tokens * L * 2 > lim) return MOE_EUNSUPPORTED;
+  if ((uint64_t)L * dims->d_expert * 2 > lim) return MOE_EUNSUPPORTED;
+  if ((uint64_t)L * dims->d_model * 2 > lim) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+struct LatentLayout {
+  size_t zpart, wsplit, idx, w, counts, offsets, perm, inv, hist, base, tiles, ntiles, lat, h, hs,
+      y, uhat, ys, total;
+};
+
+LatentLayout latent_layout(const moe_dims& d, int32_t L) {
+  const size_t T = (size_t)d.tokens, E = (size_t)d.n_experts, k = (size_t)d.top_k;
+  const size_t slots = T * k;
+  const size_t nb = (size_t)moe::permute_blocks(d.tokens);
+  // the largest tile list of the launches below: routed experts plus a T-row group
+  FfnShape sh{d.tokens, L, d.n_experts, d.top_k, d.d_expert, true};
+  const size_t max_tiles = (size_t)moe::ffn_max_tiles(sh);
+  LatentLayout P{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  P.zpart = take(T * 3 * E * 4);
+  P.wsplit = take(3 * E * (size_t)d.d_model * 2);
+  P.idx = take(slots * 4);
+  P.w = take(slots * 4);
+  P.counts = take(E * 4);
+  P.offsets = take((E + 1) * 4);
+  P.perm = take(slots * 4);
+  P.inv = take(slots * 4);
+  P.hist = take(nb * E * 4);
+  P.base = take(nb * E * 4);
+  P.tiles = take(max_tiles * sizeof(Tile));
+  P.ntiles = take(4);
+  P.lat = take(T * (size_t)L * 2);
+  P.h = take(slots * (size_t)d.d_expert * 2);
+  P.hs = take(has_shared(d) ? T * (size_t)d.d_shared * 2 : 0);
+  P.y = take(slots * (size_t)L * 4);
+  P.uhat = take(T * (size_t)L * 2);
+  P.ys = take(has_shared(d) ? T * (size_t)d.d_model * 4 : 0);
+  P.total = off;
+  return P;
+}
+
 }  // namespace
 
 extern "C" {
@@ -285,6 +338,84 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
   MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s));
   MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s));
   return combine_impl(d, y_routed, inv, w, y_shared, out, s);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+moe_status moe_latent_workspace_bytes(const moe_dims* dims, int32_t d_latent, size_t* bytes) {
+  MOE_TRY(check_latent(dims, d_latent));
+  MOE_NEED(bytes != nullptr);
+  *bytes = latent_layout(*dims, d_latent).total;
+  return MOE_OK;
+}
+
+moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint16_t* x,
+                              const float* w_router, const float* bias, const uint16_t* w_down,
+                              const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                              const uint16_t* w_up, const uint16_t* ws1, const uint16_t* ws3,
+                              const uint16_t* ws2, uint16_t* out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  MOE_TRY(check_latent(dims, d_latent));
+  const moe_dims& d = *dims;
+  const int32_t L = d_latent;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x, 16) && aligned(w_router, 16) && aligned(bias, 4) && aligned(w_down, 16));
+  MOE_NEED(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(w_up, 16));
+  MOE_NEED(aligned(out, 16));
+  if (has_shared(d)) MOE_NEED(aligned(ws1, 16) && aligned(ws3, 16) && aligned(ws2, 16));
+  const LatentLayout P = latent_layout(d, L);
+  MOE_NEED(aligned(ws, kWsAlign));
+  if (ws_bytes < P.total) return MOE_EWORKSPACE;
+  (void)hipGetLastError();
+  const hipStream_t s = (hipStream_t)stream;
+  const int64_t T = d.tokens;
+  int32_t* idx = at<int32_t>(ws, P.idx);
+  float* w = at<float>(ws, P.w);
+  int32_t* offsets = at<int32_t>(ws, P.offsets);
+  int32_t* perm = at<int32_t>(ws, P.perm);
+  int32_t* inv = at<int32_t>(ws, P.inv);
+  Tile* tiles = at<Tile>(ws, P.tiles);
+  int32_t* ntiles = at<int32_t>(ws, P.ntiles);
+  uint16_t* lat = at<uint16_t>(ws, P.lat);
+  uint16_t* h = at<uint16_t>(ws, P.h);
+  float* y = at<float>(ws, P.y);
+  uint16_t* uhat = at<uint16_t>(ws, P.uhat);
+  // router on the full-width input ("Kimi K3 · Latent up-projection": the gate scores
+  // hidden_states before the down-projection)
+  MOE_TRY(hip_status(moe::launch_router(x, w_router, bias, T, d.d_model, d.n_experts, d.top_k,
+                                        d.routed_scale, at<uint16_t>(ws, P.wsplit),
+                                        at<float>(ws, P.zpart), tiles, ntiles, nullptr, idx, w,
+                                        s)));
+  MOE_TRY(hip_status(moe::launch_permute(idx, T, d.n_experts, d.top_k, at<int32_t>(ws, P.hist),
+                                         at<int32_t>(ws, P.base), at<int32_t>(ws, P.counts),
+                                         offsets, perm, inv, s)));
+  // down-projection to the latent width (bf16: the experts' MFMA operand)
+  MOE_TRY(hip_status(moe::launch_dense(x, T, d.d_model, w_down, L, moe::DenseOut::kBF16, nullptr,
+                                       lat, nullptr, tiles, ntiles, s)));
+  // routed experts on the latent
+  const FfnShape rsh{T, L, d.n_experts, d.top_k, d.d_expert, false};
+  MOE_TRY(hip_status(moe::launch_gate_up(rsh, lat, perm, offsets, w1, w3, nullptr, nullptr, h,
+                                         tiles, ntiles, s)));
+  MOE_TRY(hip_status(moe::launch_down(rsh, h, offsets, w2, nullptr, y, nullptr, tiles, ntiles, s)));
+  // gate-weighted sum over the slots, RMSNorm (eps from the config), bf16
+  MOE_TRY(hip_status(moe::launch_combine_rmsnorm(y, inv, w, uhat, T, L, d.top_k, 1e-6f, s)));
+  if (has_shared(d)) {
+    // shared expert on the full-width input: a T-row group with no routed experts
+    const FfnShape ssh{T, d.d_model, 0, 0, d.d_shared, true};
+    uint16_t* hs = at<uint16_t>(ws, P.hs);
+    float* ys = at<float>(ws, P.ys);
+    MOE_TRY(hip_status(moe::launch_gate_up(ssh, x, nullptr, nullptr, nullptr, nullptr, ws1, ws3,
+                                           hs, tiles, ntiles, s)));
+    MOE_TRY(hip_status(moe::launch_down(ssh, hs, nullptr, nullptr, ws2, nullptr, ys, tiles, ntiles,
+                                        s)));
+    // up-projection with the shared output added before the one bf16 rounding
+    return hip_status(moe::launch_dense(uhat, T, L, w_up, d.d_model, moe::DenseOut::kAddBF16,
+                                        nullptr, out, ys, tiles, ntiles, s));
+  }
+  return hip_status(moe::launch_dense(uhat, T, L, w_up, d.d_model, moe::DenseOut::kBF16, nullptr,
+                                      out, nullptr, tiles, ntiles, s));
 }
 
 }  // extern "C"

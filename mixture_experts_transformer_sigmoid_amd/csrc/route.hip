@@ -143,7 +143,8 @@ hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias,
                      w_split);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_dense_f32(x, T, d, w_split, 3 * E, z_part, tiles, ntiles, s);
+  err = launch_dense(x, T, d, w_split, 3 * E, DenseOut::kF32, z_part, nullptr, nullptr, tiles,
+                     ntiles, s);
   if (err != hipSuccess) return err;
   const int epl = (E + 63) / 64;
   if (epl <= 1)

@@ -44,6 +44,9 @@ CONFIGS = {
     # K2 shape, skewed routing
     "k2_skew": dict(tokens=4096, d_model=7168, n_experts=384, top_k=8, d_expert=2048,
                     d_shared=2048, routed_scale=2.827, bias="zipf"),
+    # small latent MoE case the oracle finishes in well under a second
+    "tiny_latent": dict(tokens=64, d_model=256, n_experts=16, top_k=2, d_expert=128, d_shared=128,
+                        routed_scale=2.827, bias="uniform", d_latent=128),
     # latent MoE: experts on a 3584-wide latent
     "latent": dict(tokens=4096, d_model=7168, n_experts=384, top_k=8, d_expert=2048,
                    d_shared=2048, routed_scale=2.827, bias="uniform", d_latent=3584),

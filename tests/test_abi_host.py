@@ -114,3 +114,19 @@ def test_binding_raises_on_error():
     with pytest.raises(M.MoeError) as ei:
         M.moe_workspace_bytes(M.moe_dims(1, 7168, 384, 9, 2048, 2048))
     assert ei.value.status == M.MOE_EUNSUPPORTED
+
+
+def test_latent_dims_checked():
+    n = ctypes.c_size_t(0)
+    L = M.lib()
+    d = _k2(4096)
+    assert L.moe_latent_workspace_bytes(ctypes.byref(d), 3584, ctypes.byref(n)) == M.MOE_OK
+    assert n.value > M.moe_workspace_bytes(_k2(0))
+    assert L.moe_latent_workspace_bytes(ctypes.byref(d), 100, ctypes.byref(n)) == M.MOE_EUNSUPPORTED
+    assert L.moe_latent_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(n)) == M.MOE_EINVAL
+    assert L.moe_latent_workspace_bytes(ctypes.byref(d), 16384, ctypes.byref(n)) == M.MOE_EUNSUPPORTED
+    P = _fake(0x100000)
+    assert L.moe_forward_latent(ctypes.byref(d), 3584, None, P, P, P, P, P, P, P, P, P, P, P, P,
+                                n.value, None) == M.MOE_EINVAL
+    assert L.moe_forward_latent(ctypes.byref(d), 3584, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                n.value - 1, None) == M.MOE_EWORKSPACE

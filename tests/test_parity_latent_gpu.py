@@ -1,0 +1,87 @@
+"""Parity of the latent mixture of experts (moe_forward_latent) against the CPU oracle.
+
+The router scores the full-width input; the routed experts run on the latent width after
+the down-projection; their gate-weighted sum is RMS-normalised and projected back up; the
+shared expert runs on the full-width input.  Same bar as the K2 layer: routing exact
+outside the near-tie window, max |out - oracle| <= 2e-2 * RMS(oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_transformer_sigmoid_amd as M
+import synth_inputs as S
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+GAP = 1e-6
+TOL = 2e-2
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_latent(cfg, inp):
+    dims = M.dims_for(cfg)
+    L = cfg["d_latent"]
+    ws = M.latent_workspace(dims, L)
+    out = torch.full((cfg["tokens"], cfg["d_model"]), float("nan"), dtype=torch.bfloat16, device=DEV)
+    M.moe_forward_latent(dims, L, inp["x"], inp["w_r"], inp["b"], inp["w_down"], inp["w1"],
+                         inp["w3"], inp["w2"], inp["w_up"], inp.get("ws1"), inp.get("ws3"),
+                         inp.get("ws2"), out, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(cfg, inp, sample=None, seed=0):
+    T = cfg["tokens"]
+    say(f"latent case T={T} d={cfg['d_model']} L={cfg['d_latent']} E={cfg['n_experts']} k={cfg['top_k']}")
+    out = run_latent(cfg, inp)
+    again = run_latent(cfg, inp)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "not deterministic"
+    r = O.route(f64(inp["x"]), f64(inp["w_r"]), inp["b"].cpu().numpy(), cfg["top_k"],
+                cfg["routed_scale"])
+    keep = r["gap"] >= GAP
+    toks = np.arange(T) if sample is None else np.sort(
+        np.random.default_rng(seed).choice(T, size=min(sample, T), replace=False))
+    toks = toks[keep[toks]]
+    get = lambda e: (f64(inp["w1"][e]), f64(inp["w3"][e]), f64(inp["w2"][e]))  # noqa: E731
+    ref = O.moe_latent(f64(inp["x"]), f64(inp["w_r"]), inp["b"].cpu().numpy(), f64(inp["w_down"]),
+                       None, None, None, f64(inp["w_up"]), f64(inp["ws1"]), f64(inp["ws3"]),
+                       f64(inp["ws2"]), cfg["top_k"], cfg["routed_scale"], tokens=toks,
+                       get_expert=get)
+    got = f64(out)[toks]
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref["out"])
+    rms = np.sqrt(np.mean(ref["out"] ** 2))
+    say(f"  out: max|err| {err.max():.3e}  tol {TOL * rms:.3e}  (rms {rms:.3e}); "
+        f"near-tie tokens excluded {int((~keep).sum())}")
+    assert err.max() <= TOL * rms
+
+
+def test_latent_tiny():
+    cfg = S.CONFIGS["tiny_latent"]
+    check(cfg, {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu").items()})
+
+
+@pytest.mark.parametrize("T", [1, 45])
+def test_latent_ragged(T):
+    cfg = S.with_overrides("tiny_latent", tokens=T, d_latent=192)
+    check(cfg, {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu", seed=T).items()})
+
+
+def test_latent_k2_shape_4096():
+    cfg = S.CONFIGS["latent"]
+    say("generating latent-MoE weights on the GPU (384 experts on a 3584-wide latent)")
+    inp = S.make_inputs(cfg, DEV)
+    torch.cuda.synchronize()
+    check(cfg, inp, sample=8)
+    del inp
+    torch.cuda.empty_cache()
