@@ -1,5 +1,5 @@
 """CPU oracle of the sigmoid-routed MoE FFN: test infrastructure only (see moe_oracle)."""
 from .moe_oracle import *  # noqa: F401,F403
-from .moe_oracle import (ALPHA_K2, gate_matrix, moe_dense, moe_latent, moe_param_count,
-                         moe_param_shapes, moe_sparse, permute, rmsnorm, route, sigmoid,
-                         silu, swiglu)
+from .moe_oracle import (ALPHA_K2, gate_matrix, moe_block, moe_dense, moe_latent, moe_param_count,
+                         moe_param_shapes, moe_sparse, permute, rmsnorm, round_bf16, route,
+                         sigmoid, silu, swiglu)

@@ -34,7 +34,11 @@ Readings where the pages are silent (each also listed in the design doc):
   score s + b rounded to fp32.  All values (gates, FFN, sums) are float64.
 * The bias enters only the selection, added to sigma(z), never to z and never to G.
 * No epsilon in the renormalising denominator (the denominator is > 0).
-* RMSNorm (latent variant only): u / sqrt(mean(u^2) + eps) with unit gain.
+* RMSNorm: u / sqrt(mean(u^2) + eps) times the gain (the pre-MoE norm; the latent
+  variant's norm has unit gain).  The normalised block input x_ffn is a bf16 activation:
+  it is rounded to fp32, then to bf16 (nearest-even both times) before use.
+* The residual x'_n is added to Delta_ffn in full precision (the kernel adds it in fp32
+  and rounds the sum to bf16 once).
 
 Parity pins: see tests/test_oracle_pins.py.  The output values themselves have no
 worked example on the pages ("parity unpinned" beyond the invariants and closed
@@ -91,10 +95,30 @@ def silu(v):
     return v * sigmoid(v)
 
 
-def rmsnorm(u, eps=1e-6):
-    """RMSNorm with unit gain: u / sqrt(mean(u^2) + eps), per row (latent variant)."""
+def rmsnorm(u, eps=1e-6, gain=None):
+    """RMSNorm: u / sqrt(mean(u^2) + eps) per row, times the gain when one is given.
+
+    "Kimi K2 · Transformer blocks": x_ffn = RMSNorm(x'_n) before the mixture of experts,
+    with a learned gain of d_model values ("MoE RMSNorm" row of the parameter table) and
+    rms_norm_eps 1e-6 in the config; the latent variant's norm has unit gain."""
     u = np.asarray(u, dtype=np.float64)
-    return u / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+    v = u / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+    return v if gain is None else v * np.asarray(gain, dtype=np.float64)
+
+
+def round_bf16(v):
+    """Round to bfloat16 the way a stored activation is: to fp32 first, then to the
+    8-significant-bit bfloat16 grid, both round-to-nearest-even; returned as float64.
+
+    bfloat16 keeps fp32's sign and 8-bit exponent and the top 7 of its 23 stored
+    mantissa bits; rounding to nearest-even on the 16 dropped bits adds 0x7fff plus the
+    lowest kept bit before truncating.  NaN stays NaN, infinities stay infinite."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    bits = f.view(np.uint32).astype(np.uint64)
+    keep_lsb = (bits >> 16) & 1
+    r = ((bits + 0x7FFF + keep_lsb) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(f), np.nan, out)
 
 
 def _f64(a):
@@ -281,3 +305,24 @@ def moe_latent(x, w_r, b, w_down, w1, w3, w2, w_up, ws1, ws3, ws2, top_k,
     y_s = swiglu(x64[rows], ws1, ws3, ws2)
     return dict(r, rows=rows, latent=lat, y_latent=sparse["y_routed"], y_routed=y_r,
                 y_shared=y_s, out=y_r + y_s)
+
+
+# ----------------------------------------------------------- block: norm + residual
+def moe_block(x_res, gain, w_r, b, w1=None, w3=None, w2=None, ws1=None, ws3=None, ws2=None,
+              top_k=8, alpha=ALPHA_K2, eps=1e-6, *, get_expert=None, tokens=None):
+    """The MoE half of a transformer block ("Kimi K2 · Transformer blocks", MoE block
+    equations; the DeepseekV3DecoderLayer forward printed on that page):
+
+        x_ffn = RMSNorm(x'_n)  (gain, eps)  ->  Delta_ffn = MoE(x_ffn)
+        x_{n+1} = x'_n + Delta_ffn
+
+    x_ffn is an activation of the bf16 model, so it is rounded to bf16 (via fp32) before
+    the router and the experts read it; everything else is float64.  tokens: optional
+    rows to evaluate (the norm and the routing are per token)."""
+    x_res = _f64(x_res)
+    rows = np.arange(x_res.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    x_ffn = round_bf16(rmsnorm(x_res[rows], eps, gain))
+    shared = None if ws1 is None else (ws1, ws3, ws2)
+    m = moe_sparse(x_ffn, w_r, b, top_k, alpha, get_expert=get_expert, w1=w1, w3=w3, w2=w2,
+                   shared=shared)
+    return dict(m, rows=rows, x_ffn=x_ffn, delta=m["out"], out=x_res[rows] + m["out"])

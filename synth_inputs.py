@@ -15,6 +15,9 @@ Skewed routing: b_e = -0.5 * ln(rank_e) with rank a seeded permutation of 1..E, 
 few experts take most tokens and many take none.
 Latent variant: W_down ~ N(0, 1/d) [L, d], experts on the latent width L, W_up ~
 N(0, 1/L) [d, L].
+Block (pre-MoE norm + residual): the residual stream x'_n = N(0, 1) * c_j with a
+per-channel scale c_j ~ U(0.25, 4) (so the norm has real work), bf16; the norm gain
+gamma ~ U(0.5, 1.5) rounded to bf16 (a checkpoint's gain is bf16), passed as fp32.
 
 Every tensor (and every expert slice of the stacked weights) has its own seed derived
 from (seed, tensor id, slice), so one expert can be regenerated alone.  Values are drawn
@@ -29,7 +32,7 @@ import torch
 
 # tensor ids (stable: they enter the per-tensor seeds)
 TID = {"x": 0, "w_r": 1, "b": 2, "w1": 3, "w3": 4, "w2": 5, "ws1": 6, "ws3": 7, "ws2": 8,
-       "w_down": 9, "w_up": 10, "rank": 11}
+       "w_down": 9, "w_up": 10, "rank": 11, "x_res": 12, "norm_w": 13, "chan": 14}
 
 CONFIGS = {
     # small case the oracle finishes in well under a second
@@ -122,6 +125,21 @@ def make_activations(cfg, device="cpu", seed=0):
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     return {"x": normal((cfg["tokens"], cfg["d_model"]), 1.0, torch.bfloat16, device, seed, TID["x"]),
+            "b": bias(cfg, device, seed)}
+
+
+def make_block_activations(cfg, device="cpu", seed=0):
+    """Residual stream x'_n [T, d] bf16, norm gain [d] fp32 and the selection bias."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    d = cfg["d_model"]
+    g = _gen(device, seed, TID["chan"])
+    chan = torch.rand(d, generator=g, device=device, dtype=torch.float32) * 3.75 + 0.25
+    x = normal((cfg["tokens"], d), 1.0, torch.float32, device, seed, TID["x_res"])
+    g = _gen(device, seed, TID["norm_w"])
+    gain = torch.rand(d, generator=g, device=device, dtype=torch.float32) + 0.5
+    return {"x_res": (x * chan).to(torch.bfloat16),
+            "norm_w": gain.to(torch.bfloat16).to(torch.float32),
             "b": bias(cfg, device, seed)}
 
 

@@ -320,3 +320,100 @@ def test_a_planted_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(mo, "silu", lambda v: np.asarray(v, dtype=np.float64) * mo.sigmoid(-np.asarray(v)))
     bad = _run(L, "dense")["out"]
     assert not np.allclose(good, bad)
+
+
+# ------------------------------------------------- block: pre-MoE norm and residual
+def test_rmsnorm_with_gain_against_torch():
+    rng = np.random.default_rng(15)
+    u = rng.standard_normal((9, 48)) * 3.0
+    g = rng.uniform(0.5, 1.5, 48)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(u), (48,), weight=torch.from_numpy(g),
+                                       eps=1e-6).numpy()
+    np.testing.assert_allclose(oracle.rmsnorm(u, 1e-6, g), ref, rtol=1e-13)
+
+
+def test_rmsnorm_closed_forms():
+    # a constant row c gives c / sqrt(c^2 + eps) times the gain
+    g = np.linspace(0.25, 2.0, 16)
+    for c in (0.5, -3.0, 1e-4):
+        np.testing.assert_allclose(oracle.rmsnorm(np.full((1, 16), c), 1e-6, g)[0],
+                                   c / math.sqrt(c * c + 1e-6) * g, rtol=1e-14)
+    # eps = 0, unit gain: the output has mean square 1 and ignores a positive scale
+    u = np.random.default_rng(16).standard_normal((5, 64))
+    v = oracle.rmsnorm(u, 0.0)
+    np.testing.assert_allclose(np.mean(v * v, axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(oracle.rmsnorm(7.5 * u, 0.0), v, rtol=1e-14)
+
+
+def test_round_bf16_against_torch_and_ties():
+    rng = np.random.default_rng(17)
+    v = (rng.standard_normal(200_000) * np.exp(rng.uniform(-90, 80, 200_000))).astype(np.float32)
+    v = np.concatenate([v, np.float32([1e-40, -3e-42, 0.0, -0.0])])      # fp32 subnormals, zeros
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = mo.round_bf16(v)
+    assert np.array_equal(got, ref)
+    # ties go to the even neighbour on the 2^-7 grid at 1.0
+    t = mo.round_bf16(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -20]))
+    assert list(t) == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7]
+    s = mo.round_bf16(np.array([np.inf, -np.inf, np.nan]))
+    assert s[0] == np.inf and s[1] == -np.inf and np.isnan(s[2])
+
+
+def _block(L, x_res, gain, eps=1e-6, **kw):
+    args = dict(w1=L["w1"], w3=L["w3"], w2=L["w2"], ws1=L["ws1"], ws3=L["ws3"], ws2=L["ws2"])
+    args.update(kw)
+    return mo.moe_block(x_res, gain, L["w_r"], L["b"], top_k=L["top_k"], eps=eps, **args)
+
+
+def test_block_residual_passes_through_when_experts_vanish():
+    rng = np.random.default_rng(18)
+    L = _layer(rng, T=12, d=32, E=8, I=16, Is=16, k=2)
+    g = rng.uniform(0.5, 1.5, 32)
+    blk = _block(L, L["x"], g, w2=np.zeros_like(L["w2"]), ws2=np.zeros_like(L["ws2"]))
+    assert np.array_equal(blk["out"], L["x"])
+    # the experts and the router read the bf16-rounded normalised input
+    xf = blk["x_ffn"]
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(L["x"]), (32,), weight=torch.from_numpy(g),
+                                       eps=1e-6)
+    assert np.array_equal(xf, ref.to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy())
+    r = mo.route(xf, L["w_r"], L["b"], 2)
+    assert np.array_equal(blk["topk_idx"], r["topk_idx"])
+
+
+def test_block_zero_gain_routes_by_bias_alone():
+    # gain 0: x_ffn = 0, every sigmoid is 1/2, the bias alone picks the experts, the
+    # gates are alpha/k each and every expert sees a zero input, so the output is x'_n
+    rng = np.random.default_rng(19)
+    L = _layer(rng, T=6, d=32, E=8, I=16, Is=16, k=3)
+    blk = _block(L, L["x"], np.zeros(32))
+    want = np.argsort(-L["b"].astype(np.float64), kind="stable")[:3]
+    for t in range(6):
+        assert sorted(blk["topk_idx"][t]) == sorted(want)
+    np.testing.assert_allclose(blk["topk_w"], 2.827 / 3, rtol=1e-15)
+    assert np.array_equal(blk["out"], L["x"])
+
+
+def test_block_delta_ignores_input_scale_and_gain_scales_x_ffn():
+    # with eps = 0 the norm output does not change when x'_n is scaled by a power of two,
+    # so Delta_ffn does not either and the output moves by exactly the scaled residual
+    rng = np.random.default_rng(20)
+    L = _layer(rng, T=10, d=32, E=8, I=16, Is=16, k=2)
+    g = rng.uniform(0.5, 1.5, 32)
+    a = _block(L, L["x"], g, eps=0.0)
+    b = _block(L, 4.0 * L["x"], g, eps=0.0)
+    assert np.array_equal(a["x_ffn"], b["x_ffn"])
+    np.testing.assert_allclose(b["out"] - 4.0 * L["x"], a["delta"], rtol=0, atol=1e-12)
+    assert np.abs(a["delta"]).max() > 0.05
+    # doubling the gain doubles x_ffn exactly (bf16 rounding commutes with x2)
+    c = _block(L, L["x"], 2.0 * g)
+    d = _block(L, L["x"], g)
+    assert np.array_equal(c["x_ffn"], 2.0 * d["x_ffn"])
+
+
+def test_block_token_subset_matches_full():
+    rng = np.random.default_rng(21)
+    L = _layer(rng, T=20, d=32, E=8, I=16, Is=16, k=2)
+    g = rng.uniform(0.5, 1.5, 32)
+    full = _block(L, L["x"], g)
+    sub = _block(L, L["x"], g, tokens=[0, 7, 19])
+    np.testing.assert_allclose(sub["out"], full["out"][[0, 7, 19]], rtol=1e-13, atol=1e-14)
