@@ -96,6 +96,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latent", action="store_true", help="skip the latent-MoE figure")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the fused norm + residual block figure")
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens in the oracle sample")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two --pmc counter CSVs and exit")
@@ -141,6 +143,32 @@ def time_forward(M, torch, dims, inp, out, ws, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall
     return t0.elapsed_time(t1) / steps, wall
+
+
+def time_block(M, torch, S, cfg, weights, steps, warmup):
+    """moe_forward_block (pre-MoE RMSNorm + layer + residual add) on the same weights."""
+    dev = weights["w1"].device
+    act = S.make_block_activations(cfg, dev)
+    dims = M.dims_for(cfg)
+    ws = M.block_workspace(dims, dev)
+    out = torch.empty(cfg["tokens"], cfg["d_model"], dtype=torch.bfloat16, device=dev)
+
+    def call():
+        M.moe_forward_block(dims, act["x_res"], act["norm_w"], 1e-6, weights["w_r"], act["b"],
+                            weights["w1"], weights["w3"], weights["w2"], weights["ws1"],
+                            weights["ws3"], weights["ws2"], out, ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
 
 
 def split_state(M, torch, dims, inp, ws):
@@ -313,6 +341,14 @@ def main():
     }
     log(f"{args.workload}: {ms:.3f} ms/step, {res['value']:.0f} tok/s, layer {layer_gbs:.0f} GB/s, "
         f"gate/up {gu_ms:.3f} ms = {gu_gbs:.0f} GB/s")
+    if not args.no_block:
+        del ws
+        bms = time_block(M, torch, S, cfg, weights, args.steps, args.warmup)
+        res["block"] = {"entry": "moe_forward_block (pre-MoE RMSNorm, layer, residual add)",
+                        "tokens": T, "ms_per_step": bms, "tokens_per_s": T / (bms * 1e-3),
+                        "added_us_vs_layer": (bms - ms) * 1e3}
+        log(f"block ({args.workload}): {bms:.3f} ms/step ({(bms - ms) * 1e3:+.1f} us vs the layer)")
+        ws = M.workspace(dims, dev)
 
     if not args.no_prefill and args.workload != "k2_prefill":
         pcfg = S.CONFIGS["k2_prefill"]
@@ -330,10 +366,17 @@ def main():
         palg = algorithmic(pcfg, pact, pcfg["tokens"])
         ptf = palg["layer_flops"] / (pms * 1e-3) / 1e12
         pgb = palg["layer_bytes"] / (pms * 1e-3) / 1e9
+        if not args.no_block:
+            del pws
+            pbms = time_block(M, torch, S, pcfg, weights, psteps, 1)
+            pws = None
         res["prefill"] = {"workload": "k2_prefill: T=8192 (4 x 2048), same layer", "steps": psteps,
                           "ms_per_step": pms, "tokens_per_s": pcfg["tokens"] / (pms * 1e-3),
                           "mfma_tflops": ptf, "mfma_frac": ptf / MFMA_BF16_PEAK_TFLOPS,
                           "hbm_gbs": pgb, "hbm_frac": pgb / HBM_PEAK_GBS, "active_experts": pact}
+        if not args.no_block:
+            res["prefill"]["block_ms_per_step"] = pbms
+            log(f"block (k2_prefill): {pbms:.3f} ms/step ({(pbms - pms) * 1e3:+.1f} us vs the layer)")
         log(f"prefill: {pms:.3f} ms/step, {res['prefill']['tokens_per_s']:.0f} tok/s, "
             f"{ptf:.0f} TFLOP/s ({100 * ptf / MFMA_BF16_PEAK_TFLOPS:.1f}% MFMA)")
         del pws, pin

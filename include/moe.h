@@ -33,7 +33,7 @@
  *       MOE_EINVAL       null / misaligned (16 B) pointer, impossible dims
  *       MOE_EUNSUPPORTED dims this build does not handle (d, I not multiples of 64,
  *                        top_k > 8, E > 1024, Is not 0 or I, x or one weight matrix
- *                        of 4 GiB or more)
+ *                        of 4 GiB or more, T above 2^23)
  *       MOE_EWORKSPACE   ws_bytes smaller than moe_workspace_bytes()
  *       MOE_EHIP         a kernel launch failed (device faults surface at the caller's
  *                        next synchronisation, as usual for asynchronous work)
@@ -148,6 +148,27 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
                        const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
                        const uint16_t* ws2, uint16_t* out, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* The MoE half of a transformer block, with the steps either side of the layer fused in
+ * ("Kimi K2 · Transformer blocks", MoE transformer block: x_ffn = RMSNorm(x'_n), the
+ * mixture of experts on x_ffn, then x_{n+1} = x'_n + Delta_ffn; the block order of the
+ * DeepseekV3DecoderLayer forward printed on the same page: post-attention RMSNorm, MLP,
+ * residual add, with rms_norm_eps 1e-6 in the config):
+ *   x_ffn[t] = bf16( x_res[t] / sqrt(mean(x_res[t]^2) + norm_eps) * norm_w )
+ *   out[t]   = bf16( x_res[t] + Delta_ffn(x_ffn)[t] )
+ * x_res [T, d] bf16 is the residual stream x'_n; norm_w [d] fp32 is the RMSNorm gain
+ * (4-byte aligned; a bf16 checkpoint gain converts exactly); norm_eps >= 0, finite.
+ * The norm is computed in fp64 and rounded to fp32, then to bf16 (round-to-nearest-even
+ * both times); Delta_ffn is moe_forward's fp32 sum, the residual is added to it in fp32
+ * and the total rounded to bf16 once.  out must not alias x_res.
+ * Workspace: moe_block_workspace_bytes (moe_workspace_bytes plus the bf16 x_ffn, which
+ * the call leaves at byte offset moe_workspace_bytes(dims) of ws). */
+moe_status moe_block_workspace_bytes(const moe_dims* dims, size_t* bytes);
+moe_status moe_forward_block(const moe_dims* dims, const uint16_t* x_res, const float* norm_w,
+                             float norm_eps, const float* w_router, const float* bias,
+                             const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                             const uint16_t* ws1, const uint16_t* ws3, const uint16_t* ws2,
+                             uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Latent mixture of experts ("Kimi K3 · Latent up-projection": the router scores the
  * full-width input; the input is projected down to the latent width; the routed experts

@@ -19,7 +19,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 # every exported symbol of include/moe.h
 EXPORTS = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_latent_workspace_bytes", "moe_forward_latent")
+           "moe_forward", "moe_latent_workspace_bytes", "moe_forward_latent",
+           "moe_block_workspace_bytes", "moe_forward_block")
 
 
 class MoeDims(ctypes.Structure):
@@ -61,6 +62,9 @@ def lib():
         "moe_expert_ffn": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
         "moe_combine": [D, _P, _P, _P, _P, _P, _P],
         "moe_forward": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+        "moe_block_workspace_bytes": [D, ctypes.POINTER(ctypes.c_size_t)],
+        "moe_forward_block": [D, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                              _S, _P],
         "moe_latent_workspace_bytes": [D, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
         "moe_forward_latent": [D, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _S, _P],
@@ -161,6 +165,25 @@ def moe_forward(dims, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, ws, str
     _check(lib().moe_forward(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w1),
                              _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out), wp,
                              wn, _stream(stream)))
+
+
+def moe_block_workspace_bytes(dims: MoeDims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_block_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def block_workspace(dims: MoeDims, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_block_workspace_bytes(dims), 256), dtype=torch.uint8, device=device)
+
+
+def moe_forward_block(dims, x_res, norm_w, norm_eps, w_router, bias, w1, w3, w2, ws1, ws3, ws2,
+                      out, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_forward_block(ctypes.byref(dims), _ptr(x_res), _ptr(norm_w),
+                                   float(norm_eps), _ptr(w_router), _ptr(bias), _ptr(w1),
+                                   _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out),
+                                   wp, wn, _stream(stream)))
 
 
 def moe_latent_workspace_bytes(dims: MoeDims, d_latent: int) -> int:

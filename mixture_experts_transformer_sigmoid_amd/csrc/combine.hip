@@ -17,7 +17,7 @@ template <int KMAX>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ y_routed, const int32_t* __restrict__ inv,
     const float* __restrict__ topk_w, const float* __restrict__ y_shared,
-    uint16_t* __restrict__ out, int64_t T, int d, int k) {
+    const uint16_t* __restrict__ residual, uint16_t* __restrict__ out, int64_t T, int d, int k) {
   const int nchunk = (d / 8 + kCombineThreads - 1) / kCombineThreads;
   const int64_t t = blockIdx.x / nchunk;
   const int c = ((int)(blockIdx.x % nchunk) * kCombineThreads + threadIdx.x) * 8;
@@ -62,6 +62,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y_shared + t * d + c);
     lo += src[0];
     hi += src[1];
+  }
+  if (residual != nullptr) {
+    // x_{n+1} = x'_n + Delta_ffn, added in fp32 before the one bf16 rounding
+    const u32x4_t v = load16(residual + t * d + c);
+    lo[0] += bf16_to_f32(v[0] & 0xffffu);
+    lo[1] += bf16_to_f32(v[0] >> 16);
+    lo[2] += bf16_to_f32(v[1] & 0xffffu);
+    lo[3] += bf16_to_f32(v[1] >> 16);
+    hi[0] += bf16_to_f32(v[2] & 0xffffu);
+    hi[1] += bf16_to_f32(v[2] >> 16);
+    hi[2] += bf16_to_f32(v[3] & 0xffffu);
+    hi[3] += bf16_to_f32(v[3] >> 16);
   }
   u32x4_t o;
   o[0] = f32_to_bf16(lo[0]) | (f32_to_bf16(lo[1]) << 16);
@@ -155,13 +167,64 @@ hipError_t launch_combine_rmsnorm(const float* y_routed, const int32_t* inv, con
 }
 
 hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float* topk_w,
-                          const float* y_shared, uint16_t* out, int64_t T, int d, int k,
-                          hipStream_t s) {
+                          const float* y_shared, const uint16_t* residual, uint16_t* out,
+                          int64_t T, int d, int k, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int64_t nchunk = (d / 8 + kCombineThreads - 1) / kCombineThreads;
   dim3 grid((unsigned)(nchunk * T));
   hipLaunchKernelGGL(combine_kernel<kMaxTopK>, grid, dim3(kCombineThreads), 0, s, y_routed, inv,
-                     topk_w, y_shared, out, T, d, k);
+                     topk_w, y_shared, residual, out, T, d, k);
+  return hipGetLastError();
+}
+
+// Pre-MoE RMSNorm: x_ffn[t] = bf16(x'[t] / sqrt(mean(x'[t]^2) + eps) * gain), one
+// workgroup per token.  The arithmetic is fp64 (sum of squares in a fixed tree order,
+// then the scaling), rounded once to fp32 and then to bf16: the normalised row feeds the
+// router, whose top-k decision would turn on a one-ulp difference in any element, and in
+// fp64 the result does not depend on the summation order to within bf16 rounding.
+__global__ __launch_bounds__(kCombineThreads) void rmsnorm_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ gain, uint16_t* __restrict__ out,
+    int d, float eps) {
+  __shared__ double wsum[kCombineThreads / 64];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint16_t* row = x + t * d;
+  double ss = 0.0;
+  for (int c = tid * 8; c < d; c += kCombineThreads * 8) {
+    const u32x4_t v = load16(row + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double a = bf16_to_f32(v[i] & 0xffffu), b = bf16_to_f32(v[i] >> 16);
+      ss = fma(a, a, ss);
+      ss = fma(b, b, ss);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < kCombineThreads / 64; ++i) tot += wsum[i];
+  const double inv_rms = 1.0 / sqrt(tot / (double)d + (double)eps);
+  for (int c = tid * 8; c < d; c += kCombineThreads * 8) {
+    const u32x4_t v = load16(row + c);
+    u32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = (float)((double)bf16_to_f32(v[i] & 0xffffu) * inv_rms * (double)gain[c + 2 * i]);
+      const float b = (float)((double)bf16_to_f32(v[i] >> 16) * inv_rms * (double)gain[c + 2 * i + 1]);
+      o[i] = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(out + t * d + c) = o;
+  }
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, uint16_t* out, int64_t T, int d,
+                          float eps, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)T), dim3(kCombineThreads), 0, s, x, gain, out,
+                     d, eps);
   return hipGetLastError();
 }
 

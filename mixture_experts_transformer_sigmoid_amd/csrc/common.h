@@ -119,9 +119,14 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
                        const uint16_t* w2, const uint16_t* ws2, float* y_routed,
                        float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s);
 
+// residual (bf16 [T, d]) may be null; when given it is added before the bf16 rounding.
 hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float* topk_w,
-                          const float* y_shared, uint16_t* out, int64_t T, int d, int k,
-                          hipStream_t s);
+                          const float* y_shared, const uint16_t* residual, uint16_t* out,
+                          int64_t T, int d, int k, hipStream_t s);
+
+// out[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps) * gain), fp64 arithmetic.
+hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, uint16_t* out, int64_t T, int d,
+                          float eps, hipStream_t s);
 
 // out[t] = bf16(RMSNorm(sum_slot topk_w * y_routed[inv])) over L features (L <= 8192).
 hipError_t launch_combine_rmsnorm(const float* y_routed, const int32_t* inv, const float* topk_w,

@@ -31,6 +31,8 @@ moe_status check_dims(const moe_dims* dp) {
   if (d.d_shared != 0 && d.d_shared != d.d_expert) return MOE_EUNSUPPORTED;
   // grouped rows (T*k routed + T shared) are indexed with int32
   if (d.tokens > (int64_t)(INT32_MAX / 2) / (d.top_k + 1)) return MOE_EUNSUPPORTED;
+  // per-token launches (combine, norm) must stay below 2^32 work-items per grid
+  if (d.tokens > ((int64_t)1 << 23)) return MOE_EUNSUPPORTED;
   // the GEMM kernels address x, one expert's weight matrix and the split router matrix
   // through 32-bit byte offsets
   const uint64_t lim = (uint64_t)UINT32_MAX;
@@ -141,8 +143,8 @@ moe_status down_impl(const moe_dims& d, const uint16_t* h, const int32_t* offset
 
 moe_status combine_impl(const moe_dims& d, const float* y_routed, const int32_t* inv,
                         const float* w, const float* y_shared, uint16_t* out, hipStream_t s) {
-  return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, out, d.tokens, d.d_model,
-                                        d.top_k, s));
+  return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, nullptr, out, d.tokens,
+                                        d.d_model, d.top_k, s));
 }
 
 bool shared_ptrs_ok(const moe_dims& d, const void* a, const void* b) {
@@ -202,9 +204,86 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
   return P;
 }
 
+// The layer on an already-normalised bf16 input x; residual (or null) is added to the
+// output before its rounding.  Arguments checked by the callers.
+moe_status forward_impl(const moe_dims& d, const uint16_t* x, const float* w_router,
+                        const float* bias, const uint16_t* w1, const uint16_t* w3,
+                        const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
+                        const uint16_t* ws2, const uint16_t* residual, uint16_t* out, void* ws,
+                        hipStream_t s) {
+  const Layout L = layout(d);
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* w = at<float>(ws, L.w);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  float* y_routed = at<float>(ws, L.y);
+  float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
+  MOE_TRY(route_impl(d, x, w_router, bias, idx, w, nullptr, ws, s));
+  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s));
+  MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s));
+  MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s));
+  return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, residual, out, d.tokens,
+                                        d.d_model, d.top_k, s));
+}
+
+moe_status check_forward_args(const moe_dims& d, const float* w_router, const float* bias,
+                              const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                              const uint16_t* ws1, const uint16_t* ws3, const uint16_t* ws2,
+                              uint16_t* out, void* ws, size_t ws_bytes) {
+  MOE_NEED(aligned(w_router, 16) && aligned(bias, 4));
+  MOE_NEED(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(out, 16));
+  if (has_shared(d)) MOE_NEED(aligned(ws1, 16) && aligned(ws3, 16) && aligned(ws2, 16));
+  return check_ws(d, ws, ws_bytes);
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                       const float* bias, const uint16_t* w1, const uint16_t* w3,
+                       const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
+                       const uint16_t* ws2, uint16_t* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x, 16));
+  MOE_TRY(check_forward_args(d, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, ws, ws_bytes));
+  (void)hipGetLastError();
+  return forward_impl(d, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, nullptr, out, ws,
+                      (hipStream_t)stream);
+}
+
+moe_status moe_block_workspace_bytes(const moe_dims* dims, size_t* bytes) {
+  MOE_TRY(check_dims(dims));
+  MOE_NEED(bytes != nullptr);
+  *bytes = layout(*dims).total + align_up((size_t)dims->tokens * dims->d_model * 2);
+  return MOE_OK;
+}
+
+moe_status moe_forward_block(const moe_dims* dims, const uint16_t* x_res, const float* norm_w,
+                             float norm_eps, const float* w_router, const float* bias,
+                             const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                             const uint16_t* ws1, const uint16_t* ws3, const uint16_t* ws2,
+                             uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x_res, 16) && aligned(norm_w, 4) && x_res != out);
+  if (!(norm_eps >= 0.0f) || !isfinite(norm_eps)) return MOE_EINVAL;
+  MOE_TRY(check_forward_args(d, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, ws, ws_bytes));
+  const size_t base = layout(d).total;
+  if (ws_bytes < base + align_up((size_t)d.tokens * d.d_model * 2)) return MOE_EWORKSPACE;
+  (void)hipGetLastError();
+  const hipStream_t s = (hipStream_t)stream;
+  uint16_t* x_ffn = at<uint16_t>(ws, base);
+  MOE_TRY(hip_status(moe::launch_rmsnorm(x_res, norm_w, x_ffn, d.tokens, d.d_model, norm_eps, s)));
+  return forward_impl(d, x_ffn, w_router, bias, w1, w3, w2, ws1, ws3, ws2, x_res, out, ws, s);
+}
 
 const char* moe_status_str(int status) {
   switch (status) {
@@ -307,37 +386,6 @@ moe_status moe_combine(const moe_dims* dims, const float* y_routed, const int32_
   if (y_shared != nullptr) MOE_NEED(aligned(y_shared, 16));
   (void)hipGetLastError();
   return combine_impl(d, y_routed, inv_perm, topk_w, y_shared, out, (hipStream_t)stream);
-}
-
-moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_router,
-                       const float* bias, const uint16_t* w1, const uint16_t* w3,
-                       const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
-                       const uint16_t* ws2, uint16_t* out, void* ws, size_t ws_bytes,
-                       void* stream) {
-  MOE_TRY(check_dims(dims));
-  const moe_dims& d = *dims;
-  if (d.tokens == 0) return MOE_OK;
-  MOE_NEED(aligned(x, 16) && aligned(w_router, 16) && aligned(bias, 4));
-  MOE_NEED(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(out, 16));
-  if (has_shared(d)) MOE_NEED(aligned(ws1, 16) && aligned(ws3, 16) && aligned(ws2, 16));
-  MOE_TRY(check_ws(d, ws, ws_bytes));
-  (void)hipGetLastError();
-  const hipStream_t s = (hipStream_t)stream;
-  const Layout L = layout(d);
-  int32_t* idx = at<int32_t>(ws, L.idx);
-  float* w = at<float>(ws, L.w);
-  int32_t* counts = at<int32_t>(ws, L.counts);
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* perm = at<int32_t>(ws, L.perm);
-  int32_t* inv = at<int32_t>(ws, L.inv);
-  uint16_t* h = at<uint16_t>(ws, L.h);
-  float* y_routed = at<float>(ws, L.y);
-  float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
-  MOE_TRY(route_impl(d, x, w_router, bias, idx, w, nullptr, ws, s));
-  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s));
-  MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s));
-  MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s));
-  return combine_impl(d, y_routed, inv, w, y_shared, out, s);
 }
 
 }  // extern "C"

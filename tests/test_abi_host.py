@@ -65,6 +65,8 @@ def test_workspace_bytes_grow_with_tokens():
     (dict(routed_scale=float("nan")), M.MOE_EINVAL),
     (dict(tokens=1 << 40), M.MOE_EUNSUPPORTED),
     (dict(tokens=300_000), M.MOE_EUNSUPPORTED),          # x would need 4 GiB or more
+    (dict(tokens=(1 << 23) + 1, d_model=64, d_expert=64, d_shared=64, top_k=1),
+     M.MOE_EUNSUPPORTED),                                  # per-token grids above 2^32 items
 ])
 def test_bad_dims_rejected(bad, code):
     kw = dict(tokens=128, d_model=7168, n_experts=384, top_k=8, d_expert=2048, d_shared=2048,
@@ -130,3 +132,26 @@ def test_latent_dims_checked():
                                 n.value, None) == M.MOE_EINVAL
     assert L.moe_forward_latent(ctypes.byref(d), 3584, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 n.value - 1, None) == M.MOE_EWORKSPACE
+
+
+def test_block_arguments_checked():
+    L = M.lib()
+    d = _k2(128)
+    P = _fake(0x100000)
+    Q = _fake(0x200000)
+    base = M.moe_workspace_bytes(d)
+    need = M.moe_block_workspace_bytes(d)
+    assert need == base + 128 * 7168 * 2
+    args = lambda x, g, eps, out, n: (ctypes.byref(d), x, g, ctypes.c_float(eps), P, P, P, P, P,  # noqa: E731
+                                      P, P, P, out, P, n, None)
+    # the x_ffn buffer is part of the workspace
+    assert L.moe_forward_block(*args(P, P, 1e-6, Q, base)) == M.MOE_EWORKSPACE
+    assert L.moe_forward_block(*args(P, P, 1e-6, Q, need - 1)) == M.MOE_EWORKSPACE
+    # output aliasing the residual, null gain, bad eps
+    assert L.moe_forward_block(*args(P, P, 1e-6, P, need)) == M.MOE_EINVAL
+    assert L.moe_forward_block(*args(P, None, 1e-6, Q, need)) == M.MOE_EINVAL
+    assert L.moe_forward_block(*args(P, P, -1.0, Q, need)) == M.MOE_EINVAL
+    assert L.moe_forward_block(*args(P, P, float("nan"), Q, need)) == M.MOE_EINVAL
+    z = _k2(0)
+    assert L.moe_forward_block(ctypes.byref(z), None, None, ctypes.c_float(1e-6), None, None, None,
+                               None, None, None, None, None, None, None, 0, None) == M.MOE_OK

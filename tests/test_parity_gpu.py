@@ -376,16 +376,6 @@ def test_workspace_too_small_rejected_on_device():
 
 
 # ------------------------------------------------------------------ K2 shape
-@pytest.fixture(scope="module")
-def k2_weights():
-    say("generating K2-shape weights on the GPU (384 experts, d 7168, I 2048)")
-    w = S.make_weights("k2_decode", DEV)
-    torch.cuda.synchronize()
-    yield w
-    del w
-    torch.cuda.empty_cache()
-
-
 def _k2_case(name, k2_weights, sample):
     cfg = S.CONFIGS[name]
     inp = dict(k2_weights)
