@@ -157,7 +157,11 @@ __device__ __forceinline__ void store_gateup(uint16_t* dst, f32x4_t g, f32x4_t u
   *reinterpret_cast<u32x2_t*>(dst) = packed;
 }
 
-// Store four consecutive outputs (features nn .. nn+3) of grouped row p.
+// Store four consecutive outputs (features nn .. nn+3) of grouped row p.  N is a
+// multiple of 64 for every bf16 output (d, I and the latent width are); only the fp32
+// output of the router GEMM (N = 3E) can have N % 4 != 0, and then the row is neither
+// 16-byte aligned nor a whole number of 4-feature groups, so it is stored one float at a
+// time and features >= N are dropped (they would land on the next row).
 template <int EPI>
 __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x4_t v,
                                        f32x4_t u) {
@@ -166,7 +170,13 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
     store_gateup(a.C + p * N + nn, v, u);
   } else if (EPI == kF32) {
     float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
-    *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
+    if ((N & 3) == 0) {
+      *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (nn + i < N) yrow[nn + i] = v[i];
+    }
   } else {
     if (EPI == kAddBF16) v += *reinterpret_cast<const f32x4_t*>(a.R + p * N + nn);
     u32x2_t packed;
