@@ -25,7 +25,7 @@ if ROOT not in sys.path:
 
 METRIC = "K2 MoE-layer tokens/s (128 & 8192 tok, bf16); % of HBM / MFMA peak"
 # the gate/up kernel each workload runs (decode: a few rows per expert; prefill: many)
-GATEUP_KERNEL = {"k2_decode": "ffn_skinny_kernel<2, 8, true>", "k2_prefill": "ffn_stream_kernel<true>"}
+GATEUP_KERNEL = {"k2_decode": "ffn_skinny_kernel<2, 8, 0>", "k2_prefill": "ffn_stream_kernel<0>"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
@@ -47,8 +47,9 @@ def kernel_source_hash():
 
 def write_traffic(fetch_csv, write_csv):
     """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of a
-    --copy-calibration run into profiles/hbm_traffic.json: bytes per launch per kernel,
-    each counter scaled by what it reads for the 1 GiB calibration copy."""
+    --copy-calibration run into profiles/hbm_traffic.json: bytes per launch per kernel and
+    launch grid (one kernel can serve several workloads), each counter scaled by what it
+    reads for the 1 GiB calibration copy."""
     import csv
     import collections
     out = {"source_sha256": kernel_source_hash(), "kernels": {}, "scale": {}}
@@ -61,11 +62,12 @@ def write_traffic(fetch_csv, write_csv):
         for r in rows:
             if "copyBuffer" in r["Kernel_Name"]:
                 continue
-            per[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024 * scale)
-        for k, v in per.items():
-            key = "read_bytes" if counter == "FETCH_SIZE" else "write_bytes"
-            out["kernels"].setdefault(k, {})[key] = sum(v) / len(v)
-            out["kernels"][k]["launches"] = len(v)
+            per[(r["Kernel_Name"], r["Grid_Size"])].append(float(r["Counter_Value"]) * 1024 * scale)
+        key = "read_bytes" if counter == "FETCH_SIZE" else "write_bytes"
+        for (name, grid), v in per.items():
+            g = out["kernels"].setdefault(name, {}).setdefault(grid, {})
+            g[key] = sum(v) / len(v)
+            g["launches"] = len(v)
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
     print(json.dumps(out, indent=1))
@@ -73,7 +75,8 @@ def write_traffic(fetch_csv, write_csv):
 
 def traffic_for(kernel_substr):
     """HBM bytes per launch of a kernel from the committed counter summary, or None when it
-    is missing or the kernel sources changed since the counters were taken."""
+    is missing, the kernel ran with more than one grid there (several workloads), or the
+    kernel sources changed since the counters were taken."""
     try:
         with open(TRAFFIC_JSON) as f:
             t = json.load(f)
@@ -81,9 +84,11 @@ def traffic_for(kernel_substr):
         return None
     if t.get("source_sha256") != kernel_source_hash():
         return None
-    for name, v in t["kernels"].items():
-        if kernel_substr in name and "read_bytes" in v and "write_bytes" in v:
-            return v["read_bytes"] + v["write_bytes"]
+    for name, grids in t["kernels"].items():
+        if kernel_substr in name and len(grids) == 1:
+            v = next(iter(grids.values()))
+            if "read_bytes" in v and "write_bytes" in v:
+                return v["read_bytes"] + v["write_bytes"]
     return None
 
 
