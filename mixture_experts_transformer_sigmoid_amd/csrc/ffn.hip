@@ -294,13 +294,14 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
 // The main loop is straight-line code: it is instantiated for 4, 8, 12 or 16 live row
 // fragments (the tile's rows rounded up to 64: rows past the end cost at most three
 // fragments of MFMAs; finer steps measured slower, the extra copies of the loop crowd the
-// instruction cache), prefetch indices are clamped instead of guarded, and three chunks
-// are unrolled per iteration so the register ring is indexed statically.  Branches inside
-// the loop would make the compiler's wait-count analysis conservative at every join and
-// wait for the prefetched loads too.
+// instruction cache), prefetch indices are clamped instead of guarded, and one ring
+// period (RING / 2 chunks) is unrolled per iteration so the register ring is indexed
+// statically.  Branches inside the loop would make the compiler's wait-count analysis
+// conservative at every join and wait for the prefetched loads too.
 // Tuning constants of the stream kernel, measured on MI355X at the K2 prefill shape
 // (gate/up, ms): 64-row granules 6.33 vs 128-row 6.95 vs none 6.60; read groups of 1
-// fragment 6.33, 2: 6.34, 4: 6.88; without the scheduling barrier 8.40.
+// fragment 6.33, 2: 6.34, 4: 6.88; without the scheduling barrier 8.40; ring depth 6:
+// 6.25, 8: 6.87, 10: 7.47 (spills); weight requests batched two k-steps at a time 6.38.
 #ifndef MOE_STREAM_NL_STEP
 #define MOE_STREAM_NL_STEP 4      // live row fragments are rounded up to this multiple
 #endif
@@ -309,6 +310,12 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
 #endif
 #ifndef MOE_STREAM_SCHED_BARRIER
 #define MOE_STREAM_SCHED_BARRIER 1  // keep reads one group ahead of their MFMAs
+#endif
+#ifndef MOE_STREAM_RING
+#define MOE_STREAM_RING 6         // k-steps of weights held in registers per wave (even)
+#endif
+#ifndef MOE_STREAM_BATCH
+#define MOE_STREAM_BATCH 1        // k-steps of weights requested together (1 or 2)
 #endif
 
 struct StreamCtx {
@@ -328,9 +335,11 @@ __device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
                                             f32x4_t (&acc)[16][2]) {
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int BM = 256, BK = 64, NW = 2, NA = 4;
+  constexpr int D = MOE_STREAM_RING, P = MOE_STREAM_BATCH;
+  static_assert(D % 2 == 0 && D >= 4 && (P == 1 || P == 2), "weight ring shape");
   const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const int nks = c_.nks, nc = c_.nc;
-  u32x4_t W0[NW], W1[NW], W2[NW], W3[NW], W4[NW], W5[NW], AR[NA];
+  u32x4_t W[D][NW], AR[NA];
 
   auto load_w = [&](u32x4_t* S, int ks) {
     const uint32_t kb = (uint32_t)(ks < nks ? ks : nks - 1) * 64;  // past the end: re-read
@@ -373,52 +382,47 @@ __device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
       if (MOE_STREAM_SCHED_BARRIER) __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // one k-step: refill the slot freed by the previous step, then multiply this one
-  auto kstep = [&](int buf, int kk, const u32x4_t* use, u32x4_t* fill, int ks_fill) {
-    load_w(fill, ks_fill);
-    mma_step(buf, kk, use);
-  };
   // chunk c+1's activations (in AR) go to the other LDS buffer; AR then loads chunk c+2
   auto next_chunk = [&](int c) {
     store_a((c + 1) & 1);
     load_a(c + 2);
     lds_barrier();
   };
+  // Chunk j of a ring period (k-steps s = 2c + 2j and s + 1, ring slots t = 2j, t + 1).
+  // P = 1: each k-step refills the slot freed just before it, D - 1 k-steps in flight.
+  // P = 2: both refills of the chunk are issued together at its start (128 contiguous
+  // bytes of every weight row at once), D - 2 k-steps in flight.
+  auto chunk = [&](int c, int j) {
+    const int t = 2 * j, s = 2 * c + t;
+    if (P == 1) {
+      load_w(W[(t + D - 1) % D], s + D - 1);
+      mma_step((c + j) & 1, 0, W[t]);
+      load_w(W[t], s + D);
+      mma_step((c + j) & 1, 1, W[t + 1]);
+    } else {
+      load_w(W[(t + D - 2) % D], s + D - 2);
+      load_w(W[(t + D - 1) % D], s + D - 1);
+      mma_step((c + j) & 1, 0, W[t]);
+      mma_step((c + j) & 1, 1, W[t + 1]);
+    }
+    next_chunk(c + j);
+  };
 
   load_a(0);
-  load_w(W0, 0);
-  load_w(W1, 1);
-  load_w(W2, 2);
-  load_w(W3, 3);
-  load_w(W4, 4);
+#pragma unroll
+  for (int t = 0; t < D - P; ++t) load_w(W[t], t);
   store_a(0);
   load_a(1);
   lds_barrier();
   int c = 0;
-  // at the top of an iteration W0..W4 hold k-steps 2c .. 2c+4 and W5 is free
-  for (; c + 3 <= nc; c += 3) {
-    const int k0 = 2 * c;
-    kstep(c & 1, 0, W0, W5, k0 + 5);
-    kstep(c & 1, 1, W1, W0, k0 + 6);
-    next_chunk(c);
-    kstep((c + 1) & 1, 0, W2, W1, k0 + 7);
-    kstep((c + 1) & 1, 1, W3, W2, k0 + 8);
-    next_chunk(c + 1);
-    kstep((c + 2) & 1, 0, W4, W3, k0 + 9);
-    kstep((c + 2) & 1, 1, W5, W4, k0 + 10);
-    next_chunk(c + 2);
+  // at the top of an iteration W[t] holds k-step 2c + t for t < D - P
+  for (; c + D / 2 <= nc; c += D / 2) {
+#pragma unroll
+    for (int j = 0; j < D / 2; ++j) chunk(c, j);
   }
-  if (c < nc) {
-    const int k0 = 2 * c;
-    kstep(c & 1, 0, W0, W5, k0 + 5);
-    kstep(c & 1, 1, W1, W0, k0 + 6);
-    next_chunk(c);
-    if (c + 1 < nc) {
-      kstep((c + 1) & 1, 0, W2, W1, k0 + 7);
-      kstep((c + 1) & 1, 1, W3, W2, k0 + 8);
-      next_chunk(c + 1);
-    }
-  }
+#pragma unroll
+  for (int j = 0; j < D / 2 - 1; ++j)
+    if (c + j < nc) chunk(c, j);
 }
 
 // stream_loop instantiated for the smallest multiple of STEP fragments >= nfrag
@@ -560,6 +564,14 @@ dim3 grid_for(const FfnShape& sh, int BM, int BN, int N) {
 
 int64_t ffn_max_tiles(const FfnShape& sh) { return max_tiles_for(sh, kSkinnyBM); }
 
+// The 256-row-tile kernel; both variants cover 128 (gate/up) or 256 (otherwise) features
+// of N per block, so they share the grid.
+// The 256-row-tile kernel covers 128 (gate/up) or 256 (otherwise) features of N per block.
+template <int EPI>
+void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a) {
+  hipLaunchKernelGGL(ffn_stream_kernel<EPI>, grid, dim3(512), 0, s, a);
+}
+
 hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
                         DenseOut mode, float* Cf, uint16_t* Cb, const float* R, Tile* tiles,
                         int32_t* ntiles, hipStream_t s) {
@@ -587,15 +599,15 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
              gk2 = grid_for(sh, BM, 128, N);
   switch (mode) {
     case DenseOut::kF32:
-      if (wide) hipLaunchKernelGGL(ffn_stream_kernel<kF32>, gs, dim3(512), 0, s, a);
+      if (wide) launch_wide<kF32>(gs, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, kF32>), gk, dim3(256), 0, s, a);
       break;
     case DenseOut::kBF16:
-      if (wide) hipLaunchKernelGGL(ffn_stream_kernel<kBF16>, gs, dim3(512), 0, s, a);
+      if (wide) launch_wide<kBF16>(gs, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kBF16>), gk2, dim3(256), 0, s, a);
       break;
     case DenseOut::kAddBF16:
-      if (wide) hipLaunchKernelGGL(ffn_stream_kernel<kAddBF16>, gs, dim3(512), 0, s, a);
+      if (wide) launch_wide<kAddBF16>(gs, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kAddBF16>), gk2, dim3(256), 0, s, a);
       break;
   }
@@ -627,8 +639,7 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   a.K = sh.d;
   a.E = sh.E;
   if (wide)
-    hipLaunchKernelGGL(ffn_stream_kernel<kSwiGLU>, grid_for(sh, BM, kStreamBNGateUp, a.N), dim3(512),
-                       0, s, a);
+    launch_wide<kSwiGLU>(grid_for(sh, BM, kStreamBNGateUp, a.N), s, a);
   else
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kSwiGLU>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
@@ -660,8 +671,7 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.K = sh.I;
   a.E = sh.E;
   if (wide)
-    hipLaunchKernelGGL(ffn_stream_kernel<kF32>, grid_for(sh, BM, kStreamBNDown, a.N), dim3(512),
-                       0, s, a);
+    launch_wide<kF32>(grid_for(sh, BM, kStreamBNDown, a.N), s, a);
   else
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
