@@ -39,6 +39,8 @@ Readings where the pages are silent (each also listed in the design doc):
   it is rounded to fp32, then to bf16 (nearest-even both times) before use.
 * The residual x'_n is added to Delta_ffn in full precision (the kernel adds it in fp32
   and rounds the sum to bf16 once).
+* FP8 expert weights: OCP E4M3 values with one fp32 scale per 128 x 128 block of each
+  [out, in] matrix; the weight is value x scale, exactly (dequant_fp8_blocks).
 
 Parity pins: see tests/test_oracle_pins.py.  The output values themselves have no
 worked example on the pages ("parity unpinned" beyond the invariants and closed
@@ -123,6 +125,45 @@ def round_bf16(v):
 
 def _f64(a):
     return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------- FP8 block-scaled weights
+# "nnterp encyclopedia · kimi_k2" (loading a K2 checkpoint) and "Kimi K2 · Transformer
+# blocks" (parameter accounting, which leaves out "FP8 block scales"): K2's expert weights
+# are stored as FP8 values in blocks, each block with its own scale.  The pages give
+# neither the FP8 encoding nor the block size; the reading taken here is the OCP FP8
+# E4M3 encoding (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
+# infinities, exponent and mantissa all ones = NaN) and square 128 x 128 blocks of the
+# [out, in] matrix, one fp32 scale each, the stored weight being value x scale.
+FP8_BLOCK = 128
+
+
+def e4m3_value(code):
+    """The real number an OCP E4M3 byte encodes (float64; NaN for the two NaN codes)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6          # subnormal: 0.m x 2^(1 - 7)
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def dequant_fp8_blocks(q, scale, block=FP8_BLOCK):
+    """w[n, k] = value(q[n, k]) * scale[n // block, k // block], float64.
+
+    q: uint8 [N, K] (or [..., N, K]); scale: [ceil(N / block), ceil(K / block)] (same
+    leading dims)."""
+    q = np.asarray(q, dtype=np.uint8)
+    sc = _f64(scale)
+    v = E4M3_TABLE[q]
+    rows = np.arange(q.shape[-2]) // block
+    cols = np.arange(q.shape[-1]) // block
+    return v * sc[..., rows[:, None], cols[None, :]]
 
 
 # ---------------------------------------------------------------------------- router

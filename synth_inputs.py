@@ -15,6 +15,8 @@ Skewed routing: b_e = -0.5 * ln(rank_e) with rank a seeded permutation of 1..E, 
 few experts take most tokens and many take none.
 Latent variant: W_down ~ N(0, 1/d) [L, d], experts on the latent width L, W_up ~
 N(0, 1/L) [d, L].
+FP8 weights: the same N(0, 1/fan_in) draws stored as E4M3 codes with one fp32 scale
+per 128 x 128 block (block max |w| / 448), as a block-scaled checkpoint holds them.
 Block (pre-MoE norm + residual): the residual stream x'_n = N(0, 1) * c_j with a
 per-channel scale c_j ~ U(0.25, 4) (so the norm has real work), bf16; the norm gain
 gamma ~ U(0.5, 1.5) rounded to bf16 (a checkpoint's gain is bf16), passed as fp32.
@@ -117,6 +119,52 @@ def make_weights(cfg, device="cpu", seed=0, shared=True):
     if L:
         out["w_down"] = normal((L, d), 1.0 / math.sqrt(d), torch.bfloat16, device, seed, TID["w_down"])
         out["w_up"] = normal((d, L), 1.0 / math.sqrt(L), torch.bfloat16, device, seed, TID["w_up"])
+    return out
+
+
+FP8_BLOCK = 128
+FP8_MAX = 448.0
+
+
+def _fp8_blocks(w):
+    """Store an fp32 [N, K] matrix the way an FP8 block-scaled checkpoint does: one fp32
+    scale per 128 x 128 block (the block's largest magnitude over 448, the largest E4M3
+    value; 1 for an all-zero block) and E4M3 bytes of w / scale (torch's float8_e4m3fn
+    cast, nearest even).  Returns (uint8 [N, K], float32 [N/128, K/128])."""
+    N, K = w.shape
+    blk = w.reshape(N // FP8_BLOCK, FP8_BLOCK, K // FP8_BLOCK, FP8_BLOCK)
+    amax = blk.abs().amax(dim=(1, 3))
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    q = (blk / scale[:, None, :, None]).reshape(N, K).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8), scale.to(torch.float32)
+
+
+def _stacked_fp8(n, shape, std, device, seed, tid):
+    q = torch.empty((n,) + tuple(shape), dtype=torch.uint8, device=device)
+    sc = torch.empty((n, shape[0] // FP8_BLOCK, shape[1] // FP8_BLOCK), dtype=torch.float32,
+                     device=device)
+    for e in range(n):
+        q[e], sc[e] = _fp8_blocks(normal(shape, std, torch.float32, device, seed, tid, e + 1))
+    return q, sc
+
+
+def make_fp8_weights(cfg, device="cpu", seed=0, shared=True):
+    """Expert weights in FP8 block-scaled form: for each of w1, w3, w2 (and ws1, ws3, ws2)
+    a uint8 array of E4M3 codes with the bf16 layout, plus "<name>_scale" [.., N/128,
+    K/128] fp32.  The same normal draws as make_weights, before any rounding; the router
+    stays fp32."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    d, E = cfg["d_model"], cfg["n_experts"]
+    I, Is = cfg["d_expert"], cfg["d_shared"]
+    out = {"w_r": normal((E, d), 1.0 / math.sqrt(d), torch.float32, device, seed, TID["w_r"])}
+    out["w1"], out["w1_scale"] = _stacked_fp8(E, (I, d), 1.0 / math.sqrt(d), device, seed, TID["w1"])
+    out["w3"], out["w3_scale"] = _stacked_fp8(E, (I, d), 1.0 / math.sqrt(d), device, seed, TID["w3"])
+    out["w2"], out["w2_scale"] = _stacked_fp8(E, (d, I), 1.0 / math.sqrt(I), device, seed, TID["w2"])
+    if shared and Is:
+        for name, shape, fan in (("ws1", (Is, d), d), ("ws3", (Is, d), d), ("ws2", (d, Is), Is)):
+            out[name], out[name + "_scale"] = _fp8_blocks(
+                normal(shape, 1.0 / math.sqrt(fan), torch.float32, device, seed, TID[name]))
     return out
 
 

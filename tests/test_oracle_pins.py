@@ -417,3 +417,43 @@ def test_block_token_subset_matches_full():
     full = _block(L, L["x"], g)
     sub = _block(L, L["x"], g, tokens=[0, 7, 19])
     np.testing.assert_allclose(sub["out"], full["out"][[0, 7, 19]], rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------------ FP8 block-scaled weights (f3)
+def test_e4m3_table_against_torch_float8():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = mo.E4M3_TABLE
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.isnan(got).sum() == 2 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+def test_e4m3_landmarks():
+    v = mo.e4m3_value
+    assert v(0x7E) == 448.0                      # largest finite: 1.75 x 2^8
+    assert v(0x08) == 2.0 ** -6                  # smallest normal
+    assert v(0x01) == 2.0 ** -9                  # smallest subnormal
+    assert v(0x07) == 7 * 2.0 ** -9              # largest subnormal
+    assert v(0x38) == 1.0 and v(0xB8) == -1.0 and v(0x3C) == 1.5
+    assert v(0x00) == 0.0 and math.copysign(1.0, v(0x80)) == -1.0
+
+
+def test_block_dequant_indexes_blocks_by_out_then_in():
+    # a 2 x 3 grid of blocks (N = 256, K = 384) with a distinct scale per block and every
+    # code 1.0: each weight equals its own block's scale (a transposed block index fails)
+    q = np.full((256, 384), 0x38, dtype=np.uint8)
+    sc = np.array([[1.0, 2.0, 3.0], [5.0, 7.0, 11.0]])
+    w = mo.dequant_fp8_blocks(q, sc)
+    for bn in range(2):
+        for bk in range(3):
+            blk = w[bn * 128:(bn + 1) * 128, bk * 128:(bk + 1) * 128]
+            assert np.all(blk == sc[bn, bk])
+    # codes are decoded per element: a single -1.5 at (130, 200) gives -1.5 x 7
+    q2 = q.copy()
+    q2[130, 200] = 0xBC
+    assert mo.dequant_fp8_blocks(q2, sc)[130, 200] == -10.5
+    # leading (expert) dims broadcast
+    w3 = mo.dequant_fp8_blocks(np.stack([q, q2]), np.stack([sc, 2 * sc]))
+    assert np.array_equal(w3[1], 2 * mo.dequant_fp8_blocks(q2, sc))
