@@ -32,7 +32,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_transformer_sigmoid_amd", "csrc", f)
-                  for f in ("ffn.hip", "common.h")]
+                  for f in ("ffn.hip", "grouped.h", "common.h")]
 COPY_BYTES = 1 << 30
 
 
@@ -101,6 +101,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latent", action="store_true", help="skip the latent-MoE figure")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight figures")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the fused norm + residual block figure")
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens in the oracle sample")
@@ -174,6 +175,63 @@ def time_block(M, torch, S, cfg, weights, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
+
+
+def time_fp8(M, torch, S, dev, act, steps, warmup, prefill):
+    """The layer with FP8 block-scaled expert weights (moe_forward_fp8) at decode (and
+    prefill), plus its decode gate/up launch for the roofline."""
+    cfg = S.CONFIGS["k2_decode"]
+    w = S.make_fp8_weights(cfg, dev)
+    fw = M.fp8_weights(w)
+    dims = M.dims_for(cfg)
+    T, d, I = cfg["tokens"], cfg["d_model"], cfg["d_expert"]
+    ws = M.workspace(dims, dev)
+    out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, n, w_):
+        for _ in range(w_):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(n):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    ms = timed(lambda: M.moe_forward_fp8(dims, act["x"], w["w_r"], act["b"], fw, out, ws), steps,
+               warmup)
+    st = split_state(M, torch, dims, {"x": act["x"], "w_r": w["w_r"], "b": act["b"]}, ws)
+    active = int((st["counts"] > 0).sum())
+    h = torch.empty(T * 9, I, dtype=torch.bfloat16, device=dev)
+    gu = timed(lambda: M.moe_expert_gate_up_fp8(dims, act["x"], st["perm"], st["offsets"], fw, h,
+                                                ws), steps, warmup)
+    units = active + 1
+    gu_bytes = units * 2 * I * d + units * 2 * (I // 128) * (d // 128) * 4 + T * d * 2 + T * 9 * I * 2
+    layer_bytes = (units * 3 * I * d + units * 3 * (I // 128) * (d // 128) * 4
+                   + cfg["n_experts"] * d * 4 + 2 * T * d * 2)
+    res = {"entry": "moe_forward_fp8 (E4M3 expert weights, one fp32 scale per 128x128 block)",
+           "decode_ms_per_step": ms, "decode_tokens_per_s": T / (ms * 1e-3),
+           "decode_layer_hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
+           "gate_up": {"kernel": "ffn_skinny_fp8_kernel<2, 2, 0>", "ms_per_launch": gu,
+                       "bytes_per_launch": gu_bytes, "achieved_gbs": gu_bytes / (gu * 1e-3) / 1e9,
+                       "frac": gu_bytes / (gu * 1e-3) / 1e9 / HBM_PEAK_GBS},
+           "active_experts": active}
+    if prefill:
+        pcfg = S.CONFIGS["k2_prefill"]
+        pact = S.make_activations(pcfg, dev)
+        pdims = M.dims_for(pcfg)
+        del ws, h
+        pws = M.workspace(pdims, dev)
+        pout = torch.empty(pcfg["tokens"], d, dtype=torch.bfloat16, device=dev)
+        pms = timed(lambda: M.moe_forward_fp8(pdims, pact["x"], w["w_r"], pact["b"], fw, pout, pws),
+                    max(3, min(steps, 10)), 1)
+        flops = 2 * 3 * d * I * pcfg["tokens"] * (pcfg["top_k"] + 1)
+        res.update({"prefill_ms_per_step": pms, "prefill_tokens_per_s": pcfg["tokens"] / (pms * 1e-3),
+                    "prefill_mfma_tflops": flops / (pms * 1e-3) / 1e12})
+    return res
 
 
 def split_state(M, torch, dims, inp, ws):
@@ -386,6 +444,16 @@ def main():
             f"{ptf:.0f} TFLOP/s ({100 * ptf / MFMA_BF16_PEAK_TFLOPS:.1f}% MFMA)")
         del pws, pin
 
+    if not args.no_fp8:
+        log("timing moe_forward_fp8 (FP8 block-scaled expert weights)")
+        fres = time_fp8(M, torch, S, dev, {"x": inp["x"], "b": inp["b"]}, args.steps,
+                        args.warmup, not args.no_prefill)
+        res["fp8"] = fres
+        log(f"fp8: decode {fres['decode_ms_per_step']:.3f} ms/step "
+            f"({fres['decode_tokens_per_s']:.0f} tok/s), gate/up {fres['gate_up']['ms_per_launch']:.3f} ms"
+            f" = {fres['gate_up']['achieved_gbs']:.0f} GB/s"
+            + (f"; prefill {fres['prefill_ms_per_step']:.3f} ms" if "prefill_ms_per_step" in fres else ""))
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_sample} tokens")
         res["cpu_baseline"] = cpu_baseline(torch, S, cfg, inp, args.cpu_sample)

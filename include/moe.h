@@ -170,6 +170,47 @@ moe_status moe_forward_block(const moe_dims* dims, const uint16_t* x_res, const 
                              const uint16_t* ws1, const uint16_t* ws3, const uint16_t* ws2,
                              uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* FP8 block-scaled expert weights, the form K2's checkpoints store them in ("nnterp
+ * encyclopedia · kimi_k2", loading a K2 checkpoint: FP8 blocks with per-block scales;
+ * the parameter table of "Kimi K2 · Transformer blocks" leaves the block scales out).
+ * Codes are OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 = NaN), one byte per weight in the bf16 layouts above; one fp32
+ * scale per 128 x 128 block of each [out, in] matrix; weight = code value x scale.
+ * The kernels dequantise exactly: codes become bf16 without rounding, and each 128-k
+ * block's fp32 partial sum is multiplied by its scale.  Requires d and I (and Is) to be
+ * multiples of 128 and at most 16384 (else MOE_EUNSUPPORTED).  All pointers are device
+ * pointers; codes 16-byte aligned, scales 4-byte aligned; the shared expert's six
+ * pointers are used iff d_shared > 0.  The router weights stay fp32 (moe_forward_fp8's
+ * w_router). */
+typedef struct moe_fp8_weights {
+  const uint8_t* w1;       /* [E, I, d] */
+  const uint8_t* w3;       /* [E, I, d] */
+  const uint8_t* w2;       /* [E, d, I] */
+  const float* w1_scale;   /* [E, I/128, d/128] */
+  const float* w3_scale;   /* [E, I/128, d/128] */
+  const float* w2_scale;   /* [E, d/128, I/128] */
+  const uint8_t* ws1;      /* [Is, d] */
+  const uint8_t* ws3;      /* [Is, d] */
+  const uint8_t* ws2;      /* [d, Is] */
+  const float* ws1_scale;  /* [Is/128, d/128] */
+  const float* ws3_scale;  /* [Is/128, d/128] */
+  const float* ws2_scale;  /* [d/128, Is/128] */
+} moe_fp8_weights;
+
+/* moe_expert_gate_up / moe_expert_down / moe_forward with FP8 expert weights (`w` is a
+ * host pointer to the struct of device pointers); same workspace (moe_workspace_bytes),
+ * outputs and semantics otherwise. */
+moe_status moe_expert_gate_up_fp8(const moe_dims* dims, const uint16_t* x,
+                                  const int32_t* perm_rows, const int32_t* offsets,
+                                  const moe_fp8_weights* w, uint16_t* h, void* ws,
+                                  size_t ws_bytes, void* stream);
+moe_status moe_expert_down_fp8(const moe_dims* dims, const uint16_t* h, const int32_t* offsets,
+                               const moe_fp8_weights* w, float* y_routed, float* y_shared,
+                               void* ws, size_t ws_bytes, void* stream);
+moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                           const float* bias, const moe_fp8_weights* w, uint16_t* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* Latent mixture of experts ("Kimi K3 · Latent up-projection": the router scores the
  * full-width input; the input is projected down to the latent width; the routed experts
  * run on the latent; their gate-weighted sum is RMS-normalised and projected back up; the

@@ -20,7 +20,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 EXPORTS = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_latent_workspace_bytes", "moe_forward_latent",
-           "moe_block_workspace_bytes", "moe_forward_block")
+           "moe_block_workspace_bytes", "moe_forward_block", "moe_expert_gate_up_fp8",
+           "moe_expert_down_fp8", "moe_forward_fp8")
 
 
 class MoeDims(ctypes.Structure):
@@ -28,6 +29,20 @@ class MoeDims(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("d_expert", ctypes.c_int32), ("d_shared", ctypes.c_int32),
                 ("routed_scale", ctypes.c_float)]
+
+
+class MoeFp8Weights(ctypes.Structure):
+    """moe_fp8_weights: device pointers of the E4M3 codes and their block scales."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale",
+        "ws1", "ws3", "ws2", "ws1_scale", "ws3_scale", "ws2_scale")]
+
+
+def fp8_weights(t: dict) -> MoeFp8Weights:
+    """MoeFp8Weights from a dict of device tensors keyed by the field names (the shared
+    expert's entries may be missing)."""
+    return MoeFp8Weights(*[t[n].data_ptr() if t.get(n) is not None else None
+                           for n, _ in MoeFp8Weights._fields_])
 
 
 class MoeError(RuntimeError):
@@ -65,6 +80,9 @@ def lib():
         "moe_block_workspace_bytes": [D, ctypes.POINTER(ctypes.c_size_t)],
         "moe_forward_block": [D, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               _S, _P],
+        "moe_expert_gate_up_fp8": [D, _P, _P, _P, ctypes.POINTER(MoeFp8Weights), _P, _P, _S, _P],
+        "moe_expert_down_fp8": [D, _P, _P, ctypes.POINTER(MoeFp8Weights), _P, _P, _P, _S, _P],
+        "moe_forward_fp8": [D, _P, _P, _P, ctypes.POINTER(MoeFp8Weights), _P, _P, _S, _P],
         "moe_latent_workspace_bytes": [D, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
         "moe_forward_latent": [D, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _S, _P],
@@ -184,6 +202,25 @@ def moe_forward_block(dims, x_res, norm_w, norm_eps, w_router, bias, w1, w3, w2,
                                    float(norm_eps), _ptr(w_router), _ptr(bias), _ptr(w1),
                                    _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out),
                                    wp, wn, _stream(stream)))
+
+
+def moe_expert_gate_up_fp8(dims, x, perm_rows, offsets, w: MoeFp8Weights, h, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_expert_gate_up_fp8(ctypes.byref(dims), _ptr(x), _ptr(perm_rows),
+                                        _ptr(offsets), ctypes.byref(w), _ptr(h), wp, wn,
+                                        _stream(stream)))
+
+
+def moe_expert_down_fp8(dims, h, offsets, w: MoeFp8Weights, y_routed, y_shared, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_expert_down_fp8(ctypes.byref(dims), _ptr(h), _ptr(offsets), ctypes.byref(w),
+                                     _ptr(y_routed), _ptr(y_shared), wp, wn, _stream(stream)))
+
+
+def moe_forward_fp8(dims, x, w_router, bias, w: MoeFp8Weights, out, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_forward_fp8(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias),
+                                 ctypes.byref(w), _ptr(out), wp, wn, _stream(stream)))
 
 
 def moe_latent_workspace_bytes(dims: MoeDims, d_latent: int) -> int:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["route.hip", "permute.hip", "ffn.hip", "combine.hip", "moe_abi.hip"]
+SOURCES = ["route.hip", "permute.hip", "ffn.hip", "ffn_fp8.hip", "combine.hip", "moe_abi.hip"]
 
 ARCH = "gfx950"
 # packed fp32 instructions are switched off for all device code (they are not emitted

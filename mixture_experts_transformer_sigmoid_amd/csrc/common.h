@@ -119,6 +119,32 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
                        const uint16_t* w2, const uint16_t* ws2, float* y_routed,
                        float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s);
 
+// FP8 (E4M3) expert weights with one fp32 scale per 128 x 128 block; device pointers.
+struct Fp8Weights {
+  const uint8_t* w1;       // [E, I, d]
+  const uint8_t* w3;       // [E, I, d]
+  const uint8_t* w2;       // [E, d, I]
+  const float* w1_scale;   // [E, I/128, d/128]
+  const float* w3_scale;   // [E, I/128, d/128]
+  const float* w2_scale;   // [E, d/128, I/128]
+  const uint8_t* ws1;      // [Is, d]   (shared expert; null without one)
+  const uint8_t* ws3;      // [Is, d]
+  const uint8_t* ws2;      // [d, Is]
+  const float* ws1_scale;  // [Is/128, d/128]
+  const float* ws3_scale;  // [Is/128, d/128]
+  const float* ws2_scale;  // [d/128, Is/128]
+};
+constexpr int kFp8Block = 128;
+constexpr int kFp8MaxK = 16384;  // the FP8 kernels keep a row of K/128 scales in LDS
+
+hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
+                              const int32_t* offsets, const Fp8Weights& w, uint16_t* h,
+                              Tile* tiles, int32_t* ntiles, hipStream_t s);
+
+hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
+                           const Fp8Weights& w, float* y_routed, float* y_shared, Tile* tiles,
+                           int32_t* ntiles, hipStream_t s);
+
 // residual (bf16 [T, d]) may be null; when given it is added before the bf16 rounding.
 hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float* topk_w,
                           const float* y_shared, const uint16_t* residual, uint16_t* out,

@@ -1,0 +1,217 @@
+// Grouped-GEMM plumbing shared by the bf16 and FP8 expert kernels: the argument block,
+// the on-device tile list, the XCD-aware work mapping, row gathering and the epilogues.
+// Every definition lives in an unnamed namespace: each source file that includes this
+// gets its own copy.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// Epilogue of a GEMM launch.
+enum Epi : int {
+  kSwiGLU = 0,   // two weight matrices (W1, W3): h = bf16(silu(g) * u) into C
+  kF32 = 1,      // fp32 rows into Y (grouped rows) or Ys (the last group's rows)
+  kBF16 = 2,     // bf16 rows into C
+  kAddBF16 = 3,  // bf16(acc + R[row]) into C, R fp32 with the same layout
+};
+
+struct FfnArgs {
+  const uint16_t* A;      // gate/up: x [T, K]; down: h [rows, K]
+  const int32_t* perm;    // gate/up: slot id of each grouped row
+  int64_t routed_rows;    // T*k: rows at or past this index belong to the shared expert
+  const uint16_t* B1;     // routed weights [E, N, K] (w1, or w2 for down)
+  const uint16_t* B3;     // routed w3 [E, N, K] (gate/up)
+  const uint16_t* S1;     // shared weights [N, K] (ws1, or ws2 for down)
+  const uint16_t* S3;     // shared ws3 (gate/up)
+  uint16_t* C;            // gate/up: h [rows, N] bf16
+  float* Y;               // down: y_routed [T*k, N] fp32
+  float* Ys;              // down: y_shared [T, N] fp32
+  const Tile* tiles;
+  const int32_t* ntiles;
+  int32_t k;              // slots per token (gate/up gather: token = slot / k)
+  int32_t N, K, E;
+  int64_t a_rows;         // rows of A (gate/up: tokens of x)
+  const float* R;         // kAddBF16: fp32 rows added before the bf16 store
+  // FP8 kernels only: E4M3 codes with the layouts of B1, B3, S1, S3, and their fp32
+  // scales, one per 128 x 128 block ([E, N/128, K/128] routed, [N/128, K/128] shared)
+  const uint8_t* Q1;
+  const uint8_t* Q3;
+  const uint8_t* QS1;
+  const uint8_t* QS3;
+  const float* B1s;
+  const float* B3s;
+  const float* S1s;
+  const float* S3s;
+};
+
+// ------------------------------------------------------------------ tile list
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, int64_t routed_rows,
+                                                           int64_t shared_rows, int BM,
+                                                           int64_t capacity,
+                                                           Tile* __restrict__ tiles,
+                                                           int32_t* __restrict__ ntiles) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t routed_total;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t o0 = 0, o1 = 0, n = 0;
+  if (tid < E) {
+    // clamp: rows must stay inside the grouped block whatever the caller passed
+    o0 = min<int64_t>(max(offsets[tid], 0), routed_rows);
+    o1 = min<int64_t>(max<int64_t>(offsets[tid + 1], o0), routed_rows);
+    n = (o1 - o0 + BM - 1) / BM;
+  }
+  int32_t v = n;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t acc = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int32_t x = wsum[w];
+      wsum[w] = acc;
+      acc += x;
+    }
+    routed_total = acc;
+  }
+  __syncthreads();
+  // never write past the list, whatever offsets the caller passed (overlapping
+  // segments would otherwise multiply the tile count)
+  const int64_t ns = (shared_rows + BM - 1) / BM;
+  const int32_t R = (int32_t)min<int64_t>(routed_total, capacity - ns);
+  const int32_t start = v + wsum[wave] - n;
+  const int32_t cnt = max(0, min(n, R - start));
+  for (int j = 0; j < cnt; ++j) {
+    Tile t;
+    t.group = tid;
+    t.row_begin = o0 + j * BM;
+    t.row_end = min(o0 + (j + 1) * BM, o1);
+    t.first = start;
+    t.count = cnt;
+    t.pad[0] = t.pad[1] = t.pad[2] = 0;
+    tiles[start + j] = t;
+  }
+  for (int64_t j = tid; j < ns; j += 1024) {
+    Tile t;
+    t.group = E;
+    t.row_begin = (int32_t)(routed_rows + j * BM);
+    t.row_end = (int32_t)min<int64_t>(routed_rows + (j + 1) * BM, routed_rows + shared_rows);
+    t.first = R;
+    t.count = (int32_t)ns;
+    t.pad[0] = t.pad[1] = t.pad[2] = 0;
+    tiles[R + j] = t;
+  }
+  if (tid == 0) *ntiles = R + (int32_t)ns;
+}
+
+// Work item of this workgroup (see the ordering above).  False: nothing to do.
+__device__ __forceinline__ bool map_work(const FfnArgs& a, int NB, Tile& tile, int& nb) {
+  const int32_t nt = *a.ntiles;
+  const int64_t total = (int64_t)nt * NB;
+  const int64_t per = (total + 7) / 8;
+  const int64_t b = blockIdx.x;
+  if (b >= 8 * per) return false;
+  const int64_t L = (b & 7) * per + (b >> 3);
+  if (L >= total) return false;
+  const Tile t0 = a.tiles[L / NB];
+  const int64_t local = L - (int64_t)t0.first * NB;
+  const int j = (int)(local % t0.count);
+  nb = (int)(local / t0.count);
+  tile = a.tiles[t0.first + j];
+  return true;
+}
+
+// Row p of the grouped order -> its activation row.
+__device__ __forceinline__ const uint16_t* act_row(const FfnArgs& a, bool gateup, int64_t p) {
+  if (!gateup) return a.A + p * a.K;
+  int64_t tok;
+  if (p < a.routed_rows) {
+    int64_t sl = a.perm[p];
+    if (sl < 0 || sl >= a.routed_rows) sl = 0;
+    tok = sl / a.k;
+  } else {
+    tok = p - a.routed_rows;
+  }
+  return a.A + tok * a.K;
+}
+
+__device__ __forceinline__ void store_gateup(uint16_t* dst, f32x4_t g, f32x4_t u) {
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = silu_f32(g[i]) * u[i];
+  u32x2_t packed;
+  packed[0] = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  packed[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<u32x2_t*>(dst) = packed;
+}
+
+// Store four consecutive outputs (features nn .. nn+3) of grouped row p.  N is a
+// multiple of 64 for every bf16 output (d, I and the latent width are); only the fp32
+// output of the router GEMM (N = 3E) can have N % 4 != 0, and then the row is neither
+// 16-byte aligned nor a whole number of 4-feature groups, so it is stored one float at a
+// time and features >= N are dropped (they would land on the next row).
+template <int EPI>
+__device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x4_t v,
+                                       f32x4_t u) {
+  const int N = a.N;
+  if (EPI == kSwiGLU) {
+    store_gateup(a.C + p * N + nn, v, u);
+  } else if (EPI == kF32) {
+    float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
+    if ((N & 3) == 0) {
+      *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (nn + i < N) yrow[nn + i] = v[i];
+    }
+  } else {
+    if (EPI == kAddBF16) v += *reinterpret_cast<const f32x4_t*>(a.R + p * N + nn);
+    u32x2_t packed;
+    packed[0] = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    packed[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<u32x2_t*>(a.C + p * N + nn) = packed;
+  }
+}
+
+constexpr int kSkinnyBM = 16;
+constexpr int kStreamBM = 256;
+constexpr int kSkinnyNF = 2;       // skinny: 4 waves x 2 fragments = 128 features per block
+constexpr int kSkinnyKU = 8;       // skinny: k-steps (of 32) per batch of loads
+constexpr int kStreamBNGateUp = 128;  // stream: features of N per block (x2 weight matrices)
+constexpr int kStreamBNDown = 256;
+
+int64_t max_tiles_for(const FfnShape& sh, int BM) {
+  // sum_e ceil(c_e / BM) <= (T*k) / BM + E, plus the shared expert's ceil(T / BM)
+  return sh.T * sh.k / BM + sh.E + (sh.shared ? (sh.T + BM - 1) / BM : 0) + 1;
+}
+
+// Average rows per group (routed experts plus the shared expert) decides the kernel: a
+// few (decode) -> skinny kernel; many (prefill) -> 256-row stream kernel.
+bool use_wide(const FfnShape& sh) {
+  const int64_t rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
+  const int64_t groups = sh.E + (sh.shared ? 1 : 0);
+  return rows > (int64_t)16 * groups;
+}
+
+hipError_t tiles_launch(const FfnShape& sh, const int32_t* offsets, int BM, Tile* tiles,
+                        int32_t* ntiles, hipStream_t s) {
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, sh.E, sh.T * sh.k,
+                     sh.shared ? sh.T : (int64_t)0, BM, max_tiles_for(sh, BM), tiles, ntiles);
+  return hipGetLastError();
+}
+
+dim3 grid_for(const FfnShape& sh, int BM, int BN, int N) {
+  const int64_t NB = (N + BN - 1) / BN;
+  const int64_t total = max_tiles_for(sh, BM) * NB;
+  return dim3((unsigned)((total + 7) / 8 * 8));
+}
+
+}  // namespace
+}  // namespace moe

@@ -229,6 +229,32 @@ moe_status forward_impl(const moe_dims& d, const uint16_t* x, const float* w_rou
                                         d.d_model, d.top_k, s));
 }
 
+// ---------------------------------------------------------------------- FP8 weights
+moe_status check_fp8(const moe_dims& d, const moe_fp8_weights* w, bool gate_up, bool down) {
+  if (w == nullptr) return MOE_EINVAL;
+  const int B = moe::kFp8Block;
+  if (d.d_model % B != 0 || d.d_expert % B != 0) return MOE_EUNSUPPORTED;
+  if (d.d_model > moe::kFp8MaxK || d.d_expert > moe::kFp8MaxK) return MOE_EUNSUPPORTED;
+  if (gate_up) {
+    MOE_NEED(aligned(w->w1, 16) && aligned(w->w3, 16));
+    MOE_NEED(aligned(w->w1_scale, 4) && aligned(w->w3_scale, 4));
+    if (has_shared(d)) {
+      MOE_NEED(aligned(w->ws1, 16) && aligned(w->ws3, 16));
+      MOE_NEED(aligned(w->ws1_scale, 4) && aligned(w->ws3_scale, 4));
+    }
+  }
+  if (down) {
+    MOE_NEED(aligned(w->w2, 16) && aligned(w->w2_scale, 4));
+    if (has_shared(d)) MOE_NEED(aligned(w->ws2, 16) && aligned(w->ws2_scale, 4));
+  }
+  return MOE_OK;
+}
+
+moe::Fp8Weights fp8_of(const moe_fp8_weights& w) {
+  return moe::Fp8Weights{w.w1, w.w3, w.w2, w.w1_scale, w.w3_scale, w.w2_scale,
+                         w.ws1, w.ws3, w.ws2, w.ws1_scale, w.ws3_scale, w.ws2_scale};
+}
+
 moe_status check_forward_args(const moe_dims& d, const float* w_router, const float* bias,
                               const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
                               const uint16_t* ws1, const uint16_t* ws3, const uint16_t* ws2,
@@ -256,6 +282,74 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
   (void)hipGetLastError();
   return forward_impl(d, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, nullptr, out, ws,
                       (hipStream_t)stream);
+}
+
+moe_status moe_expert_gate_up_fp8(const moe_dims* dims, const uint16_t* x,
+                                  const int32_t* perm_rows, const int32_t* offsets,
+                                  const moe_fp8_weights* w, uint16_t* h, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  MOE_TRY(check_fp8(d, w, true, false));
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x, 16) && aligned(perm_rows, 4) && aligned(offsets, 4) && aligned(h, 16));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  (void)hipGetLastError();
+  const Layout L = layout(d);
+  return hip_status(moe::launch_gate_up_fp8(ffn_shape(d), x, perm_rows, offsets, fp8_of(*w), h,
+                                            at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                                            (hipStream_t)stream));
+}
+
+moe_status moe_expert_down_fp8(const moe_dims* dims, const uint16_t* h, const int32_t* offsets,
+                               const moe_fp8_weights* w, float* y_routed, float* y_shared,
+                               void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  MOE_TRY(check_fp8(d, w, false, true));
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(h, 16) && aligned(offsets, 4) && aligned(y_routed, 16));
+  if (has_shared(d)) MOE_NEED(aligned(y_shared, 16));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  (void)hipGetLastError();
+  const Layout L = layout(d);
+  return hip_status(moe::launch_down_fp8(ffn_shape(d), h, offsets, fp8_of(*w), y_routed,
+                                         has_shared(d) ? y_shared : nullptr,
+                                         at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                                         (hipStream_t)stream));
+}
+
+moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                           const float* bias, const moe_fp8_weights* w, uint16_t* out,
+                           void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  MOE_TRY(check_fp8(d, w, true, true));
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x, 16) && aligned(w_router, 16) && aligned(bias, 4) && aligned(out, 16));
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  (void)hipGetLastError();
+  const hipStream_t s = (hipStream_t)stream;
+  const Layout L = layout(d);
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* gw = at<float>(ws, L.w);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  float* y_routed = at<float>(ws, L.y);
+  float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
+  const moe::Fp8Weights fw = fp8_of(*w);
+  MOE_TRY(route_impl(d, x, w_router, bias, idx, gw, nullptr, ws, s));
+  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s));
+  MOE_TRY(hip_status(moe::launch_gate_up_fp8(ffn_shape(d), x, perm, offsets, fw, h,
+                                             at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                                             s)));
+  MOE_TRY(hip_status(moe::launch_down_fp8(ffn_shape(d), h, offsets, fw, y_routed, y_shared,
+                                          at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                                          s)));
+  return combine_impl(d, y_routed, inv, gw, y_shared, out, s);
 }
 
 moe_status moe_block_workspace_bytes(const moe_dims* dims, size_t* bytes) {

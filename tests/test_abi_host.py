@@ -155,3 +155,41 @@ def test_block_arguments_checked():
     z = _k2(0)
     assert L.moe_forward_block(ctypes.byref(z), None, None, ctypes.c_float(1e-6), None, None, None,
                                None, None, None, None, None, None, None, 0, None) == M.MOE_OK
+
+
+def test_fp8_arguments_checked():
+    L = M.lib()
+    P = _fake(0x100000)
+    ws_need = M.moe_workspace_bytes(_k2(128))
+    good = B.MoeFp8Weights(*([0x100000] * 12))
+    d = _k2(128)
+    args = lambda dims, w, n: (ctypes.byref(dims), P, P, P, w, P, P, n, None)  # noqa: E731
+    # null weight struct, misaligned codes, scales only need 4 bytes
+    assert L.moe_forward_fp8(ctypes.byref(d), P, P, P, None, P, P, ws_need, None) == M.MOE_EINVAL
+    bad = B.MoeFp8Weights(*([0x100000] * 12))
+    bad.w2 = 0x100004
+    assert L.moe_forward_fp8(*args(d, ctypes.byref(bad), ws_need)) == M.MOE_EINVAL
+    sc4 = B.MoeFp8Weights(*([0x100000] * 12))
+    sc4.w1_scale = 0x100004
+    assert L.moe_forward_fp8(*args(d, ctypes.byref(sc4), ws_need - 1)) == M.MOE_EWORKSPACE
+    # widths must be multiples of 128 (the scale blocks) and at most 16384
+    d192 = M.moe_dims(128, 7168, 384, 8, 192, 192)
+    assert L.moe_forward_fp8(*args(d192, ctypes.byref(good), ws_need)) == M.MOE_EUNSUPPORTED
+    d_big = M.moe_dims(16, 16512, 8, 2, 128, 128)
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_bytes(ctypes.byref(d_big), ctypes.byref(n)) == M.MOE_OK
+    assert L.moe_forward_fp8(ctypes.byref(d_big), P, P, P, ctypes.byref(good), P, P, n.value,
+                             None) == M.MOE_EUNSUPPORTED
+    # the shared expert's pointers are checked only when there is one
+    ns = M.moe_dims(128, 7168, 384, 8, 2048, 0)
+    noshared = B.MoeFp8Weights(*([0x100000] * 6 + [0] * 6))
+    assert L.moe_expert_gate_up_fp8(ctypes.byref(ns), P, P, P, ctypes.byref(noshared), P, P, 0,
+                                    None) == M.MOE_EWORKSPACE
+    assert L.moe_expert_gate_up_fp8(ctypes.byref(d), P, P, P, ctypes.byref(noshared), P, P,
+                                    ws_need, None) == M.MOE_EINVAL
+    # T = 0: nothing to do, nothing dereferenced
+    z = _k2(0)
+    assert L.moe_forward_fp8(ctypes.byref(z), None, None, None, ctypes.byref(good), None, None, 0,
+                             None) == M.MOE_OK
+    assert L.moe_expert_down_fp8(ctypes.byref(z), None, None, ctypes.byref(good), None, None,
+                                 None, 0, None) == M.MOE_OK
