@@ -81,7 +81,17 @@ struct Tile {
   int32_t pad[3];
 };
 
-// Router: w_split [3E, d] bf16 and z_part [T, 3E] fp32 are workspace; logits may be null.
+// Router: w_split [3E, d] bf16 and z_part (router_zpart_floats) fp32 are workspace;
+// logits may be null.  Up to kRouterSmallT tokens take the K-sliced small kernel, whose
+// partial logits need kRouterKSplit times the room.
+constexpr int64_t kRouterSmallT = 512;
+#ifndef MOE_ROUTER_KSPLIT
+#define MOE_ROUTER_KSPLIT 8
+#endif
+constexpr int kRouterKSplit = MOE_ROUTER_KSPLIT;
+inline int64_t router_zpart_floats(int64_t T, int E) {
+  return T * 3 * E * (T <= kRouterSmallT ? kRouterKSplit : 1);
+}
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
                          int E, int k, float alpha, uint16_t* w_split, float* z_part,
                          Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,

@@ -182,8 +182,14 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
 
 constexpr int kSkinnyBM = 16;
 constexpr int kStreamBM = 256;
-constexpr int kSkinnyNF = 2;       // skinny: 4 waves x 2 fragments = 128 features per block
-constexpr int kSkinnyKU = 8;       // skinny: k-steps (of 32) per batch of loads
+#ifndef MOE_SKINNY_NF
+#define MOE_SKINNY_NF 2
+#endif
+#ifndef MOE_SKINNY_KU
+#define MOE_SKINNY_KU 8
+#endif
+constexpr int kSkinnyNF = MOE_SKINNY_NF;  // skinny: 4 waves x NF fragments = 64 NF features per block
+constexpr int kSkinnyKU = MOE_SKINNY_KU;  // skinny: k-steps (of 32) per batch of loads
 constexpr int kStreamBNGateUp = 128;  // stream: features of N per block (x2 weight matrices)
 constexpr int kStreamBNDown = 256;
 

@@ -8,6 +8,8 @@
 // significant bits), so x W_r^T = x hi^T + x mid^T + x lo^T.  x is bf16, so every
 // product is exact in fp32; the three partial logits are accumulated in fp32 by the
 // grouped-GEMM kernels (one group, 3E outputs) and added in fp64 by the selection kernel.
+// For a few tokens (decode) one kernel does the split in registers and cuts K into
+// slices instead (router_small_kernel below).
 // (The split follows the bf16x3 scheme of Henry, Tang and Heinecke, "Leveraging the
 // bfloat16 artificial intelligence datatype for higher-precision computations", 2019.)
 #include <math.h>
@@ -33,6 +35,112 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
   }
 }
 
+// ---------------------------------------------------------------- logits, few tokens
+// For a decode-sized batch the logits GEMM is small (T x E outputs) and its cost is
+// reading W_r.  This kernel reads the fp32 router weights once, splits each value into
+// its hi, mid and lo bf16 parts in registers (no split pass, no bf16 copy of W_r) and
+// accumulates the three partial logits in three fp32 accumulators.  K is cut into
+// kRouterKSplit slices (grid z) so that the launch fills the chip; every (slice, part)
+// pair writes its own partial, and the selection kernel adds the 3 * kRouterKSplit
+// partials of a logit in fp64, in a fixed order.
+// Block: 4 waves; wave w owns experts n0 + 16 w .. + 15 (one MFMA fragment), the block
+// 16 rows (tokens).  Lane (r, q): expert n0 + 16 w + r, token t0 + r, k 8q .. 8q + 7 of
+// each 32-wide step; weights are the MFMA's A operand, tokens its B operand.
+#ifndef MOE_ROUTER_KU
+#define MOE_ROUTER_KU 4
+#endif
+constexpr int kRouterKU = MOE_ROUTER_KU;   // k-steps of loads issued before their MFMAs
+
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f32_to_bf16(w);
+  const float r1 = w - bf16_to_f32(hi);
+  mid = f32_to_bf16(r1);
+  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+}
+
+__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ w_r,
+                                                           int64_t T, int d, int E,
+                                                           float* __restrict__ z_part) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int n0 = blockIdx.y * 64 + wave * 16;
+  const int kz = blockIdx.z, nks = d / 32;
+  const int ks0 = (int)((int64_t)nks * kz / kRouterKSplit);
+  const int ks1 = (int)((int64_t)nks * (kz + 1) / kRouterKSplit);
+  int64_t t = t0 + r;
+  if (t > T - 1) t = T - 1;
+  int e = n0 + r;
+  if (e > E - 1) e = E - 1;
+  const float* wrow = w_r + (int64_t)e * d + q * 8;
+  const uint16_t* xrow = x + t * d + q * 8;
+  f32x4_t acc[3] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f},
+                    f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  auto step = [&](const u32x4_t (&wv)[2], u32x4_t xv) {
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      split3(__uint_as_float(wv[0][i]), h[i], m[i], l[i]);
+      split3(__uint_as_float(wv[1][i]), h[4 + i], m[4 + i], l[4 + i]);
+    }
+    const u32x4_t H = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                       h[6] | (h[7] << 16)};
+    const u32x4_t Mv = {m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16),
+                        m[6] | (m[7] << 16)};
+    const u32x4_t Lv = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
+                        l[6] | (l[7] << 16)};
+    acc[0] = mfma16x16x32(H, xv, acc[0]);
+    acc[1] = mfma16x16x32(Mv, xv, acc[1]);
+    acc[2] = mfma16x16x32(Lv, xv, acc[2]);
+  };
+  int ks = ks0;
+  for (; ks + kRouterKU <= ks1; ks += kRouterKU) {
+    u32x4_t wv[kRouterKU][2], xv[kRouterKU];
+#pragma unroll
+    for (int u = 0; u < kRouterKU; ++u) {
+      const float* wp = wrow + (ks + u) * 32;
+      wv[u][0] = *reinterpret_cast<const u32x4_t*>(wp);
+      wv[u][1] = *reinterpret_cast<const u32x4_t*>(wp + 4);
+      xv[u] = load16(xrow + (ks + u) * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kRouterKU; ++u) step(wv[u], xv[u]);
+  }
+  for (; ks < ks1; ++ks) {
+    const float* wp = wrow + ks * 32;
+    const u32x4_t wv[2] = {*reinterpret_cast<const u32x4_t*>(wp),
+                           *reinterpret_cast<const u32x4_t*>(wp + 4)};
+    step(wv, load16(xrow + ks * 32));
+  }
+  // lane holds experts n0 + 4q .. + 3 of token t0 + r; partial (slice kz, part p) of a
+  // token's logits sits at z_part[t][(3 kz + p) E + e]
+  if (t0 + r >= T) return;
+  float* zrow = z_part + (t0 + r) * (int64_t)(3 * kRouterKSplit) * E;
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = n0 + 4 * q + i;
+      if (ee < E) zrow[(3 * kz + p) * (int64_t)E + ee] = acc[p][i];
+    }
+}
+
+// Sum of the np partial logits of every (token, expert) in fp64, in slice order, rounded
+// once to fp32: the selection then reads one value per logit.  z_part rows are [np][E];
+// the sum goes to part 0 of the row.
+__global__ __launch_bounds__(256) void router_reduce_kernel(float* __restrict__ z_part,
+                                                            int64_t T, int E, int np) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * E) return;
+  const int64_t t = i / E;
+  const int e = (int)(i - t * E);
+  float* row = z_part + t * (int64_t)np * E;
+  double z = 0.0;
+  for (int p = 0; p < np; ++p) z += (double)row[(int64_t)p * E + e];
+  row[e] = (float)z;
+}
+
 // ---------------------------------------------------------------- top-k + gates
 // One wave per token.  z = hi + mid + lo partial logits summed in fp64, rounded to fp32.
 // Lane l holds experts l, l + 64, ...; k rounds of a wave-wide argmax over (score,
@@ -40,6 +148,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // gates use the sigmoid without the bias.
 template <int EPL>
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ z_part,
+                                                            int np, int row_parts,
                                                             const float* __restrict__ bias,
                                                             int64_t T, int E, int k, float alpha,
                                                             float* __restrict__ logits,
@@ -48,14 +157,16 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* zp = z_part + t * 3 * E;
+  const float* zp = z_part + t * (int64_t)row_parts * E;
 
   float score[EPL], sig[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      const float z = (float)((double)zp[e] + (double)zp[E + e] + (double)zp[2 * E + e]);
+      double zd = 0.0;
+      for (int p = 0; p < np; ++p) zd += (double)zp[p * E + e];
+      const float z = (float)zd;
       if (logits != nullptr) logits[t * E + e] = z;
       const float s = 1.0f / (1.0f + expf(-z));
       float v = s + bias[e];
@@ -123,11 +234,12 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
 }
 
 template <int EPL>
-void select_launch(const float* z_part, const float* bias, int64_t T, int E, int k, float alpha,
-                   float* logits, int32_t* idx, float* w, hipStream_t s) {
+void select_launch(const float* z_part, int np, int row_parts, const float* bias, int64_t T,
+                   int E, int k, float alpha, float* logits, int32_t* idx, float* w,
+                   hipStream_t s) {
   const unsigned grid = (unsigned)((T + 3) / 4);
-  hipLaunchKernelGGL(router_select_kernel<EPL>, dim3(grid), dim3(256), 0, s, z_part, bias, T, E,
-                     k, alpha, logits, idx, w);
+  hipLaunchKernelGGL(router_select_kernel<EPL>, dim3(grid), dim3(256), 0, s, z_part, np,
+                     row_parts, bias, T, E, k, alpha, logits, idx, w);
 }
 
 }  // namespace
@@ -137,28 +249,49 @@ hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias,
                          Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,
                          float* topk_w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const int64_t n = (int64_t)E * d;
-  const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-  hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w_r, n,
-                     w_split);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  err = launch_dense(x, T, d, w_split, 3 * E, DenseOut::kF32, z_part, nullptr, nullptr, tiles,
-                     ntiles, s);
-  if (err != hipSuccess) return err;
+  hipError_t err;
+  int np, row_parts;
+  if (T <= kRouterSmallT) {
+    const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 63) / 64), kRouterKSplit);
+    hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, x, w_r, T, d, E, z_part);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // every thread reads its logit's partials before writing part 0 of the same logit,
+    // and no other thread touches that logit: the in-place sum is race-free
+    const int64_t n = T * E;
+    hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       z_part, T, E, 3 * kRouterKSplit);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // the selection reads rows of 3 * kRouterKSplit parts, of which part 0 is the sum
+    np = 1;
+    row_parts = 3 * kRouterKSplit;
+  } else {
+    const int64_t n = (int64_t)E * d;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w_r, n,
+                       w_split);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = launch_dense(x, T, d, w_split, 3 * E, DenseOut::kF32, z_part, nullptr, nullptr, tiles,
+                       ntiles, s);
+    if (err != hipSuccess) return err;
+    np = 3;
+    row_parts = 3;
+  }
   const int epl = (E + 63) / 64;
   if (epl <= 1)
-    select_launch<1>(z_part, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<1>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else if (epl <= 2)
-    select_launch<2>(z_part, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<2>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else if (epl <= 4)
-    select_launch<4>(z_part, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<4>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else if (epl <= 6)
-    select_launch<6>(z_part, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<6>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else if (epl <= 8)
-    select_launch<8>(z_part, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<8>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else
-    select_launch<16>(z_part, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<16>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   return hipGetLastError();
 }
 
