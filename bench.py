@@ -25,7 +25,7 @@ if ROOT not in sys.path:
 
 METRIC = "K2 MoE-layer tokens/s (128 & 8192 tok, bf16); % of HBM / MFMA peak"
 # the gate/up kernel each workload runs (decode: a few rows per expert; prefill: many)
-GATEUP_KERNEL = {"k2_decode": "ffn_skinny_kernel<2, 8, 0>", "k2_prefill": "ffn_stream_kernel<0>"}
+GATEUP_KERNEL = {"k2_decode": "ffn_skinny_kernel<2, 8, 0>", "k2_prefill": "ffn_lds_kernel<0>"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 

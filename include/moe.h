@@ -33,7 +33,7 @@
  *       MOE_EINVAL       null / misaligned (16 B) pointer, impossible dims
  *       MOE_EUNSUPPORTED dims this build does not handle (d, I not multiples of 64,
  *                        top_k > 8, E > 1024, Is not 0 or I, x or one weight matrix
- *                        of 4 GiB or more, T above 2^23)
+ *                        of 2 GiB or more, T above 2^23)
  *       MOE_EWORKSPACE   ws_bytes smaller than moe_workspace_bytes()
  *       MOE_EHIP         a kernel launch failed (device faults surface at the caller's
  *                        next synchronisation, as usual for asynchronous work)

@@ -11,6 +11,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kWave = 64;
 constexpr int kMaxTopK = 8;
@@ -51,6 +53,21 @@ __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t vo
 // (l & 15).  Any k assignment works as long as A and B use the same one.
 __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// C(32x32, fp32) += A(32x16) * B(16x32), bf16 operands.
+// Lane l supplies row (l & 31) of A and column (l & 31) of B, each with the 8 consecutive
+// k values 8*(l >> 5) .. +7; it receives column (l & 31) of C, rows
+// 8*(j >> 2) + 4*(l >> 5) + (j & 3) in register j (four runs of 4 consecutive rows).
+__device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// 16 bytes per lane from a raw buffer straight into LDS: lane l's bytes land at
+// lds + 16 l (the wave writes 1 KiB contiguous); `lds` must be wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }

@@ -16,10 +16,10 @@
 // each XCD walks one contiguous run of items and an expert's weight and activation
 // reuse stays inside one L2.
 //
-// Two kernels, both streaming weights from HBM straight into MFMA registers: "skinny"
-// for row tiles of <= 16 rows (decode: a few tokens per expert), activations from L2;
-// "stream" for 256-row tiles (prefill), activations staged in LDS and shared by the
-// workgroup's waves.
+// Two kernels: "skinny" for row tiles of <= 16 rows (decode: a few tokens per expert),
+// weights streamed from HBM straight into MFMA registers and activations from L2; and an
+// LDS-tiled kernel for 256-row tiles (prefill, and the dense projections), both operands
+// staged in LDS and shared by the workgroup's four waves.
 #include "grouped.h"
 
 namespace moe {
@@ -117,252 +117,279 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
   }
 }
 
-// ------------------------------------------------------------- stream GEMM
-// 256-row tiles (prefill: an expert's rows usually fit one tile, so its weights leave HBM
-// once).  Eight waves, each owning all of the tile's rows (16 row fragments) x 32 outputs
-// (gate/up: 16 features of W1 and the same 16 of W3; down: 32 features), so no two waves
-// load the same weights.  Weights stream from HBM straight into MFMA registers, the same
-// operand layout as the skinny kernel, through a ring of six k-step register sets: five
-// k-steps (10 KiB per wave, 80 KiB per CU) are in flight while one is multiplied.  The
-// tile's activation rows are staged in LDS in 64-wide k-chunks, double-buffered, with one
-// LDS-only barrier per chunk (it does not drain the weight loads in flight).  Within a
-// buffer the 16-byte pieces are stored k-chunk-major with the row index XOR-swizzled by
-// the chunk (slot = c * 256 + (m ^ 2c)), so the 16 lanes of an MFMA operand read (16 rows,
-// one chunk) and of a chunk write (2 rows x 8 chunks) touch 16 distinct bank groups.  Activation fragments are
-// read from LDS one at a time, one fragment ahead of the two MFMAs that use it.
-// The main loop is straight-line code: it is instantiated for 4, 8, 12 or 16 live row
-// fragments (the tile's rows rounded up to 64: rows past the end cost at most three
-// fragments of MFMAs; finer steps measured slower, the extra copies of the loop crowd the
-// instruction cache), prefetch indices are clamped instead of guarded, and one ring
-// period (RING / 2 chunks) is unrolled per iteration so the register ring is indexed
-// statically.  Branches inside the loop would make the compiler's wait-count analysis
-// conservative at every join and wait for the prefetched loads too.
-// Tuning constants of the stream kernel, measured on MI355X at the K2 prefill shape
-// (gate/up, ms): 64-row granules 6.33 vs 128-row 6.95 vs none 6.60; read groups of 1
-// fragment 6.33, 2: 6.34, 4: 6.88; without the scheduling barrier 8.40; ring depth 6:
-// 6.25, 8: 6.87, 10: 7.47 (spills); weight requests batched two k-steps at a time 6.38.
-#ifndef MOE_STREAM_NL_STEP
-#define MOE_STREAM_NL_STEP 4      // live row fragments are rounded up to this multiple
-#endif
-#ifndef MOE_STREAM_GS
-#define MOE_STREAM_GS 1           // activation fragments read from LDS per group
-#endif
-#ifndef MOE_STREAM_SCHED_BARRIER
-#define MOE_STREAM_SCHED_BARRIER 1  // keep reads one group ahead of their MFMAs
-#endif
-#ifndef MOE_STREAM_RING
-#define MOE_STREAM_RING 6         // k-steps of weights held in registers per wave (even)
-#endif
-#ifndef MOE_STREAM_BATCH
-#define MOE_STREAM_BATCH 1        // k-steps of weights requested together (1 or 2)
-#endif
+// ------------------------------------------------------------- LDS-tiled GEMM
+// 256-row tiles x 256 outputs per workgroup (gate/up: 128 features of W1 and the same 128
+// of W3; otherwise 256 features).  Four waves, one per SIMD, each owning a 128-row x
+// 128-output quarter as sixteen 32 x 32 fp32 accumulator tiles (256 accumulator
+// registers), so every operand fragment read from LDS feeds four MFMAs; the 32x32x16
+// MFMA also reads half the operand bytes per flop of the 16x16x32 one.  On this part
+// the prefill GEMMs run at the power limit, and both choices cut the energy per flop.
+//
+// K goes in chunks of 64.  Per chunk a workgroup moves 32 KiB of weights and 32 KiB of
+// activations (gate/up: rows of x gathered through perm), 8 rows x 128 contiguous bytes
+// per wave-wide 16-byte-per-lane load:
+//   - weights go from HBM straight into LDS (buffer loads that write LDS), three chunk
+//     buffers, requested two chunks ahead;
+//   - activations (mostly L2 hits) go through registers into two LDS chunk buffers,
+//     requested one chunk ahead.
+// 160 KiB of LDS in all.  Loads retire in order, so once a wave has its activation
+// registers for chunk c + 1 its weight transfers for chunk c + 1 have landed too.
+//
+// LDS layout of a chunk operand (256 rows x 8 pieces of 16 bytes): the 1 KiB unit u holds
+// rows 8u .. 8u+7; piece p of row m sits in slot 8 (m & 7) + (p ^ sigma(m)) of its unit,
+// sigma(m) = (m & 7) ^ ((m >> 3) & 1).  A load lane fetches whichever piece belongs to its
+// slot, so the global reads stay 128 contiguous bytes per row, and an MFMA operand read
+// (16 consecutive rows, one piece) touches 16 distinct 16-byte bank groups.
+constexpr int kLdsChunkK = 64;
 
-struct StreamCtx {
-  __amdgpu_buffer_rsrc_t w1;   // matrix of weight fragment 0 (and 1 unless gate/up)
-  __amdgpu_buffer_rsrc_t w3;   // gate/up: matrix of weight fragment 1
+struct LdsCtx {
   __amdgpu_buffer_rsrc_t act;  // activation rows (x, or the tile's rows of h)
-  uint32_t woff[2];            // byte offset of the lane's row and k lane-group, per fragment
-  uint32_t aoff[4];            // byte offset of each activation piece (row start + chunk)
-  int adst;                    // LDS offset (elements) of the first activation piece; the
-                               // XOR touches bits 1..3 of the row only, so piece i (row
-                               // + 64 i) sits 64 i slots further
-  int nks, nc;                 // k-steps (32) and chunks (64)
+  __amdgpu_buffer_rsrc_t wgt;  // this wave's weight matrix (gate/up: W1 for waves 0-1,
+                               // W3 for waves 2-3)
+  uint32_t aoff[8];            // per-lane byte offset of the wave's activation units
+  uint32_t woff[2];            // per-lane byte offset of the wave's even / odd weight
+                               // units, less the unit stride
+  uint32_t wstride;            // bytes between the wave's consecutive weight units (8 rows)
+  uint32_t aoob, woob;         // a wave-uniform offset past the end of act / wgt: a load
+                               // there returns zeros and moves no data
+  int wrd[4];                  // per-lane slot (16 B units) of sub-step kk's piece in the
+  int ard[4];                  // wave's first weight / activation row fragment
+  int nc;                      // chunks
 };
 
-template <int EPI, int NL>
-__device__ __forceinline__ void stream_loop(const StreamCtx& c_, uint16_t* lds,
-                                            f32x4_t (&acc)[16][2]) {
-  constexpr bool GATEUP = EPI == kSwiGLU;
-  constexpr int BM = 256, BK = 64, NW = 2, NA = 4;
-  constexpr int D = MOE_STREAM_RING, P = MOE_STREAM_BATCH;
-  static_assert(D % 2 == 0 && D >= 4 && (P == 1 || P == 2), "weight ring shape");
-  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
-  const int nks = c_.nks, nc = c_.nc;
-  u32x4_t W[D][NW], AR[NA];
-
-  auto load_w = [&](u32x4_t* S, int ks) {
-    const uint32_t kb = (uint32_t)(ks < nks ? ks : nks - 1) * 64;  // past the end: re-read
-    S[0] = bload16(c_.w1, c_.woff[0], kb);
-    S[1] = bload16(GATEUP ? c_.w3 : c_.w1, c_.woff[1], kb);
-  };
-  auto load_a = [&](int c) {
-    const uint32_t cb = (uint32_t)(c < nc ? c : nc - 1) * (BK * 2);
+// The wave's 8 weight transfers of chunk c (units 8 wave .. 8 wave + 7); past the last
+// chunk they read nothing.
+__device__ __forceinline__ void lds_fetch_w(const LdsCtx& x, u32x4_t* wgt, int wave, int c) {
+  const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.woob;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) AR[i] = bload16(c_.act, c_.aoff[i], cb);
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-      *reinterpret_cast<u32x4_t*>(lds + buf * BM * BK + c_.adst + i * 64 * 8) = AR[i];
-  };
-  // slot of (row m, 8-element k-chunk c) = c * BM + (m ^ 2c): a lane's fragment read is
-  // row 16 i + r of chunk c = 4 kk + q, i.e. slot c * BM + 16 i + (r ^ 2c)
-  auto mma_step = [&](int buf, int kk, const u32x4_t* S) {
-    constexpr int GS = MOE_STREAM_GS;         // fragments per read group
-    const int c = 4 * kk + q;
-    const uint16_t* As = lds + buf * BM * BK + (c * BM + (r ^ (2 * c))) * 8;
-    u32x4_t G0[GS], G1[GS];
-#pragma unroll
-    for (int j = 0; j < GS; ++j) G0[j] = *reinterpret_cast<const u32x4_t*>(As + 16 * j * 8);
-#pragma unroll
-    for (int g = 0; g < NL / GS; ++g) {
-      u32x4_t* cur = (g & 1) ? G1 : G0;
-      u32x4_t* nxt = (g & 1) ? G0 : G1;
-      if (g + 1 < NL / GS) {
-#pragma unroll
-        for (int j = 0; j < GS; ++j)
-          nxt[j] = *reinterpret_cast<const u32x4_t*>(As + 16 * (GS * (g + 1) + j) * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < GS; ++j) {
-        acc[GS * g + j][0] = mfma16x16x32(S[0], cur[j], acc[GS * g + j][0]);
-        acc[GS * g + j][1] = mfma16x16x32(S[1], cur[j], acc[GS * g + j][1]);
-      }
-      if (MOE_STREAM_SCHED_BARRIER) __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // chunk c+1's activations (in AR) go to the other LDS buffer; AR then loads chunk c+2
-  auto next_chunk = [&](int c) {
-    store_a((c + 1) & 1);
-    load_a(c + 2);
-    lds_barrier();
-  };
-  // Chunk j of a ring period (k-steps s = 2c + 2j and s + 1, ring slots t = 2j, t + 1).
-  // P = 1: each k-step refills the slot freed just before it, D - 1 k-steps in flight.
-  // P = 2: both refills of the chunk are issued together at its start (128 contiguous
-  // bytes of every weight row at once), D - 2 k-steps in flight.
-  auto chunk = [&](int c, int j) {
-    const int t = 2 * j, s = 2 * c + t;
-    if (P == 1) {
-      load_w(W[(t + D - 1) % D], s + D - 1);
-      mma_step((c + j) & 1, 0, W[t]);
-      load_w(W[t], s + D);
-      mma_step((c + j) & 1, 1, W[t + 1]);
-    } else {
-      load_w(W[(t + D - 2) % D], s + D - 2);
-      load_w(W[(t + D - 1) % D], s + D - 1);
-      mma_step((c + j) & 1, 0, W[t]);
-      mma_step((c + j) & 1, 1, W[t + 1]);
-    }
-    next_chunk(c + j);
-  };
-
-  load_a(0);
-#pragma unroll
-  for (int t = 0; t < D - P; ++t) load_w(W[t], t);
-  store_a(0);
-  load_a(1);
-  lds_barrier();
-  int c = 0;
-  // at the top of an iteration W[t] holds k-step 2c + t for t < D - P
-  for (; c + D / 2 <= nc; c += D / 2) {
-#pragma unroll
-    for (int j = 0; j < D / 2; ++j) chunk(c, j);
-  }
-#pragma unroll
-  for (int j = 0; j < D / 2 - 1; ++j)
-    if (c + j < nc) chunk(c, j);
+  for (int j = 0; j < 8; ++j)
+    dma16(x.wgt, wgt + (wave * 8 + j) * 64, x.woff[j & 1], soff + (uint32_t)j * x.wstride);
 }
 
-// stream_loop instantiated for the smallest multiple of STEP fragments >= nfrag
-template <int EPI, int STEP, int NL = STEP>
-__device__ __forceinline__ void stream_dispatch(int nfrag, const StreamCtx& ctx, uint16_t* lds,
-                                                f32x4_t (&acc)[16][2]) {
-  if constexpr (NL >= 16) {
-    stream_loop<EPI, 16>(ctx, lds, acc);
-  } else {
-    if (nfrag <= NL)
-      stream_loop<EPI, NL>(ctx, lds, acc);
-    else
-      stream_dispatch<EPI, STEP, NL + STEP>(nfrag, ctx, lds, acc);
+__device__ __forceinline__ void lds_load_a(const LdsCtx& x, u32x4_t (&ar)[8], int c) {
+  const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.aoob;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ar[j] = bload16(x.act, x.aoff[j], soff);
+}
+
+__device__ __forceinline__ void lds_store_a(u32x4_t* act, const u32x4_t (&ar)[8], int wave) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) act[(wave * 8 + j) * 64 + lane] = ar[j];
+}
+
+// Every wave has stored its activations and finished reading the buffers of the previous
+// chunk, and its weight transfers of this chunk have landed (only the 16 loads requested
+// during the previous chunk may still be in flight).
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One chunk (4 sub-steps of 16 k) on NF of the wave's 4 row fragments.  Sub-step kk reads
+// weight fragment o at slot wrd[kk] + 8 wfrag_row(o) and row fragment t (tile rows
+// 64 t + 32 wm ..) at slot ard[kk] + 512 t (the wave-dependent parts are in wrd/ard, so
+// the fragment offsets are immediates).  The operands of sub-step kk + 1 are read while the MFMAs of sub-step kk
+// run.
+template <bool GATEUP>
+__device__ __forceinline__ constexpr int wfrag_row(int o) {
+  // gate/up: o = 0, 1 are W1 rows 32 o of the wave's 64 features, o = 2, 3 the same
+  // features of W3 (128 rows further); otherwise 32 o
+  return GATEUP ? 128 * (o >> 1) + 32 * (o & 1) : 32 * o;
+}
+
+template <bool GATEUP, int NF>
+__device__ __forceinline__ void lds_mma(const LdsCtx& x, const u32x4_t* act, const u32x4_t* wgt,
+                                        f32x16_t (&acc)[NF][4]) {
+  u32x4_t wv[2][4], av[2][NF];
+  auto read = [&](int kk, int b) {
+#pragma unroll
+    for (int o = 0; o < 4; ++o) wv[b][o] = wgt[x.wrd[kk] + 8 * wfrag_row<GATEUP>(o)];
+#pragma unroll
+    for (int t = 0; t < NF; ++t) av[b][t] = act[x.ard[kk] + 512 * t];
+  };
+  read(0, 0);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk < 3) read(kk + 1, (kk + 1) & 1);
+    // keep the next sub-step's reads ahead of this sub-step's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NF; ++t)
+#pragma unroll
+      for (int o = 0; o < 4; ++o) acc[t][o] = mfma32x32x16(wv[kk & 1][o], av[kk & 1][t], acc[t][o]);
+  }
+}
+
+struct LdsBufs {
+  u32x4_t* A;     // two activation chunk buffers, 2048 slots each (one LDS array, indexed
+                  // by chunk parity: a pointer picked from a table would lose its address
+                  // space)
+  u32x4_t* W0;    // weight chunk buffers (named separately so that the compiler can tell
+  u32x4_t* W1;    // which transfers a read depends on)
+  u32x4_t* W2;
+};
+
+// Chunk c with its weights in buffer WB (WB == c % 3): wait, request weights c + 2 and
+// activations c + 2 (registers), multiply, then store activations c + 1 for the next chunk.
+template <bool GATEUP, int NF>
+__device__ __forceinline__ void lds_step(const LdsCtx& x, const LdsBufs& b, u32x4_t* wcur,
+                                         u32x4_t* wnext2, u32x4_t (&ar)[8], int wave, int c,
+                                         f32x16_t (&acc)[NF > 0 ? NF : 1][4]) {
+  lds_sync();
+  lds_fetch_w(x, wnext2, wave, c + 2);
+  if constexpr (NF > 0) lds_mma<GATEUP, NF>(x, b.A + (c & 1) * 2048, wcur, acc);
+  lds_store_a(b.A + ((c + 1) & 1) * 2048, ar, wave);
+  lds_load_a(x, ar, c + 2);
+}
+
+// A tile for a wave with NF live row fragments (NF = 0: the wave only moves data): the K
+// loop, then the epilogue.  Every wave runs the same loads and barriers whatever its NF.
+template <int EPI, int NF>
+__device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, const LdsBufs& b,
+                                         int wave, int arow, const Tile& tile, int nbase) {
+  constexpr bool GATEUP = EPI == kSwiGLU;
+  constexpr int NA = NF > 0 ? NF : 1;
+  f32x16_t acc[NA][4];
+#pragma unroll
+  for (int t = 0; t < NA; ++t)
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][o][e] = 0.f;
+
+  const int nc = x.nc;
+  u32x4_t ar[8];
+  lds_fetch_w(x, b.W0, wave, 0);
+  lds_fetch_w(x, b.W1, wave, 1);
+  lds_load_a(x, ar, 0);
+  lds_store_a(b.A, ar, wave);
+  lds_load_a(x, ar, 1);
+  int c = 0;
+  for (; c + 3 <= nc; c += 3) {
+    lds_step<GATEUP, NF>(x, b, b.W0, b.W2, ar, wave, c, acc);
+    lds_step<GATEUP, NF>(x, b, b.W1, b.W0, ar, wave, c + 1, acc);
+    lds_step<GATEUP, NF>(x, b, b.W2, b.W1, ar, wave, c + 2, acc);
+  }
+  if (c < nc) lds_step<GATEUP, NF>(x, b, b.W0, b.W2, ar, wave, c, acc);
+  if (c + 1 < nc) lds_step<GATEUP, NF>(x, b, b.W1, b.W0, ar, wave, c + 1, acc);
+  // the requests past the last chunk read nothing; let them retire before the stores
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (NF == 0) return;
+
+  // epilogue: acc[t][o] register j of lane l = tile row arow + 64 t + (l & 31), output
+  // 8 (j >> 2) + 4 (l >> 5) + (j & 3) of weight fragment o (first output nbase + ...)
+  const int lane = threadIdx.x & 63, fl = 4 * (lane >> 5);
+  const int nrows = tile.row_end - tile.row_begin;
+#pragma unroll
+  for (int t = 0; t < NA; ++t) {
+    const int m = arow + 64 * t + (lane & 31);
+    if (m >= nrows) continue;
+    const int64_t p = tile.row_begin + m;
+#pragma unroll
+    for (int oo = 0; oo < (GATEUP ? 2 : 4); ++oo)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nn = nbase + 32 * oo + 8 * q + fl;
+        if (nn >= a.N) continue;
+        const f32x16_t& g = acc[t][oo];
+        const f32x16_t& u = acc[t][GATEUP ? oo + 2 : oo];
+        const f32x4_t gv = {g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
+        const f32x4_t uv = {u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]};
+        store4<EPI>(a, p, nn, gv, uv);
+      }
   }
 }
 
 template <int EPI>
-__global__ __launch_bounds__(512, 1) void ffn_stream_kernel(const FfnArgs a) {
+__global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   constexpr bool GATEUP = EPI == kSwiGLU;
-  constexpr int BM = 256, BK = 64;
-  constexpr int FM = BM / 16;                 // row fragments (every wave has all rows)
-  constexpr int NW = 2;                       // weight fragments per wave per k-step
-  constexpr int FEAT_WAVE = GATEUP ? 16 : 32; // features of N per wave
-  constexpr int FEAT = 8 * FEAT_WAVE;         // features of N per workgroup
-  constexpr int NT = 512;                     // threads
-  constexpr int NA = BM * BK / 8 / NT;        // 16-byte activation pieces per thread (4)
-  static_assert(NA == 4 && FM == 16, "stream tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * BK];
+  constexpr int BM = 256;
+  constexpr int FEAT = GATEUP ? 128 : 256;  // features of N per workgroup
+  __shared__ __attribute__((aligned(1024))) u32x4_t Ab[2 * BM * 8];
+  __shared__ __attribute__((aligned(1024))) u32x4_t W0[BM * 8];
+  __shared__ __attribute__((aligned(1024))) u32x4_t W1[BM * 8];
+  __shared__ __attribute__((aligned(1024))) u32x4_t W2[BM * 8];
 
   Tile tile;
   int nb;
   if (!map_work(a, (a.N + FEAT - 1) / FEAT, tile, nb)) return;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = lane & 15, q = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   const int K = a.K, N = a.N;
   const int nrows = tile.row_end - tile.row_begin;
-  const int n_wave = nb * FEAT + wave * FEAT_WAVE;
+  const int f0 = nb * FEAT;
 
   const bool is_shared = tile.group >= a.E;
   const int64_t wofs = (int64_t)tile.group * N * K;
-  const uint16_t* W1 = is_shared ? a.S1 : a.B1 + wofs;
-  const uint16_t* W3 = GATEUP ? (is_shared ? a.S3 : a.B3 + wofs) : nullptr;
+  const uint16_t* Wa = is_shared ? a.S1 : a.B1 + wofs;
+  const uint16_t* Wb = GATEUP ? (is_shared ? a.S3 : a.B3 + wofs) : Wa;
 
-  StreamCtx ctx;
-  // one weight matrix is N*K*2 < 2^32 bytes (checked on the host)
+  LdsCtx x;
+  // one weight matrix is N*K*2 < 2^32 bytes, and so is x (checked on the host)
   const uint32_t wbytes = (uint32_t)N * (uint32_t)K * 2u;
-  ctx.w1 = buffer_rsrc(W1, wbytes);
-  ctx.w3 = buffer_rsrc(GATEUP ? W3 : W1, wbytes);
-  // gate/up gathers rows of x (T*K*2 < 2^32 bytes, checked on the host); down reads the
-  // tile's own contiguous rows of h
+  x.wgt = buffer_rsrc(GATEUP && wave >= 2 ? Wb : Wa, wbytes);
   const uint16_t* abase = GATEUP ? a.A : a.A + (int64_t)tile.row_begin * K;
   const uint32_t abytes = GATEUP ? (uint32_t)(a.a_rows * K * 2) : (uint32_t)nrows * K * 2u;
-  ctx.act = buffer_rsrc(abase, abytes);
-  // weight fragment f: gate/up: f = 0 -> W1 rows, f = 1 -> the same rows of W3;
-  // down: 16 rows each
+  x.act = buffer_rsrc(abase, abytes);
+  // transfer lane l of unit u: row 8u + (l >> 3), slot piece l & 7 holding piece
+  // (l & 7) ^ sigma(row)
+  // rows past the tile's end load nothing (an offset past the buffer reads zeros and
+  // moves no data; their outputs are not stored)
 #pragma unroll
-  for (int f = 0; f < NW; ++f) {
-    int n = n_wave + (GATEUP ? 0 : 16 * f) + r;
-    if (n > N - 1) n = N - 1;
-    ctx.woff[f] = ((uint32_t)n * (uint32_t)K + q * 8) * 2u;
-  }
-  // activation pieces of this thread: row (tid >> 3) + 64 i, 16-byte chunk tid & 7
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int m = (tid >> 3) + (NT / 8) * i;
-    int64_t p = tile.row_begin + m;
-    if (p >= tile.row_end) p = tile.row_end - 1;
-    ctx.aoff[i] = (uint32_t)(act_row(a, GATEUP, p) - abase) * 2u + (tid & 7) * 16;
-  }
-  ctx.adst = ((tid & 7) * BM + ((tid >> 3) ^ (2 * (tid & 7)))) * 8;
-  ctx.nks = K / 32;
-  ctx.nc = K / BK;
-
-  f32x4_t acc[FM][NW];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int f = 0; f < NW; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // live row fragments rounded up to a multiple of MOE_STREAM_NL_STEP (workgroup-uniform)
-  const int nfrag = (nrows + 15) / 16;
-  stream_dispatch<EPI, MOE_STREAM_NL_STEP>(nfrag, ctx, lds, acc);
-
-  // epilogue: acc[i][f] of this lane = tile row 16 i + r, features 4 q .. 4 q + 3 of
-  // weight fragment f
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = 16 * i + r;
-    if (m >= nrows) continue;
+  for (int j = 0; j < 8; ++j) {
+    const int u = wave * 8 + j, m = 8 * u + (lane >> 3);
+    const int piece = (lane & 7) ^ (m & 7) ^ (u & 1);
     const int64_t p = tile.row_begin + m;
-    if (GATEUP) {
-      const int nn = n_wave + 4 * q;
-      if (nn < N) store4<EPI>(a, p, nn, acc[i][0], acc[i][1]);
-    } else {
+    x.aoff[j] = p < tile.row_end
+                    ? (uint32_t)(act_row(a, GATEUP, p) - abase) * 2u + piece * 16
+                    : abytes;
+  }
+  // weight row m of the workgroup: gate/up rows 0..127 are W1 features f0 + m, rows
+  // 128..255 the same features of W3; otherwise features f0 + m.  Unit j of the wave:
+  // m = 64 wave + 8 j + (lane >> 3), piece (lane & 7) ^ (lane >> 3) ^ (j & 1).  Features
+  // past N read beyond the matrix and get zeros (their outputs are not stored).
+  {
+    const int n0 = f0 + 64 * (GATEUP ? (wave & 1) : wave) + (lane >> 3);
 #pragma unroll
-      for (int f = 0; f < NW; ++f) {
-        const int nn = n_wave + 16 * f + 4 * q;
-        if (nn < N) store4<EPI>(a, p, nn, acc[i][f], acc[i][f]);
-      }
+    for (int e = 0; e < 2; ++e)
+      x.woff[e] = (uint32_t)n0 * (uint32_t)K * 2u + ((lane & 7) ^ (lane >> 3) ^ e) * 16;
+    x.wstride = 8u * (uint32_t)K * 2u;
+  }
+  // the two row halves interleave 32-row fragments (wave wm: tile rows 64 t + 32 wm ..),
+  // so a partly filled tile keeps both halves equally busy
+  const int arow = 32 * wm;
+  // first weight row of this wave's fragments: gate/up W1 rows 64 wn (W3 rows 128 + 64 wn);
+  // otherwise 128 wn
+  const int wrow0 = (GATEUP ? 64 : 128) * wn;
+  {
+    const int r32 = lane & 31, sig = (lane & 7) ^ ((r32 >> 3) & 1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int rd = (r32 >> 3) * 64 + (lane & 7) * 8 + ((2 * kk + (lane >> 5)) ^ sig);
+      x.wrd[kk] = wrow0 * 8 + rd;
+      x.ard[kk] = arow * 8 + rd;
     }
+  }
+  x.nc = K / kLdsChunkK;
+  // both buffers are under 2 GiB (checked on the host), so offset + this stays in 32 bits
+  x.aoob = abytes;
+  x.woob = wbytes;
+  // first output feature of this wave's fragments (gate/up: of its W1 and W3 fragments)
+  const int nbase = f0 + (GATEUP ? 64 : 128) * wn;
+
+  // live 32-row fragments of this wave's half of the tile (wave-uniform)
+  const int nf = min(4, max(0, (nrows - arow + 63) / 64));
+  const LdsBufs bufs{Ab, W0, W1, W2};
+  switch (nf) {
+    case 0: lds_tile<EPI, 0>(a, x, bufs, wave, arow, tile, nbase); break;
+    case 1: lds_tile<EPI, 1>(a, x, bufs, wave, arow, tile, nbase); break;
+    case 2: lds_tile<EPI, 2>(a, x, bufs, wave, arow, tile, nbase); break;
+    case 3: lds_tile<EPI, 3>(a, x, bufs, wave, arow, tile, nbase); break;
+    default: lds_tile<EPI, 4>(a, x, bufs, wave, arow, tile, nbase); break;
   }
 }
 
@@ -373,7 +400,7 @@ int64_t ffn_max_tiles(const FfnShape& sh) { return max_tiles_for(sh, kSkinnyBM);
 // The 256-row-tile kernel covers 128 (gate/up) or 256 (otherwise) features of N per block.
 template <int EPI>
 void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a) {
-  hipLaunchKernelGGL(ffn_stream_kernel<EPI>, grid, dim3(512), 0, s, a);
+  hipLaunchKernelGGL(ffn_lds_kernel<EPI>, grid, dim3(256), 0, s, a);
 }
 
 hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
@@ -382,7 +409,7 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
   // one group (the "shared" slot of the tile list) whose rows are all the rows of A
   const FfnShape sh{rows, K, 0, 0, N, true};
   const bool wide = rows > 512;
-  const int BM = wide ? kStreamBM : kSkinnyBM;
+  const int BM = wide ? kWideBM : kSkinnyBM;
   hipError_t err = tiles_launch(sh, nullptr, BM, tiles, ntiles, s);
   if (err != hipSuccess) return err;
   FfnArgs a{};
@@ -399,7 +426,7 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
   a.N = N;
   a.K = K;
   a.E = 0;
-  const dim3 gs = grid_for(sh, BM, kStreamBNDown, N), gk = grid_for(sh, BM, 64, N),
+  const dim3 gs = grid_for(sh, BM, kWideBNDown, N), gk = grid_for(sh, BM, 64, N),
              gk2 = grid_for(sh, BM, 128, N);
   switch (mode) {
     case DenseOut::kF32:
@@ -423,7 +450,7 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
                           const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, Tile* tiles,
                           int32_t* ntiles, hipStream_t s) {
   const bool wide = use_wide(sh);
-  const int BM = wide ? kStreamBM : kSkinnyBM;
+  const int BM = wide ? kWideBM : kSkinnyBM;
   hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
   if (err != hipSuccess) return err;
   FfnArgs a{};
@@ -443,7 +470,7 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   a.K = sh.d;
   a.E = sh.E;
   if (wide)
-    launch_wide<kSwiGLU>(grid_for(sh, BM, kStreamBNGateUp, a.N), s, a);
+    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a);
   else
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kSwiGLU>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
@@ -454,7 +481,7 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
                        const uint16_t* w2, const uint16_t* ws2, float* y_routed,
                        float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s) {
   const bool wide = use_wide(sh);
-  const int BM = wide ? kStreamBM : kSkinnyBM;
+  const int BM = wide ? kWideBM : kSkinnyBM;
   hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
   if (err != hipSuccess) return err;
   FfnArgs a{};
@@ -475,7 +502,7 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.K = sh.I;
   a.E = sh.E;
   if (wide)
-    launch_wide<kF32>(grid_for(sh, BM, kStreamBNDown, a.N), s, a);
+    launch_wide<kF32>(grid_for(sh, BM, kWideBNDown, a.N), s, a);
   else
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);

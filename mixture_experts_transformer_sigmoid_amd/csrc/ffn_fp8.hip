@@ -420,7 +420,7 @@ hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32
   a.N = sh.I;
   a.K = sh.d;
   if (wide)
-    hipLaunchKernelGGL(ffn_stream_fp8_kernel<kSwiGLU>, grid_for(sh, BM, kStreamBNGateUp, a.N),
+    hipLaunchKernelGGL(ffn_stream_fp8_kernel<kSwiGLU>, grid_for(sh, BM, kWideBNGateUp, a.N),
                        dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((ffn_skinny_fp8_kernel<kSkinnyNF, kSkinnyF8KB, kSwiGLU>),
@@ -443,7 +443,7 @@ hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t*
   a.N = sh.d;
   a.K = sh.I;
   if (wide)
-    hipLaunchKernelGGL(ffn_stream_fp8_kernel<kF32>, grid_for(sh, BM, kStreamBNDown, a.N),
+    hipLaunchKernelGGL(ffn_stream_fp8_kernel<kF32>, grid_for(sh, BM, kWideBNDown, a.N),
                        dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((ffn_skinny_fp8_kernel<kSkinnyNF, kSkinnyF8KB, kF32>),

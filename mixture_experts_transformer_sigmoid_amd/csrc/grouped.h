@@ -47,6 +47,12 @@ struct FfnArgs {
 };
 
 // ------------------------------------------------------------------ tile list
+// The shared expert's row tiles are cut into kSharedParts parts, part i placed after the
+// i-th eighth of the routed experts: the work list is dealt to the 8 XCDs as 8 contiguous
+// runs, and the shared tiles (full rows, at prefill the heaviest tiles) must not all land
+// on one XCD.
+constexpr int kSharedParts = 8;
+
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int E, int64_t routed_rows,
                                                            int64_t shared_rows, int BM,
@@ -55,6 +61,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ ntiles) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t routed_total;
+  __shared__ int32_t set_start[kSharedParts + 1];  // routed tiles before expert E*i/P
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t o0 = 0, o1 = 0, n = 0;
   if (tid < E) {
@@ -79,33 +86,59 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
       acc += x;
     }
     routed_total = acc;
+    // a set with no expert (E = 0 in dense launches, or E < 8) starts after all routed
+    // tiles; the first expert of a set overwrites its entry below
+    set_start[0] = 0;
+    for (int i = 1; i <= kSharedParts; ++i) set_start[i] = acc;
   }
   __syncthreads();
-  // never write past the list, whatever offsets the caller passed (overlapping
-  // segments would otherwise multiply the tile count)
+  // exclusive prefix of routed tiles before expert tid
+  const int32_t before = v + wsum[wave] - n;
+  if (tid < E) {
+#pragma unroll
+    for (int i = 1; i < kSharedParts; ++i)
+      if (tid == (int)((int64_t)E * i / kSharedParts)) set_start[i] = before;
+  }
+  __syncthreads();
+  // never write past the list, whatever offsets the caller passed (overlapping segments
+  // would otherwise multiply the tile count)
   const int64_t ns = (shared_rows + BM - 1) / BM;
   const int32_t R = (int32_t)min<int64_t>(routed_total, capacity - ns);
-  const int32_t start = v + wsum[wave] - n;
-  const int32_t cnt = max(0, min(n, R - start));
-  for (int j = 0; j < cnt; ++j) {
-    Tile t;
-    t.group = tid;
-    t.row_begin = o0 + j * BM;
-    t.row_end = min(o0 + (j + 1) * BM, o1);
-    t.first = start;
-    t.count = cnt;
-    t.pad[0] = t.pad[1] = t.pad[2] = 0;
-    tiles[start + j] = t;
+  // shared tiles placed before routed set s: ns * s / P (parts 0 .. s-1)
+  auto shared_before = [&](int s) { return (int32_t)(ns * s / kSharedParts); };
+  if (tid < E) {
+    // the set of expert tid: largest s with E*s/P <= tid
+    int s = 0;
+#pragma unroll
+    for (int i = 1; i < kSharedParts; ++i)
+      if (tid >= (int)((int64_t)E * i / kSharedParts)) s = i;
+    const int32_t start = before + shared_before(s);
+    const int32_t cnt = max(0, min(n, R - before));  // routed tiles stop at R
+    for (int j = 0; j < cnt; ++j) {
+      Tile t;
+      t.group = tid;
+      t.row_begin = o0 + j * BM;
+      t.row_end = min(o0 + (j + 1) * BM, o1);
+      t.first = start;
+      t.count = cnt;
+      t.pad[0] = t.pad[1] = t.pad[2] = 0;
+      tiles[start + j] = t;
+    }
   }
+  // shared part i: tiles ns*i/P .. ns*(i+1)/P of the shared rows, after routed set i
   for (int64_t j = tid; j < ns; j += 1024) {
+    int i = 0;
+    while (i + 1 < kSharedParts && j >= shared_before(i + 1)) ++i;
+    const int32_t rs = min(set_start[i + 1], R);  // routed tiles before part i
+    const int32_t first = rs + shared_before(i);
     Tile t;
     t.group = E;
     t.row_begin = (int32_t)(routed_rows + j * BM);
     t.row_end = (int32_t)min<int64_t>(routed_rows + (j + 1) * BM, routed_rows + shared_rows);
-    t.first = R;
-    t.count = (int32_t)ns;
+    t.first = first;
+    t.count = shared_before(i + 1) - shared_before(i);
     t.pad[0] = t.pad[1] = t.pad[2] = 0;
-    tiles[R + j] = t;
+    tiles[first + (j - shared_before(i))] = t;
   }
   if (tid == 0) *ntiles = R + (int32_t)ns;
 }
@@ -181,7 +214,7 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
 }
 
 constexpr int kSkinnyBM = 16;
-constexpr int kStreamBM = 256;
+constexpr int kWideBM = 256;
 #ifndef MOE_SKINNY_NF
 #define MOE_SKINNY_NF 2
 #endif
@@ -190,8 +223,9 @@ constexpr int kStreamBM = 256;
 #endif
 constexpr int kSkinnyNF = MOE_SKINNY_NF;  // skinny: 4 waves x NF fragments = 64 NF features per block
 constexpr int kSkinnyKU = MOE_SKINNY_KU;  // skinny: k-steps (of 32) per batch of loads
-constexpr int kStreamBNGateUp = 128;  // stream: features of N per block (x2 weight matrices)
-constexpr int kStreamBNDown = 256;
+// 256-row kernels (bf16 LDS-tiled, FP8 stream): features of N per workgroup
+constexpr int kWideBNGateUp = 128;  // gate/up: 128 features of W1 and the same of W3
+constexpr int kWideBNDown = 256;
 
 int64_t max_tiles_for(const FfnShape& sh, int BM) {
   // sum_e ceil(c_e / BM) <= (T*k) / BM + E, plus the shared expert's ceil(T / BM)
@@ -199,7 +233,7 @@ int64_t max_tiles_for(const FfnShape& sh, int BM) {
 }
 
 // Average rows per group (routed experts plus the shared expert) decides the kernel: a
-// few (decode) -> skinny kernel; many (prefill) -> 256-row stream kernel.
+// few (decode) -> skinny kernel; many (prefill) -> a 256-row kernel.
 bool use_wide(const FfnShape& sh) {
   const int64_t rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
   const int64_t groups = sh.E + (sh.shared ? 1 : 0);

@@ -18,6 +18,11 @@ bool aligned(const void* p, size_t a) { return p != nullptr && ((uintptr_t)p % a
 
 bool has_shared(const moe_dims& d) { return d.d_shared > 0; }
 
+constexpr uint64_t kMaxBuffer = (uint64_t)1 << 31;
+
+// An [N, K] bf16 weight matrix the GEMM kernels can address (with 256 rows of slack).
+bool matrix_ok(int64_t N, int64_t K) { return (uint64_t)(N + 256) * K * 2 < kMaxBuffer; }
+
 moe_status check_dims(const moe_dims* dp) {
   if (dp == nullptr) return MOE_EINVAL;
   const moe_dims& d = *dp;
@@ -34,11 +39,12 @@ moe_status check_dims(const moe_dims* dp) {
   // per-token launches (combine, norm) must stay below 2^32 work-items per grid
   if (d.tokens > ((int64_t)1 << 23)) return MOE_EUNSUPPORTED;
   // the GEMM kernels address x, one expert's weight matrix and the split router matrix
-  // through 32-bit byte offsets
-  const uint64_t lim = (uint64_t)UINT32_MAX;
-  if ((uint64_t)d.tokens * d.d_model * 2 > lim) return MOE_EUNSUPPORTED;
-  if ((uint64_t)d.d_model * d.d_expert * 2 > lim) return MOE_EUNSUPPORTED;
-  if ((uint64_t)3 * d.n_experts * d.d_model * 2 > lim) return MOE_EUNSUPPORTED;
+  // through 32-bit byte offsets, and the wide kernel adds a buffer's size to an offset
+  // (up to 256 rows past the matrix) to make a load read nothing: each stays below 2 GiB
+  if ((uint64_t)d.tokens * d.d_model * 2 >= kMaxBuffer) return MOE_EUNSUPPORTED;
+  if (!matrix_ok(d.d_expert, d.d_model) || !matrix_ok(d.d_model, d.d_expert))
+    return MOE_EUNSUPPORTED;
+  if (!matrix_ok(3 * d.n_experts, d.d_model)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -156,10 +162,11 @@ moe_status check_latent(const moe_dims* dims, int32_t L) {
   MOE_TRY(check_dims(dims));
   if (L <= 0) return MOE_EINVAL;
   if (L % 64 != 0 || L > moe::kMaxLatent) return MOE_EUNSUPPORTED;
-  const uint64_t lim = (uint64_t)UINT32_MAX;
-  if ((uint64_t)dims->tokens * L * 2 > lim) return MOE_EUNSUPPORTED;
-  if ((uint64_t)L * dims->d_expert * 2 > lim) return MOE_EUNSUPPORTED;
-  if ((uint64_t)L * dims->d_model * 2 > lim) return MOE_EUNSUPPORTED;
+  // the same 2 GiB bound as check_dims, for the latent rows, the experts on width L and
+  // both projections
+  if ((uint64_t)dims->tokens * L * 2 >= kMaxBuffer) return MOE_EUNSUPPORTED;
+  if (!matrix_ok(dims->d_expert, L) || !matrix_ok(L, dims->d_expert)) return MOE_EUNSUPPORTED;
+  if (!matrix_ok(L, dims->d_model) || !matrix_ok(dims->d_model, L)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 

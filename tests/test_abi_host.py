@@ -64,7 +64,9 @@ def test_workspace_bytes_grow_with_tokens():
     (dict(tokens=-1), M.MOE_EINVAL),
     (dict(routed_scale=float("nan")), M.MOE_EINVAL),
     (dict(tokens=1 << 40), M.MOE_EUNSUPPORTED),
-    (dict(tokens=300_000), M.MOE_EUNSUPPORTED),          # x would need 4 GiB or more
+    (dict(tokens=150_000), M.MOE_EUNSUPPORTED),          # x would need 2 GiB or more
+    (dict(d_model=1 << 16, d_expert=1 << 14, d_shared=1 << 14),
+     M.MOE_EUNSUPPORTED),                                  # one weight matrix near 2 GiB
     (dict(tokens=(1 << 23) + 1, d_model=64, d_expert=64, d_shared=64, top_k=1),
      M.MOE_EUNSUPPORTED),                                  # per-token grids above 2^32 items
 ])
@@ -75,6 +77,13 @@ def test_bad_dims_rejected(bad, code):
     d = M.moe_dims(**kw)
     n = ctypes.c_size_t(0)
     assert M.lib().moe_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == code
+
+
+def test_largest_x_accepted():
+    # x just under 2 GiB at d = 7168 (149,796 tokens) is addressable
+    d = M.moe_dims(149_796, 7168, 384, 8, 2048, 2048)
+    n = ctypes.c_size_t(0)
+    assert M.lib().moe_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == M.MOE_OK
 
 
 def _fake(addr):
