@@ -105,6 +105,8 @@ def parse():
     ap.add_argument("--no-block", action="store_true",
                     help="skip the fused norm + residual block figure")
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens in the oracle sample")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured HBM-copy and vendor-GEMM peaks")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two --pmc counter CSVs and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -310,6 +312,46 @@ def time_latent(M, torch, S, dev, steps):
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
+def measure_ceilings(torch, dev):
+    """Achievable peaks on this GPU, next to the published ones: a 1 GiB device copy (read +
+    write) for HBM, and the vendor GEMM (torch.matmul -> hipBLASLt) on an 8192^3 bf16
+    product with N(0, 1) operands and with all-zero operands.  bf16 MFMA throughput on this
+    part depends on the data: random operands toggle the datapath and the chip lowers its
+    clock to stay in its power budget."""
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(n):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+    src = torch.full((COPY_BYTES,), 7, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda: dst.copy_(src), 5)
+    del src, dst
+    n = 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    rand_ms = timed(lambda: torch.matmul(a, b), 5)
+    a.zero_()
+    b.zero_()
+    zero_ms = timed(lambda: torch.matmul(a, b), 5)
+    del a, b
+    torch.cuda.empty_cache()
+    flops = 2.0 * n ** 3
+    return {"hbm_copy_gbs": 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9,
+            "mfma_bf16_random_tflops": flops / (rand_ms * 1e-3) / 1e12,
+            "mfma_bf16_zeros_tflops": flops / (zero_ms * 1e-3) / 1e12,
+            "how": "1 GiB device-to-device copy (bytes read + written); torch.matmul "
+                   "(hipBLASLt) 8192x8192x8192 bf16, N(0,1) operands and all-zero operands"}
+
+
 def cpu_baseline(torch, S, cfg, inp, n_tok):
     """The oracle as it stands on a bounded sample: route + sparse FFN for n_tok tokens of
     the batch, weights pre-staged on the host (bf16), timed on the host cores."""
@@ -458,6 +500,14 @@ def main():
         log(f"timing the CPU oracle on {args.cpu_sample} tokens")
         res["cpu_baseline"] = cpu_baseline(torch, S, cfg, inp, args.cpu_sample)
         log(f"cpu oracle: {res['cpu_baseline']['value']:.2f} tok/s on {res['cpu_baseline']['cores']} threads")
+    if not args.no_ceilings:
+        ceil = measure_ceilings(torch, dev)
+        res["ceilings"] = ceil
+        rt = ceil["mfma_bf16_random_tflops"]
+        if "prefill" in res:
+            res["prefill"]["mfma_frac_of_measured_random"] = res["prefill"]["mfma_tflops"] / rt
+        log(f"ceilings: copy {ceil['hbm_copy_gbs']:.0f} GB/s; vendor GEMM bf16 {rt:.0f} TFLOP/s "
+            f"(random), {ceil['mfma_bf16_zeros_tflops']:.0f} TFLOP/s (zeros)")
     if not args.no_latent:
         # latent variant (experts on a 3584-wide latent), 4096 tokens; its own weights
         del weights
@@ -465,6 +515,9 @@ def main():
             del inp[key]
         torch.cuda.empty_cache()
         lres = time_latent(M, torch, S, dev, max(3, min(args.steps, 10)))
+        if "ceilings" in res:
+            lres["mfma_frac_of_measured_random"] = (lres["mfma_tflops"]
+                                                    / res["ceilings"]["mfma_bf16_random_tflops"])
         res["latent"] = lres
         log(f"latent: {lres['ms_per_step']:.3f} ms/step, {lres['tokens_per_s']:.0f} tok/s, "
             f"{lres['hbm_gbs']:.0f} GB/s, {lres['mfma_tflops']:.0f} TFLOP/s")

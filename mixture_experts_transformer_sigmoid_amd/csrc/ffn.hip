@@ -157,8 +157,8 @@ struct LdsCtx {
   int nc;                      // chunks
 };
 
-// The wave's 8 weight transfers of chunk c (units 8 wave .. 8 wave + 7); past the last
-// chunk they read nothing.
+// Whole-chunk moves, for the prologue: the wave's 8 weight transfers of chunk c (units
+// 8 wave .. 8 wave + 7), its 8 activation loads, and their store to LDS.
 __device__ __forceinline__ void lds_fetch_w(const LdsCtx& x, u32x4_t* wgt, int wave, int c) {
   const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.woob;
 #pragma unroll
@@ -178,20 +178,42 @@ __device__ __forceinline__ void lds_store_a(u32x4_t* act, const u32x4_t (&ar)[8]
   for (int j = 0; j < 8; ++j) act[(wave * 8 + j) * 64 + lane] = ar[j];
 }
 
-// Every wave has stored its activations and finished reading the buffers of the previous
-// chunk, and its weight transfers of this chunk have landed (only the 16 loads requested
-// during the previous chunk may still be in flight).
+// Data movement of sub-step kk (of 4) of a chunk, spread so that no wave issues a burst
+// of loads (bursts from four waves at once fill the texture unit's queues and stall the
+// MFMA stream behind them): the activation pieces 2kk, 2kk+1 of the next chunk go from
+// registers to LDS, the same registers are refilled with the pieces of the chunk after it,
+// and the weight units 2kk, 2kk+1 of that chunk are requested (they land in LDS two chunks
+// ahead).  Loads past the last chunk read nothing.
+__device__ __forceinline__ void lds_move(const LdsCtx& x, u32x4_t* act_next, u32x4_t* wnext2,
+                                         u32x4_t (&ar)[8], int wave, int c2, int kk) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t asoff = c2 < x.nc ? (uint32_t)c2 * (kLdsChunkK * 2) : x.aoob;
+  const uint32_t wsoff = c2 < x.nc ? (uint32_t)c2 * (kLdsChunkK * 2) : x.woob;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int j = 2 * kk + e;
+    act_next[(wave * 8 + j) * 64 + lane] = ar[j];
+    ar[j] = bload16(x.act, x.aoff[j], asoff);
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int j = 2 * kk + e;
+    dma16(x.wgt, wnext2 + (wave * 8 + j) * 64, x.woff[j & 1], wsoff + (uint32_t)j * x.wstride);
+  }
+}
+
+// Every wave has stored the activations of this chunk and finished reading the buffers of
+// the previous one, and its weight transfers of this chunk have landed (only the 16 loads
+// issued during the previous chunk may still be in flight).
 __device__ __forceinline__ void lds_sync() {
   asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// One chunk (4 sub-steps of 16 k) on NF of the wave's 4 row fragments.  Sub-step kk reads
-// weight fragment o at slot wrd[kk] + 8 wfrag_row(o) and row fragment t (tile rows
-// 64 t + 32 wm ..) at slot ard[kk] + 512 t (the wave-dependent parts are in wrd/ard, so
-// the fragment offsets are immediates).  The operands of sub-step kk + 1 are read while the MFMAs of sub-step kk
-// run.
+// Sub-step kk reads weight fragment o at slot wrd[kk] + 8 wfrag_row(o) and row fragment t
+// (tile rows 64 t + 32 wm ..) at slot ard[kk] + 512 t (the wave-dependent parts are in
+// wrd/ard, so the fragment offsets are immediates).
 template <bool GATEUP>
 __device__ __forceinline__ constexpr int wfrag_row(int o) {
   // gate/up: o = 0, 1 are W1 rows 32 o of the wave's 64 features, o = 2, 3 the same
@@ -199,26 +221,39 @@ __device__ __forceinline__ constexpr int wfrag_row(int o) {
   return GATEUP ? 128 * (o >> 1) + 32 * (o & 1) : 32 * o;
 }
 
+// Chunk c (weights in wcur): wait, then four sub-steps of 16 k, each moving its share of
+// the next chunks' data, then reading the operands of the following sub-step while its
+// own MFMAs run.
 template <bool GATEUP, int NF>
-__device__ __forceinline__ void lds_mma(const LdsCtx& x, const u32x4_t* act, const u32x4_t* wgt,
-                                        f32x16_t (&acc)[NF][4]) {
-  u32x4_t wv[2][4], av[2][NF];
+__device__ __forceinline__ void lds_chunk(const LdsCtx& x, u32x4_t* Ab, const u32x4_t* wcur,
+                                          u32x4_t* wnext2, u32x4_t (&ar)[8], int wave, int c,
+                                          f32x16_t (&acc)[NF > 0 ? NF : 1][4]) {
+  lds_sync();
+  const u32x4_t* act = Ab + (c & 1) * 2048;
+  u32x4_t* act_next = Ab + ((c + 1) & 1) * 2048;
+  constexpr int NA = NF > 0 ? NF : 1;
+  u32x4_t wv[2][4], av[2][NA];
   auto read = [&](int kk, int b) {
 #pragma unroll
-    for (int o = 0; o < 4; ++o) wv[b][o] = wgt[x.wrd[kk] + 8 * wfrag_row<GATEUP>(o)];
+    for (int o = 0; o < 4; ++o) wv[b][o] = wcur[x.wrd[kk] + 8 * wfrag_row<GATEUP>(o)];
 #pragma unroll
     for (int t = 0; t < NF; ++t) av[b][t] = act[x.ard[kk] + 512 * t];
   };
-  read(0, 0);
+  if constexpr (NF > 0) read(0, 0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    if (kk < 3) read(kk + 1, (kk + 1) & 1);
-    // keep the next sub-step's reads ahead of this sub-step's MFMAs
-    __builtin_amdgcn_sched_barrier(0);
+    lds_move(x, act_next, wnext2, ar, wave, c + 2, kk);
+    if constexpr (NF > 0) {
+      if (kk < 3) read(kk + 1, (kk + 1) & 1);
+      // keep this sub-step's data movement and the next sub-step's reads ahead of its
+      // MFMAs
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < NF; ++t)
+      for (int t = 0; t < NF; ++t)
 #pragma unroll
-      for (int o = 0; o < 4; ++o) acc[t][o] = mfma32x32x16(wv[kk & 1][o], av[kk & 1][t], acc[t][o]);
+        for (int o = 0; o < 4; ++o)
+          acc[t][o] = mfma32x32x16(wv[kk & 1][o], av[kk & 1][t], acc[t][o]);
+    }
   }
 }
 
@@ -230,19 +265,6 @@ struct LdsBufs {
   u32x4_t* W1;    // which transfers a read depends on)
   u32x4_t* W2;
 };
-
-// Chunk c with its weights in buffer WB (WB == c % 3): wait, request weights c + 2 and
-// activations c + 2 (registers), multiply, then store activations c + 1 for the next chunk.
-template <bool GATEUP, int NF>
-__device__ __forceinline__ void lds_step(const LdsCtx& x, const LdsBufs& b, u32x4_t* wcur,
-                                         u32x4_t* wnext2, u32x4_t (&ar)[8], int wave, int c,
-                                         f32x16_t (&acc)[NF > 0 ? NF : 1][4]) {
-  lds_sync();
-  lds_fetch_w(x, wnext2, wave, c + 2);
-  if constexpr (NF > 0) lds_mma<GATEUP, NF>(x, b.A + (c & 1) * 2048, wcur, acc);
-  lds_store_a(b.A + ((c + 1) & 1) * 2048, ar, wave);
-  lds_load_a(x, ar, c + 2);
-}
 
 // A tile for a wave with NF live row fragments (NF = 0: the wave only moves data): the K
 // loop, then the epilogue.  Every wave runs the same loads and barriers whatever its NF.
@@ -261,19 +283,21 @@ __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, cons
 
   const int nc = x.nc;
   u32x4_t ar[8];
+  // prologue: activations of chunk 0 to LDS, weights of chunks 0 and 1 requested,
+  // activations of chunk 1 in registers
+  lds_load_a(x, ar, 0);
   lds_fetch_w(x, b.W0, wave, 0);
   lds_fetch_w(x, b.W1, wave, 1);
-  lds_load_a(x, ar, 0);
   lds_store_a(b.A, ar, wave);
   lds_load_a(x, ar, 1);
   int c = 0;
   for (; c + 3 <= nc; c += 3) {
-    lds_step<GATEUP, NF>(x, b, b.W0, b.W2, ar, wave, c, acc);
-    lds_step<GATEUP, NF>(x, b, b.W1, b.W0, ar, wave, c + 1, acc);
-    lds_step<GATEUP, NF>(x, b, b.W2, b.W1, ar, wave, c + 2, acc);
+    lds_chunk<GATEUP, NF>(x, b.A, b.W0, b.W2, ar, wave, c, acc);
+    lds_chunk<GATEUP, NF>(x, b.A, b.W1, b.W0, ar, wave, c + 1, acc);
+    lds_chunk<GATEUP, NF>(x, b.A, b.W2, b.W1, ar, wave, c + 2, acc);
   }
-  if (c < nc) lds_step<GATEUP, NF>(x, b, b.W0, b.W2, ar, wave, c, acc);
-  if (c + 1 < nc) lds_step<GATEUP, NF>(x, b, b.W1, b.W0, ar, wave, c + 1, acc);
+  if (c < nc) lds_chunk<GATEUP, NF>(x, b.A, b.W0, b.W2, ar, wave, c, acc);
+  if (c + 1 < nc) lds_chunk<GATEUP, NF>(x, b.A, b.W1, b.W0, ar, wave, c + 1, acc);
   // the requests past the last chunk read nothing; let them retire before the stores
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (NF == 0) return;
