@@ -105,6 +105,8 @@ def parse():
     ap.add_argument("--no-block", action="store_true",
                     help="skip the fused norm + residual block figure")
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens in the oracle sample")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip sampling socket power / clock during the prefill loop")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured HBM-copy and vendor-GEMM peaks")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -352,6 +354,67 @@ def measure_ceilings(torch, dev):
                    "(hipBLASLt) 8192x8192x8192 bf16, N(0,1) operands and all-zero operands"}
 
 
+def sample_power(M, torch, dims, inp, out, ws, seconds=6.0):
+    """Socket power and graphics clock while the layer runs back to back: amd-smi is
+    sampled from a thread while the main thread keeps the GPU busy.  Returns None when
+    amd-smi is not available."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    smi = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if smi is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                txt = subprocess.run([smi, "metric", "-p", "-c"], capture_output=True, text=True,
+                                     timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            w = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+            clk, section = [], ""
+            for line in txt.splitlines():
+                head = re.match(r"^\s*([A-Z]+_?\d*):\s*$", line)
+                if head:
+                    section = head.group(1)
+                    continue
+                m = re.match(r"^\s*CLK:\s*([0-9.]+)\s*MHz", line)
+                if m and section.startswith("GFX"):  # graphics clock of each XCD
+                    clk.append(float(m.group(1)))
+            if w:
+                samples.append((float(w[0]), sum(clk) / len(clk) if clk else None))
+            stop.wait(0.5)
+
+    def call():
+        M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
+                      inp["ws1"], inp["ws3"], inp["ws2"], out, ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    n = 0
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        n += 10
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    ws_ = [p for p, _ in samples]
+    cs = [c for _, c in samples if c is not None]
+    return {"socket_power_w": sum(ws_) / len(ws_), "socket_power_w_max": max(ws_),
+            "gfx_clock_mhz": (sum(cs) / len(cs)) if cs else None, "samples": len(samples),
+            "layer_passes": n, "how": "amd-smi metric -p -c every 0.5 s while moe_forward runs "
+                                      "back to back (k2_prefill)"}
+
+
 def cpu_baseline(torch, S, cfg, inp, n_tok):
     """The oracle as it stands on a bounded sample: route + sparse FFN for n_tok tokens of
     the batch, weights pre-staged on the host (bf16), timed on the host cores."""
@@ -471,6 +534,7 @@ def main():
         palg = algorithmic(pcfg, pact, pcfg["tokens"])
         ptf = palg["layer_flops"] / (pms * 1e-3) / 1e12
         pgb = palg["layer_bytes"] / (pms * 1e-3) / 1e9
+        power = None if args.no_power else sample_power(M, torch, pdims, pin, pout, pws)
         if not args.no_block:
             del pws
             pbms = time_block(M, torch, S, pcfg, weights, psteps, 1)
@@ -479,6 +543,10 @@ def main():
                           "ms_per_step": pms, "tokens_per_s": pcfg["tokens"] / (pms * 1e-3),
                           "mfma_tflops": ptf, "mfma_frac": ptf / MFMA_BF16_PEAK_TFLOPS,
                           "hbm_gbs": pgb, "hbm_frac": pgb / HBM_PEAK_GBS, "active_experts": pact}
+        if power is not None:
+            res["prefill"]["power"] = power
+            log(f"prefill power: {power['socket_power_w']:.0f} W socket, "
+                f"graphics clock {power['gfx_clock_mhz'] or 0:.0f} MHz")
         if not args.no_block:
             res["prefill"]["block_ms_per_step"] = pbms
             log(f"block (k2_prefill): {pbms:.3f} ms/step ({(pbms - pms) * 1e3:+.1f} us vs the layer)")

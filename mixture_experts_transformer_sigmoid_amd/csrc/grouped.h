@@ -47,21 +47,23 @@ struct FfnArgs {
 };
 
 // ------------------------------------------------------------------ tile list
-// The shared expert's row tiles are cut into kSharedParts parts, part i placed after the
-// i-th eighth of the routed experts: the work list is dealt to the 8 XCDs as 8 contiguous
-// runs, and the shared tiles (full rows, at prefill the heaviest tiles) must not all land
-// on one XCD.
-constexpr int kSharedParts = 8;
+// The shared expert's row tiles can be cut into `parts` parts (at most kMaxSharedParts),
+// part i placed after the i-th share of the routed experts.  The work list is dealt to the
+// 8 XCDs as 8 contiguous runs: with 256-row tiles (prefill) the shared tiles are the
+// heaviest work and are spread over all 8 (parts = 8); with 16-row tiles (decode) every
+// shared tile reads the whole shared weight matrix, and keeping them together (parts = 1)
+// lets them share it in one L2.
+constexpr int kMaxSharedParts = 8;
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int E, int64_t routed_rows,
                                                            int64_t shared_rows, int BM,
-                                                           int64_t capacity,
+                                                           int parts, int64_t capacity,
                                                            Tile* __restrict__ tiles,
                                                            int32_t* __restrict__ ntiles) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t routed_total;
-  __shared__ int32_t set_start[kSharedParts + 1];  // routed tiles before expert E*i/P
+  __shared__ int32_t set_start[kMaxSharedParts + 1];  // routed tiles before expert E*i/P
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t o0 = 0, o1 = 0, n = 0;
   if (tid < E) {
@@ -89,15 +91,14 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     // a set with no expert (E = 0 in dense launches, or E < 8) starts after all routed
     // tiles; the first expert of a set overwrites its entry below
     set_start[0] = 0;
-    for (int i = 1; i <= kSharedParts; ++i) set_start[i] = acc;
+    for (int i = 1; i <= parts; ++i) set_start[i] = acc;
   }
   __syncthreads();
   // exclusive prefix of routed tiles before expert tid
   const int32_t before = v + wsum[wave] - n;
   if (tid < E) {
-#pragma unroll
-    for (int i = 1; i < kSharedParts; ++i)
-      if (tid == (int)((int64_t)E * i / kSharedParts)) set_start[i] = before;
+    for (int i = 1; i < parts; ++i)
+      if (tid == (int)((int64_t)E * i / parts)) set_start[i] = before;
   }
   __syncthreads();
   // never write past the list, whatever offsets the caller passed (overlapping segments
@@ -105,13 +106,12 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   const int64_t ns = (shared_rows + BM - 1) / BM;
   const int32_t R = (int32_t)min<int64_t>(routed_total, capacity - ns);
   // shared tiles placed before routed set s: ns * s / P (parts 0 .. s-1)
-  auto shared_before = [&](int s) { return (int32_t)(ns * s / kSharedParts); };
+  auto shared_before = [&](int s) { return (int32_t)(ns * s / parts); };
   if (tid < E) {
     // the set of expert tid: largest s with E*s/P <= tid
     int s = 0;
-#pragma unroll
-    for (int i = 1; i < kSharedParts; ++i)
-      if (tid >= (int)((int64_t)E * i / kSharedParts)) s = i;
+    for (int i = 1; i < parts; ++i)
+      if (tid >= (int)((int64_t)E * i / parts)) s = i;
     const int32_t start = before + shared_before(s);
     const int32_t cnt = max(0, min(n, R - before));  // routed tiles stop at R
     for (int j = 0; j < cnt; ++j) {
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   // shared part i: tiles ns*i/P .. ns*(i+1)/P of the shared rows, after routed set i
   for (int64_t j = tid; j < ns; j += 1024) {
     int i = 0;
-    while (i + 1 < kSharedParts && j >= shared_before(i + 1)) ++i;
+    while (i + 1 < parts && j >= shared_before(i + 1)) ++i;
     const int32_t rs = min(set_start[i + 1], R);  // routed tiles before part i
     const int32_t first = rs + shared_before(i);
     Tile t;
@@ -242,8 +242,10 @@ bool use_wide(const FfnShape& sh) {
 
 hipError_t tiles_launch(const FfnShape& sh, const int32_t* offsets, int BM, Tile* tiles,
                         int32_t* ntiles, hipStream_t s) {
+  const int parts = BM > kSkinnyBM ? kMaxSharedParts : 1;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, sh.E, sh.T * sh.k,
-                     sh.shared ? sh.T : (int64_t)0, BM, max_tiles_for(sh, BM), tiles, ntiles);
+                     sh.shared ? sh.T : (int64_t)0, BM, parts, max_tiles_for(sh, BM), tiles,
+                     ntiles);
   return hipGetLastError();
 }
 
