@@ -90,6 +90,11 @@ def full_check(cfg, inp, sample=None, seed=0, intermediates=True, inter_tokens=2
     say(f"fp8 case T={T} d={cfg['d_model']} E={cfg['n_experts']} k={k} I={cfg['d_expert']} "
         f"Is={cfg['d_shared']}")
     g = run_split(cfg, inp)
+    # every output element was written (each was pre-filled with NaN): no row tile or
+    # n-block of the device-built work list was missed
+    for name in ("h", "y", "ys", "out", "fw"):
+        if g[name] is not None:
+            assert bool(torch.isfinite(g[name].float()).all()), f"{name}: elements never written"
     assert torch.equal(g["fw"].view(torch.int16), g["out"].view(torch.int16)), "forward != split"
     again = run_split(cfg, inp)
     assert torch.equal(again["out"].view(torch.int16), g["out"].view(torch.int16)), "not deterministic"

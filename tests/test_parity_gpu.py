@@ -193,11 +193,24 @@ def shared_of(inp):
     return (f64(inp["ws1"]), f64(inp["ws3"]), f64(inp["ws2"])) if "ws1" in inp else None
 
 
+def assert_all_written(g):
+    """Every element of every output was written: run_split pre-fills them with NaN (or -7)
+    sentinels, so a row tile or n-block that the device-built work list missed would leave
+    one behind.  At the full sizes the value checks only sample tokens; this covers all."""
+    for name in ("h", "y_r", "y_s", "out", "w", "z"):
+        if g.get(name) is not None:
+            bad = int((~torch.isfinite(g[name].float())).sum())
+            assert bad == 0, f"{name}: {bad} elements never written"
+    for name in ("idx", "counts", "offsets", "perm", "inv"):
+        assert int((g[name] == -7).sum()) == 0, f"{name}: sentinel left"
+
+
 def full_check(cfg, inp, dims=None, sample=None, intermediates=False, seed=0):
     dims = dims or M.dims_for(cfg)
     say(f"case T={dims.tokens} d={dims.d_model} E={dims.n_experts} k={dims.top_k} "
         f"I={dims.d_expert} Is={dims.d_shared} alpha={dims.routed_scale}")
     g = run_split(cfg, inp, dims)
+    assert_all_written(g)
     ref = oracle_route(inp, dims)
     n_ex = check_routing(g, ref, dims)
     say(f"  routing ok; near-tie tokens excluded: {n_ex}")
