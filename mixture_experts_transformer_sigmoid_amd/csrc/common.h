@@ -70,7 +70,23 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// SwiGLU of one output, silu(g) u = g u / (1 + e^-g).  e^-g is 2^(-g log2 e) on the
+// hardware exp2 and the quotient one hardware reciprocal, each within about an fp32 ulp:
+// far inside the bf16 rounding that h gets next.  Large negative g: the exp2 overflows to
+// inf, the reciprocal gives 0 and the result is 0, the limit; large positive g: g u.
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16 (lo in bits 0..15) with the hardware conversion
+// (v_cvt_pk_bf16_f32): round to nearest even, NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations, then meets
 // the other waves.  Unlike __syncthreads() it does not drain the wave's outstanding

@@ -177,10 +177,10 @@ __device__ __forceinline__ const uint16_t* act_row(const FfnArgs& a, bool gateup
 __device__ __forceinline__ void store_gateup(uint16_t* dst, f32x4_t g, f32x4_t u) {
   float v[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = silu_f32(g[i]) * u[i];
+  for (int i = 0; i < 4; ++i) v[i] = swiglu_f32(g[i], u[i]);
   u32x2_t packed;
-  packed[0] = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-  packed[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  packed[0] = pack_bf16x2(v[0], v[1]);
+  packed[1] = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<u32x2_t*>(dst) = packed;
 }
 
@@ -207,8 +207,8 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
   } else {
     if (EPI == kAddBF16) v += *reinterpret_cast<const f32x4_t*>(a.R + p * N + nn);
     u32x2_t packed;
-    packed[0] = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-    packed[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    packed[0] = pack_bf16x2(v[0], v[1]);
+    packed[1] = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<u32x2_t*>(a.C + p * N + nn) = packed;
   }
 }
