@@ -257,93 +257,6 @@ __device__ __forceinline__ void lds_chunk(const LdsCtx& x, u32x4_t* Ab, const u3
   }
 }
 
-// Epilogue of a 256-row tile.  Accumulator register j of fragment (t, o), lane l, is tile
-// row arow + 64 t + (l & 31) and output 32 o + 8 (j >> 2) + 4 (l >> 5) + (j & 3) of the
-// wave's block, so a direct store writes 16 bytes into each of 32 rows, and the memory
-// system handles such scattered pieces far slower than whole lines.  Instead each wave
-// stages one 32-row fragment at a time in its own 16 KiB of the (by then idle) activation
-// buffers — fp32, the SwiGLU already applied — and reads it back along the rows, so that
-// one store instruction covers whole rows: 2 x 512 B (fp32, 128 outputs) or 4 x 128 B
-// (bf16 h, 64 outputs).
-//
-// Staging layout: row r (0..31) holds FW / 4 pieces of 4 outputs; piece p sits in slot
-// r (FW / 4) + (p ^ (r & 7)), so the 8 lanes that the LDS serves together (8 rows, one
-// piece, on the write side; one row, 8 pieces, on the read side) hit distinct banks.
-template <int EPI>
-__device__ __forceinline__ void store_row4(const FfnArgs& a, int64_t p, int nn, f32x4_t v) {
-  const int N = a.N;
-  if constexpr (EPI == kF32) {
-    float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
-    *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
-  } else {
-    if constexpr (EPI == kAddBF16) v += *reinterpret_cast<const f32x4_t*>(a.R + p * N + nn);
-    u32x2_t packed;
-    packed[0] = pack_bf16x2(v[0], v[1]);
-    packed[1] = pack_bf16x2(v[2], v[3]);
-    *reinterpret_cast<u32x2_t*>(a.C + p * N + nn) = packed;
-  }
-}
-
-template <int EPI, int NF>
-__device__ __forceinline__ void lds_epilogue(const FfnArgs& a, u32x4_t* stage,
-                                             const f32x16_t (&acc)[NF][4], int arow,
-                                             const Tile& tile, int nbase) {
-  constexpr bool GATEUP = EPI == kSwiGLU;
-  constexpr int FO = GATEUP ? 2 : 4;  // 32-output fragments per row
-  constexpr int PPR = 8 * FO;         // 16-byte pieces per staged row
-  constexpr int RPI = 64 / PPR;       // rows per read-back instruction
-  const int lane = threadIdx.x & 63, hl = lane >> 5;
-  const int nrows = tile.row_end - tile.row_begin;
-  // fp32 rows of 3E router logits need not be whole 4-output groups: per-output stores
-  if (EPI == kF32 && (a.N & 3) != 0) {
-#pragma unroll
-    for (int t = 0; t < NF; ++t) {
-      const int m = arow + 64 * t + (lane & 31);
-      if (m >= nrows) continue;
-#pragma unroll
-      for (int oo = 0; oo < FO; ++oo)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nn = nbase + 32 * oo + 8 * q + 4 * hl;
-          const f32x16_t& g = acc[t][oo];
-          store4<EPI>(a, tile.row_begin + m, nn,
-                      f32x4_t{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]}, f32x4_t{});
-        }
-    }
-    return;
-  }
-  const int rw = lane & 31;
-  const int rr = lane / PPR, pr = lane % PPR;  // read side: row within the group, piece
-#pragma unroll
-  for (int t = 0; t < NF; ++t) {
-#pragma unroll
-    for (int oo = 0; oo < FO; ++oo)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x16_t& g = acc[t][oo];
-        f32x4_t v = {g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
-        if constexpr (GATEUP) {
-          const f32x16_t& u = acc[t][oo + 2];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = swiglu_f32(v[i], u[4 * q + i]);
-        }
-        const int piece = 8 * oo + 2 * q + hl;
-        stage[rw * PPR + (piece ^ (rw & 7))] = __builtin_bit_cast(u32x4_t, v);
-      }
-    // LDS operations of one wave complete in order: the reads below see these writes, and
-    // the next fragment's writes come after these reads
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = RPI * i + rr;
-      const f32x4_t v = __builtin_bit_cast(f32x4_t, stage[r * PPR + (pr ^ (r & 7))]);
-      const int m = arow + 64 * t + r;
-      const int nn = nbase + 4 * pr;
-      if (m < nrows && nn < a.N)
-        store_row4<GATEUP ? kBF16 : EPI>(a, tile.row_begin + m, nn, v);
-    }
-  }
-}
-
 struct LdsBufs {
   u32x4_t* A;     // two activation chunk buffers, 2048 slots each (one LDS array, indexed
                   // by chunk parity: a pointer picked from a table would lose its address
@@ -389,7 +302,7 @@ __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, cons
   // land, and every wave finish its last operand reads, before the buffers are reused
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
-  if constexpr (NF > 0) lds_epilogue<EPI, NF>(a, b.A + wave * 1024, acc, arow, tile, nbase);
+  if constexpr (NF > 0) lds_epilogue<EPI, NF>(a, b.A + wave * 1024, acc, arow, 64, tile, nbase);
 }
 
 template <int EPI>

@@ -189,6 +189,27 @@ def test_fp8_zero_and_extreme_scales():
     full_check(cfg, inp, inter_tokens=touch, per_row_bar=True)
 
 
+def test_fp8_zero_and_extreme_scales_wide():
+    # the same scale edits on the 256-row kernel (600 tokens, top-8 of 16: ~300 rows per
+    # expert): its per-128-k-block partial sums must keep the zero block and the extreme
+    # scales exact too
+    cfg = S.with_overrides("tiny", tokens=600, n_experts=16, top_k=8)
+    inp = fp8_inputs(cfg, seed=5)
+    inp["w1_scale"][0, 0, 1] = 0.0
+    inp["w3_scale"][1] *= 2.0 ** -20
+    inp["w2_scale"][2] *= 2.0 ** 10
+    dims = M.dims_for(cfg)
+    ws = M.workspace(dims)
+    T, k = cfg["tokens"], cfg["top_k"]
+    ti = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    tw = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    M.moe_route(dims, inp["x"], inp["w_r"], inp["b"], ti, tw, None, ws)
+    idx = ti.cpu().numpy()
+    touch = [t for t in range(T) if np.isin(idx[t], [0, 1, 2]).any()][:24]
+    assert touch
+    full_check(cfg, inp, inter_tokens=touch, per_row_bar=True)
+
+
 @pytest.fixture(scope="module")
 def k2_fp8_weights():
     say("generating K2-shape FP8 weights on the GPU (384 experts, d 7168, I 2048)")
