@@ -158,9 +158,12 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
                           const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, Tile* tiles,
                           int32_t* ntiles, hipStream_t s);
 
+// tiles_ready: the tile list already holds this shape's tiles for the same offsets (the
+// gate/up launch just before built it), so the down launch skips rebuilding it.
 hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
                        const uint16_t* w2, const uint16_t* ws2, float* y_routed,
-                       float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s);
+                       float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s,
+                       bool tiles_ready = false);
 
 // FP8 (E4M3) expert weights with one fp32 scale per 128 x 128 block; device pointers.
 struct Fp8Weights {
@@ -186,7 +189,7 @@ hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32
 
 hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
                            const Fp8Weights& w, float* y_routed, float* y_shared, Tile* tiles,
-                           int32_t* ntiles, hipStream_t s);
+                           int32_t* ntiles, hipStream_t s, bool tiles_ready = false);
 
 // residual (bf16 [T, d]) may be null; when given it is added before the bf16 rounding.
 hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float* topk_w,

@@ -475,18 +475,21 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   if (wide)
     launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a);
   else
-    hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kSwiGLU>),
-                       grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyGuNF, kSkinnyGuKU, kSwiGLU>),
+                       grid_for(sh, BM, 64 * kSkinnyGuNF, a.N), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
                        const uint16_t* w2, const uint16_t* ws2, float* y_routed,
-                       float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s) {
+                       float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s,
+                       bool tiles_ready) {
   const bool wide = use_wide(sh);
   const int BM = wide ? kWideBM : kSkinnyBM;
-  hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
-  if (err != hipSuccess) return err;
+  if (!tiles_ready) {
+    hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
+    if (err != hipSuccess) return err;
+  }
   FfnArgs a{};
   a.A = h;
   a.a_rows = sh.T * sh.k + (sh.shared ? sh.T : 0);

@@ -430,11 +430,13 @@ hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32
 
 hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
                            const Fp8Weights& w, float* y_routed, float* y_shared, Tile* tiles,
-                           int32_t* ntiles, hipStream_t s) {
+                           int32_t* ntiles, hipStream_t s, bool tiles_ready) {
   const bool wide = use_wide(sh);
   const int BM = wide ? kF8BM : kSkinnyBM;
-  hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
-  if (err != hipSuccess) return err;
+  if (!tiles_ready) {
+    hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
+    if (err != hipSuccess) return err;
+  }
   FfnArgs a = fp8_args(sh, w, false, tiles, ntiles);
   a.A = h;
   a.a_rows = sh.T * sh.k + (sh.shared ? sh.T : 0);

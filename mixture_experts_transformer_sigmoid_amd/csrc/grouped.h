@@ -308,8 +308,19 @@ constexpr int kWideBM = 256;
 #ifndef MOE_SKINNY_KU
 #define MOE_SKINNY_KU 8
 #endif
+#ifndef MOE_SKINNY_GU_NF
+#define MOE_SKINNY_GU_NF 1
+#endif
+#ifndef MOE_SKINNY_GU_KU
+#define MOE_SKINNY_GU_KU 16
+#endif
 constexpr int kSkinnyNF = MOE_SKINNY_NF;  // skinny: 4 waves x NF fragments = 64 NF features per block
 constexpr int kSkinnyKU = MOE_SKINNY_KU;  // skinny: k-steps (of 32) per batch of loads
+// gate/up reads two matrices per fragment, so it keeps as many bytes in flight with half
+// the fragments; its smaller blocks also shorten the launch's tail (K2 decode: 3.49 against
+// 3.54 ms with the down GEMM's 2 x 8)
+constexpr int kSkinnyGuNF = MOE_SKINNY_GU_NF;
+constexpr int kSkinnyGuKU = MOE_SKINNY_GU_KU;
 // 256-row kernels (bf16 LDS-tiled, FP8 stream): features of N per workgroup
 constexpr int kWideBNGateUp = 128;  // gate/up: 128 features of W1 and the same of W3
 constexpr int kWideBNDown = 256;

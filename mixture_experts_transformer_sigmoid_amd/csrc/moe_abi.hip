@@ -139,12 +139,15 @@ moe_status gate_up_impl(const moe_dims& d, const uint16_t* x, const int32_t* per
                                         at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles), s));
 }
 
+// tiles_ready: called right after gate_up_impl on the same offsets and workspace, whose
+// tile list the down GEMM shares
 moe_status down_impl(const moe_dims& d, const uint16_t* h, const int32_t* offsets,
                      const uint16_t* w2, const uint16_t* ws2, float* y_routed,
-                     float* y_shared, void* ws, hipStream_t s) {
+                     float* y_shared, void* ws, hipStream_t s, bool tiles_ready = false) {
   const Layout L = layout(d);
   return hip_status(moe::launch_down(ffn_shape(d), h, offsets, w2, ws2, y_routed, y_shared,
-                                     at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles), s));
+                                     at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles), s,
+                                     tiles_ready));
 }
 
 moe_status combine_impl(const moe_dims& d, const float* y_routed, const int32_t* inv,
@@ -231,7 +234,7 @@ moe_status forward_impl(const moe_dims& d, const uint16_t* x, const float* w_rou
   MOE_TRY(route_impl(d, x, w_router, bias, idx, w, nullptr, ws, s));
   MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s));
   MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s));
-  MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s));
+  MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s, true));
   return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, residual, out, d.tokens,
                                         d.d_model, d.top_k, s));
 }
@@ -355,7 +358,7 @@ moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float*
                                              s)));
   MOE_TRY(hip_status(moe::launch_down_fp8(ffn_shape(d), h, offsets, fw, y_routed, y_shared,
                                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
-                                          s)));
+                                          s, true)));
   return combine_impl(d, y_routed, inv, gw, y_shared, out, s);
 }
 
@@ -474,7 +477,7 @@ moe_status moe_expert_ffn(const moe_dims* dims, const uint16_t* x, const int32_t
   const hipStream_t s = (hipStream_t)stream;
   uint16_t* h = at<uint16_t>(ws, layout(d).h);
   MOE_TRY(gate_up_impl(d, x, perm_rows, offsets, w1, w3, ws1, ws3, h, ws, s));
-  return down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s);
+  return down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s, true);
 }
 
 moe_status moe_combine(const moe_dims* dims, const float* y_routed, const int32_t* inv_perm,
@@ -547,7 +550,8 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
   const FfnShape rsh{T, L, d.n_experts, d.top_k, d.d_expert, false};
   MOE_TRY(hip_status(moe::launch_gate_up(rsh, lat, perm, offsets, w1, w3, nullptr, nullptr, h,
                                          tiles, ntiles, s)));
-  MOE_TRY(hip_status(moe::launch_down(rsh, h, offsets, w2, nullptr, y, nullptr, tiles, ntiles, s)));
+  MOE_TRY(hip_status(
+      moe::launch_down(rsh, h, offsets, w2, nullptr, y, nullptr, tiles, ntiles, s, true)));
   // gate-weighted sum over the slots, RMSNorm (eps from the config), bf16
   MOE_TRY(hip_status(moe::launch_combine_rmsnorm(y, inv, w, uhat, T, L, d.top_k, 1e-6f, s)));
   if (has_shared(d)) {
@@ -558,7 +562,7 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
     MOE_TRY(hip_status(moe::launch_gate_up(ssh, x, nullptr, nullptr, nullptr, nullptr, ws1, ws3,
                                            hs, tiles, ntiles, s)));
     MOE_TRY(hip_status(moe::launch_down(ssh, hs, nullptr, nullptr, ws2, nullptr, ys, tiles, ntiles,
-                                        s)));
+                                        s, true)));
     // up-projection with the shared output added before the one bf16 rounding
     return hip_status(moe::launch_dense(uhat, T, L, w_up, d.d_model, moe::DenseOut::kAddBF16,
                                         nullptr, out, ys, tiles, ntiles, s));

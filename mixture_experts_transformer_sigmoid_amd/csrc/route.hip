@@ -51,11 +51,15 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 #endif
 constexpr int kRouterKU = MOE_ROUTER_KU;   // k-steps of loads issued before their MFMAs
 
-__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  hi = f32_to_bf16(w);
-  const float r1 = w - bf16_to_f32(hi);
-  mid = f32_to_bf16(r1);
-  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+// The split of two weights at once, each part a packed bf16 pair (first weight in bits
+// 0..15), on the hardware round-to-nearest-even conversion (two values per instruction;
+// the same rounding as f32_to_bf16).  Each remainder is exact in fp32.
+__device__ __forceinline__ void split3x2(float a, float b, uint32_t& H, uint32_t& M,
+                                         uint32_t& L) {
+  H = pack_bf16x2(a, b);
+  const float ra = a - __uint_as_float(H << 16), rb = b - __uint_as_float(H & 0xffff0000u);
+  M = pack_bf16x2(ra, rb);
+  L = pack_bf16x2(ra - __uint_as_float(M << 16), rb - __uint_as_float(M & 0xffff0000u));
 }
 
 __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
@@ -77,18 +81,15 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   f32x4_t acc[3] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f},
                     f32x4_t{0.f, 0.f, 0.f, 0.f}};
   auto step = [&](const u32x4_t (&wv)[2], u32x4_t xv) {
-    uint32_t h[8], m[8], l[8];
+    uint32_t h[4], m[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      split3(__uint_as_float(wv[0][i]), h[i], m[i], l[i]);
-      split3(__uint_as_float(wv[1][i]), h[4 + i], m[4 + i], l[4 + i]);
+      const u32x4_t& w = wv[i >> 1];
+      split3x2(__uint_as_float(w[2 * (i & 1)]), __uint_as_float(w[2 * (i & 1) + 1]), h[i], m[i],
+               l[i]);
     }
-    const u32x4_t H = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                       h[6] | (h[7] << 16)};
-    const u32x4_t Mv = {m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16),
-                        m[6] | (m[7] << 16)};
-    const u32x4_t Lv = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                        l[6] | (l[7] << 16)};
+    const u32x4_t H = {h[0], h[1], h[2], h[3]}, Mv = {m[0], m[1], m[2], m[3]},
+                  Lv = {l[0], l[1], l[2], l[3]};
     acc[0] = mfma16x16x32(H, xv, acc[0]);
     acc[1] = mfma16x16x32(Mv, xv, acc[1]);
     acc[2] = mfma16x16x32(Lv, xv, acc[2]);
