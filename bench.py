@@ -8,8 +8,9 @@ synthetic, K2 shape: d 7168, 384 experts, top-8, I 2048, one shared expert, bf16
 weights, fp32 router) are resident in HBM before the timed region.  Prints one JSON
 line: whole-layer tokens/s for the main workload (128-token decode by default), the
 roofline of the dominant kernel (the gate/up grouped GEMM) timed with HIP events on
-the stream it runs on, the 8192-token prefill figure, and the CPU oracle timed on a
-bounded sample on the host cores.
+the stream it runs on, the 8192-token prefill figure, the 4096-token skewed-routing figure,
+the block, FP8-weight and latent variants, measured ceilings (read-only stream, copy,
+vendor GEMM), and the CPU oracle timed on a bounded sample on the host cores.
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "K2 MoE-layer tokens/s (128 & 8192 tok, bf16); % of HBM / MFMA peak"
 # the gate/up kernel each workload runs (decode: a few rows per expert; prefill: many)
-GATEUP_KERNEL = {"k2_decode": "ffn_skinny_kernel<2, 8, 0>", "k2_prefill": "ffn_lds_kernel<0>"}
+GATEUP_KERNEL = {"k2_decode": "ffn_skinny_kernel<1, 16, 0>", "k2_prefill": "ffn_lds_kernel<0>"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
@@ -34,6 +35,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_transformer_sigmoid_amd", "csrc", f)
                   for f in ("ffn.hip", "grouped.h", "common.h")]
 COPY_BYTES = 1 << 30
+READ_BYTES = 4 << 30
 
 
 def kernel_source_hash():
@@ -101,6 +103,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latent", action="store_true", help="skip the latent-MoE figure")
+    ap.add_argument("--no-skew", action="store_true", help="skip the skewed-routing figure")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight figures")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the fused norm + residual block figure")
@@ -335,6 +338,11 @@ def measure_ceilings(torch, dev):
     dst = torch.empty_like(src)
     copy_ms = timed(lambda: dst.copy_(src), 5)
     del src, dst
+    # read-only stream: row sums of a 4 GiB fp32 array (65,536 rows of 64 KiB), 256 KiB
+    # written; the fastest of torch's reductions on this part
+    rd = torch.full((READ_BYTES // 4,), 1.0, dtype=torch.float32, device=dev).view(65536, -1)
+    read_ms = timed(lambda: rd.sum(dim=1), 5)
+    del rd
     n = 8192
     g = torch.Generator(device=dev)
     g.manual_seed(0)
@@ -348,9 +356,11 @@ def measure_ceilings(torch, dev):
     torch.cuda.empty_cache()
     flops = 2.0 * n ** 3
     return {"hbm_copy_gbs": 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9,
+            "hbm_read_gbs": READ_BYTES / (read_ms * 1e-3) / 1e9,
             "mfma_bf16_random_tflops": flops / (rand_ms * 1e-3) / 1e12,
             "mfma_bf16_zeros_tflops": flops / (zero_ms * 1e-3) / 1e12,
-            "how": "1 GiB device-to-device copy (bytes read + written); torch.matmul "
+            "how": "1 GiB device-to-device copy (bytes read + written); row sums of a 4 GiB "
+                   "fp32 array (bytes read); torch.matmul "
                    "(hipBLASLt) 8192x8192x8192 bf16, N(0,1) operands and all-zero operands"}
 
 
@@ -554,6 +564,31 @@ def main():
             f"{ptf:.0f} TFLOP/s ({100 * ptf / MFMA_BF16_PEAK_TFLOPS:.1f}% MFMA)")
         del pws, pin
 
+    if not args.no_skew and args.workload != "k2_skew":
+        scfg = S.CONFIGS["k2_skew"]
+        sin = dict(weights)
+        sin.update(S.make_activations(scfg, dev))
+        sdims = M.dims_for(scfg)
+        sws = M.workspace(sdims, dev)
+        sout = torch.empty(scfg["tokens"], scfg["d_model"], dtype=torch.bfloat16, device=dev)
+        log("timing moe_forward, k2_skew, T=4096")
+        ssteps = max(3, min(args.steps, 10))
+        sms, _ = time_forward(M, torch, sdims, sin, sout, sws, ssteps, 1)
+        sst = split_state(M, torch, sdims, sin, sws)
+        cnt = sst["counts"].to("cpu")
+        sact = int((cnt > 0).sum())
+        salg = algorithmic(scfg, sact, scfg["tokens"])
+        stf = salg["layer_flops"] / (sms * 1e-3) / 1e12
+        res["skew"] = {"workload": "k2_skew: T=4096, same layer, selection bias -0.5 ln(rank) over a "
+                                   "seeded ranking of the experts (most tokens on ~20 experts)",
+                       "steps": ssteps, "ms_per_step": sms, "tokens_per_s": scfg["tokens"] / (sms * 1e-3),
+                       "mfma_tflops": stf, "mfma_frac": stf / MFMA_BF16_PEAK_TFLOPS,
+                       "active_experts": sact, "max_rows_per_expert": int(cnt.max()),
+                       "hbm_gbs": salg["layer_bytes"] / (sms * 1e-3) / 1e9}
+        log(f"skew: {sms:.3f} ms/step, {res['skew']['tokens_per_s']:.0f} tok/s, {stf:.0f} TFLOP/s, "
+            f"{sact} active experts, up to {int(cnt.max())} rows")
+        del sws, sin, sout
+
     if not args.no_fp8:
         log("timing moe_forward_fp8 (FP8 block-scaled expert weights)")
         fres = time_fp8(M, torch, S, dev, {"x": inp["x"], "b": inp["b"]}, args.steps,
@@ -572,9 +607,11 @@ def main():
         ceil = measure_ceilings(torch, dev)
         res["ceilings"] = ceil
         rt = ceil["mfma_bf16_random_tflops"]
-        if "prefill" in res:
-            res["prefill"]["mfma_frac_of_measured_random"] = res["prefill"]["mfma_tflops"] / rt
-        log(f"ceilings: copy {ceil['hbm_copy_gbs']:.0f} GB/s; vendor GEMM bf16 {rt:.0f} TFLOP/s "
+        res["roofline"]["frac_of_measured_read"] = res["roofline"]["achieved"] / ceil["hbm_read_gbs"]
+        for leg in ("prefill", "skew"):
+            if leg in res:
+                res[leg]["mfma_frac_of_measured_random"] = res[leg]["mfma_tflops"] / rt
+        log(f"ceilings: copy {ceil['hbm_copy_gbs']:.0f} GB/s, read {ceil['hbm_read_gbs']:.0f} GB/s; vendor GEMM bf16 {rt:.0f} TFLOP/s "
             f"(random), {ceil['mfma_bf16_zeros_tflops']:.0f} TFLOP/s (zeros)")
     if not args.no_latent:
         # latent variant (experts on a 3584-wide latent), 4096 tokens; its own weights
