@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // accumulates the three partial logits in three fp32 accumulators.  K is cut into
 // kRouterKSplit slices (grid z) so that the launch fills the chip; every (slice, part)
 // pair writes its own partial, and the selection kernel adds the 3 * kRouterKSplit
-// partials of a logit in fp64, in a fixed order.
+// partials of a logit in fp64, in a fixed order (slice by slice, hi, mid, lo).
 // Block: 4 waves; wave w owns experts n0 + 16 w .. + 15 (one MFMA fragment), the block
 // 16 rows (tokens).  Lane (r, q): expert n0 + 16 w + r, token t0 + r, k 8q .. 8q + 7 of
 // each 32-wide step; weights are the MFMA's A operand, tokens its B operand.
@@ -125,21 +125,6 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
       const int ee = n0 + 4 * q + i;
       if (ee < E) zrow[(3 * kz + p) * (int64_t)E + ee] = acc[p][i];
     }
-}
-
-// Sum of the np partial logits of every (token, expert) in fp64, in slice order, rounded
-// once to fp32: the selection then reads one value per logit.  z_part rows are [np][E];
-// the sum goes to part 0 of the row.
-__global__ __launch_bounds__(256) void router_reduce_kernel(float* __restrict__ z_part,
-                                                            int64_t T, int E, int np) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * E) return;
-  const int64_t t = i / E;
-  const int e = (int)(i - t * E);
-  float* row = z_part + t * (int64_t)np * E;
-  double z = 0.0;
-  for (int p = 0; p < np; ++p) z += (double)row[(int64_t)p * E + e];
-  row[e] = (float)z;
 }
 
 // ---------------------------------------------------------------- top-k + gates
@@ -257,15 +242,9 @@ hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias,
     hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, x, w_r, T, d, E, z_part);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // every thread reads its logit's partials before writing part 0 of the same logit,
-    // and no other thread touches that logit: the in-place sum is race-free
-    const int64_t n = T * E;
-    hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       z_part, T, E, 3 * kRouterKSplit);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    // the selection reads rows of 3 * kRouterKSplit parts, of which part 0 is the sum
-    np = 1;
+    // the selection adds the 3 * kRouterKSplit partials of each logit in fp64, slice by
+    // slice
+    np = 3 * kRouterKSplit;
     row_parts = 3 * kRouterKSplit;
   } else {
     const int64_t n = (int64_t)E * d;
