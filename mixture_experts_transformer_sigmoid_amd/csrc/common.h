@@ -122,8 +122,30 @@ constexpr int64_t kRouterSmallT = 512;
 #define MOE_ROUTER_KSPLIT 8
 #endif
 constexpr int kRouterKSplit = MOE_ROUTER_KSPLIT;
-inline int64_t router_zpart_floats(int64_t T, int E) {
-  return T * 3 * E * (T <= kRouterSmallT ? kRouterKSplit : 1);
+// Above kRouterSmallT tokens the logits GEMM runs on the 256-row kernel, one workgroup per
+// 256 tokens x 256 outputs: 160 workgroups at 8,192 tokens and E = 384, 80 at 4,096, for
+// 256 CUs.  K is then cut into S slices, each writing its own partial logits, with S the
+// smallest that minimises (rounds of workgroups) / S + S / 20: the second term stands
+// for each slice's fixed cost (its pipeline fill and its partial output).  S = 3 for
+// 8,192 and 4,096 tokens at K2 width.
+inline int router_ksplit(int64_t T, int E, int d) {
+  if (T <= kRouterSmallT) return 1;
+  const int64_t wgs = ((T + 255) / 256) * ((3 * (int64_t)E + 255) / 256);
+  const int chunks = d / 64;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sl = 1; sl <= 8 && sl <= chunks; ++sl) {
+    const double rounds = (double)((wgs * sl + 255) / 256);
+    const double cost = rounds / sl + sl / 20.0;
+    if (cost < best_cost - 1e-12) {
+      best_cost = cost;
+      best = sl;
+    }
+  }
+  return best;
+}
+inline int64_t router_zpart_floats(int64_t T, int E, int d) {
+  return T * 3 * E * (T <= kRouterSmallT ? kRouterKSplit : router_ksplit(T, E, d));
 }
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
                          int E, int k, float alpha, uint16_t* w_split, float* z_part,
@@ -148,10 +170,13 @@ int64_t ffn_max_tiles(const FfnShape& sh);
 
 // Dense C[rows, N] = A[rows, K] . W[N, K]^T with the grouped-GEMM kernels (one group):
 // fp32 into Cf; bf16 into Cb; or bf16(C + R) into Cb with R [rows, N] fp32.
+// ksplit > 1 (fp32 output, more than 512 rows only): K is cut into ksplit slices of whole
+// 64-k chunks, and slice j writes its partial product to columns j N .. j N + N - 1 of
+// Cf [rows, ksplit N].
 enum class DenseOut { kF32, kBF16, kAddBF16 };
 hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
                         DenseOut mode, float* Cf, uint16_t* Cb, const float* R, Tile* tiles,
-                        int32_t* ntiles, hipStream_t s);
+                        int32_t* ntiles, hipStream_t s, int ksplit = 1);
 
 hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,

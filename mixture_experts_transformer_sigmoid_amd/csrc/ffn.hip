@@ -270,7 +270,8 @@ struct LdsBufs {
 // loop, then the epilogue.  Every wave runs the same loads and barriers whatever its NF.
 template <int EPI, int NF>
 __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, const LdsBufs& b,
-                                         int wave, int arow, const Tile& tile, int nbase) {
+                                         int wave, int arow, const Tile& tile, int nbase,
+                                         int col0) {
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int NA = NF > 0 ? NF : 1;
   f32x16_t acc[NA][4];
@@ -302,7 +303,8 @@ __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, cons
   // land, and every wave finish its last operand reads, before the buffers are reused
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
-  if constexpr (NF > 0) lds_epilogue<EPI, NF>(a, b.A + wave * 1024, acc, arow, 64, tile, nbase);
+  if constexpr (NF > 0)
+    lds_epilogue<EPI, NF>(a, b.A + wave * 1024, acc, arow, 64, tile, nbase, col0);
 }
 
 template <int EPI>
@@ -315,9 +317,12 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   __shared__ __attribute__((aligned(1024))) u32x4_t W1[BM * 8];
   __shared__ __attribute__((aligned(1024))) u32x4_t W2[BM * 8];
 
+  // fp32 output only: K cut into ksplit slices, the slices of one n-block adjacent
+  const int nks = (EPI == kF32 && a.ksplit > 1) ? a.ksplit : 1;
   Tile tile;
-  int nb;
-  if (!map_work(a, (a.N + FEAT - 1) / FEAT, tile, nb)) return;
+  int nbk;
+  if (!map_work(a, ((a.N + FEAT - 1) / FEAT) * nks, tile, nbk)) return;
+  const int nb = nbk / nks, ks = nbk - nb * nks;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -330,6 +335,12 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   const int64_t wofs = (int64_t)tile.group * N * K;
   const uint16_t* Wa = is_shared ? a.S1 : a.B1 + wofs;
   const uint16_t* Wb = GATEUP ? (is_shared ? a.S3 : a.B3 + wofs) : Wa;
+
+  // this slice's chunks c0 .. c1 - 1 of K: its byte offset goes into every row's
+  // starting offset (rows past the tile or the matrix keep theirs, past the buffer end)
+  const int nct = K / kLdsChunkK;
+  const int c0 = nct * ks / nks, c1 = nct * (ks + 1) / nks;
+  const uint32_t kofs = (uint32_t)c0 * (kLdsChunkK * 2);
 
   LdsCtx x;
   // one weight matrix is N*K*2 < 2^32 bytes, and so is x (checked on the host)
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
     const int piece = (lane & 7) ^ (m & 7) ^ (u & 1);
     const int64_t p = tile.row_begin + m;
     x.aoff[j] = p < tile.row_end
-                    ? (uint32_t)(act_row(a, GATEUP, p) - abase) * 2u + piece * 16
+                    ? (uint32_t)(act_row(a, GATEUP, p) - abase) * 2u + piece * 16 + kofs
                     : abytes;
   }
   // weight row m of the workgroup: gate/up rows 0..127 are W1 features f0 + m, rows
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
     const int n0 = f0 + 64 * (GATEUP ? (wave & 1) : wave) + (lane >> 3);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      x.woff[e] = (uint32_t)n0 * (uint32_t)K * 2u + ((lane & 7) ^ (lane >> 3) ^ e) * 16;
+      x.woff[e] = (uint32_t)n0 * (uint32_t)K * 2u + ((lane & 7) ^ (lane >> 3) ^ e) * 16 + kofs;
     x.wstride = 8u * (uint32_t)K * 2u;
   }
   // the two row halves interleave 32-row fragments (wave wm: tile rows 64 t + 32 wm ..),
@@ -377,7 +388,7 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
       x.ard[kk] = arow * 8 + rd;
     }
   }
-  x.nc = K / kLdsChunkK;
+  x.nc = c1 - c0;
   // both buffers are under 2 GiB (checked on the host), so offset + this stays in 32 bits
   x.aoob = abytes;
   x.woob = wbytes;
@@ -387,12 +398,13 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   // live 32-row fragments of this wave's half of the tile (wave-uniform)
   const int nf = min(4, max(0, (nrows - arow + 63) / 64));
   const LdsBufs bufs{Ab, W0, W1, W2};
+  const int col0 = ks * N;  // this slice's columns in a row of Ys
   switch (nf) {
-    case 0: lds_tile<EPI, 0>(a, x, bufs, wave, arow, tile, nbase); break;
-    case 1: lds_tile<EPI, 1>(a, x, bufs, wave, arow, tile, nbase); break;
-    case 2: lds_tile<EPI, 2>(a, x, bufs, wave, arow, tile, nbase); break;
-    case 3: lds_tile<EPI, 3>(a, x, bufs, wave, arow, tile, nbase); break;
-    default: lds_tile<EPI, 4>(a, x, bufs, wave, arow, tile, nbase); break;
+    case 0: lds_tile<EPI, 0>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 1: lds_tile<EPI, 1>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 2: lds_tile<EPI, 2>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 3: lds_tile<EPI, 3>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    default: lds_tile<EPI, 4>(a, x, bufs, wave, arow, tile, nbase, col0); break;
   }
 }
 
@@ -408,7 +420,7 @@ void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a) {
 
 hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
                         DenseOut mode, float* Cf, uint16_t* Cb, const float* R, Tile* tiles,
-                        int32_t* ntiles, hipStream_t s) {
+                        int32_t* ntiles, hipStream_t s, int ksplit) {
   // one group (the "shared" slot of the tile list) whose rows are all the rows of A
   const FfnShape sh{rows, K, 0, 0, N, true};
   const bool wide = rows > 512;
@@ -429,11 +441,17 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
   a.N = N;
   a.K = K;
   a.E = 0;
+  // K slices only on the 256-row kernel's fp32 output, each at least one 64-k chunk
+  const int nks = (mode == DenseOut::kF32 && wide && ksplit > 1)
+                      ? (ksplit < K / kLdsChunkK ? ksplit : K / kLdsChunkK)
+                      : 1;
+  a.ksplit = nks;
+  a.ldc = nks * N;
   const dim3 gs = grid_for(sh, BM, kWideBNDown, N), gk = grid_for(sh, BM, 64, N),
              gk2 = grid_for(sh, BM, 128, N);
   switch (mode) {
     case DenseOut::kF32:
-      if (wide) launch_wide<kF32>(gs, s, a);
+      if (wide) launch_wide<kF32>(dim3(gs.x * nks), s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, kF32>), gk, dim3(256), 0, s, a);
       break;
     case DenseOut::kBF16:

@@ -32,6 +32,8 @@ struct FfnArgs {
   const int32_t* ntiles;
   int32_t k;              // slots per token (gate/up gather: token = slot / k)
   int32_t N, K, E;
+  int32_t ksplit;         // 256-row kernel, fp32 output: K slices (0 or 1: none)
+  int32_t ldc;            // row stride of Ys (0: N); slice j writes from column j N
   int64_t a_rows;         // rows of A (gate/up: tokens of x)
   const float* R;         // kAddBF16: fp32 rows added before the bf16 store
   // FP8 kernels only: E4M3 codes with the layouts of B1, B3, S1, S3, and their fp32
@@ -191,12 +193,13 @@ __device__ __forceinline__ void store_gateup(uint16_t* dst, f32x4_t g, f32x4_t u
 // time and features >= N are dropped (they would land on the next row).
 template <int EPI>
 __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x4_t v,
-                                       f32x4_t u) {
+                                       f32x4_t u, int col0 = 0) {
   const int N = a.N;
   if (EPI == kSwiGLU) {
     store_gateup(a.C + p * N + nn, v, u);
   } else if (EPI == kF32) {
-    float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
+    float* yrow = p < a.routed_rows ? a.Y + p * N
+                                    : a.Ys + (p - a.routed_rows) * (a.ldc ? a.ldc : N) + col0;
     if ((N & 3) == 0) {
       *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
     } else {
@@ -226,10 +229,12 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
 // r (FW / 4) + (p ^ (r & 7)), so the 8 lanes that the LDS serves together (8 rows, one
 // piece, on the write side; one row, 8 pieces, on the read side) hit distinct banks.
 template <int EPI>
-__device__ __forceinline__ void store_row4(const FfnArgs& a, int64_t p, int nn, f32x4_t v) {
+__device__ __forceinline__ void store_row4(const FfnArgs& a, int64_t p, int nn, f32x4_t v,
+                                           int col0) {
   const int N = a.N;
   if constexpr (EPI == kF32) {
-    float* yrow = p < a.routed_rows ? a.Y + p * N : a.Ys + (p - a.routed_rows) * N;
+    float* yrow = p < a.routed_rows ? a.Y + p * N
+                                    : a.Ys + (p - a.routed_rows) * (a.ldc ? a.ldc : N) + col0;
     *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
   } else {
     if constexpr (EPI == kAddBF16) v += *reinterpret_cast<const f32x4_t*>(a.R + p * N + nn);
@@ -240,10 +245,12 @@ __device__ __forceinline__ void store_row4(const FfnArgs& a, int64_t p, int nn, 
   }
 }
 
+// col0: first column of this workgroup's K slice in a row of Ys (fp32 output only).
 template <int EPI, int NF>
 __device__ __forceinline__ void lds_epilogue(const FfnArgs& a, u32x4_t* stage,
                                              const f32x16_t (&acc)[NF][4], int arow,
-                                             int tstride, const Tile& tile, int nbase) {
+                                             int tstride, const Tile& tile, int nbase,
+                                             int col0 = 0) {
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int FO = GATEUP ? 2 : 4;  // 32-output fragments per row
   constexpr int PPR = 8 * FO;         // 16-byte pieces per staged row
@@ -263,7 +270,8 @@ __device__ __forceinline__ void lds_epilogue(const FfnArgs& a, u32x4_t* stage,
           const int nn = nbase + 32 * oo + 8 * q + 4 * hl;
           const f32x16_t& g = acc[t][oo];
           store4<EPI>(a, tile.row_begin + m, nn,
-                      f32x4_t{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]}, f32x4_t{});
+                      f32x4_t{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]}, f32x4_t{},
+                      col0);
         }
     }
     return;
@@ -295,7 +303,7 @@ __device__ __forceinline__ void lds_epilogue(const FfnArgs& a, u32x4_t* stage,
       const int m = arow + tstride * t + r;
       const int nn = nbase + 4 * pr;
       if (m < nrows && nn < a.N)
-        store_row4<GATEUP ? kBF16 : EPI>(a, tile.row_begin + m, nn, v);
+        store_row4<GATEUP ? kBF16 : EPI>(a, tile.row_begin + m, nn, v, col0);
     }
   }
 }

@@ -67,7 +67,7 @@ Layout layout(const moe_dims& d) {
     off += align_up(bytes);
     return o;
   };
-  L.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts) * 4);
+  L.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
   L.wsplit = take(3 * E * (size_t)d.d_model * 2);
   L.idx = take(slots * 4);
   L.w = take(slots * 4);
@@ -192,7 +192,7 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
     off += align_up(bytes);
     return o;
   };
-  P.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts) * 4);
+  P.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
   P.wsplit = take(3 * E * (size_t)d.d_model * 2);
   P.idx = take(slots * 4);
   P.w = take(slots * 4);

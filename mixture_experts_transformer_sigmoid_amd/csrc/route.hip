@@ -253,11 +253,14 @@ hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias,
                        w_split);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
+    // K cut into S slices (router_ksplit): every token's row holds S x (hi, mid, lo)
+    // partial logits, which the selection adds in fp64 in that order
+    const int S = router_ksplit(T, E, d);
     err = launch_dense(x, T, d, w_split, 3 * E, DenseOut::kF32, z_part, nullptr, nullptr, tiles,
-                       ntiles, s);
+                       ntiles, s, S);
     if (err != hipSuccess) return err;
-    np = 3;
-    row_parts = 3;
+    np = 3 * S;
+    row_parts = 3 * S;
   }
   const int epl = (E + 63) / 64;
   if (epl <= 1)
