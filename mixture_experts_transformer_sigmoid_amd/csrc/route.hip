@@ -145,14 +145,32 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   if (t >= T) return;
   const float* zp = z_part + t * (int64_t)row_parts * E;
 
+  // the np partial logits of each expert, added in fp64 in part order.  Loads of 8 parts
+  // are issued together: every load reads an in-range element (part and expert clamped)
+  // and the out-of-range ones are dropped afterwards, so that no load sits behind a branch
+  // (a guarded load compiles to a branch and a wait per load)
+  double zd[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) zd[i] = 0.0;
+  for (int p0 = 0; p0 < np; p0 += 8) {
+    float v[8][EPL];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        v[j][i] = zp[min(p0 + j, np - 1) * E + min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        zd[i] += (p0 + j < np) ? (double)v[j][i] : 0.0;
+  }
   float score[EPL], sig[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      double zd = 0.0;
-      for (int p = 0; p < np; ++p) zd += (double)zp[p * E + e];
-      const float z = (float)zd;
+      const float z = (float)zd[i];
       if (logits != nullptr) logits[t * E + e] = z;
       const float s = 1.0f / (1.0f + expf(-z));
       float v = s + bias[e];
