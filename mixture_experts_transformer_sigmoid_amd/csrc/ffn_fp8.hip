@@ -382,7 +382,26 @@ __global__ __launch_bounds__(512, 1) void ffn_stream_fp8_kernel(const FfnArgs a)
   }
 }
 
-constexpr int kSkinnyF8KB = 2;
+// Skinny FP8 shapes (NF 16-feature fragments per wave, KB 128-k blocks per load batch).
+// A sweep at K2 decode on one box (gate/up, ms): 2x2 1.88, 1x4 1.94, 2x3 1.87, 2x4 2.09,
+// 4x2 1.95, 4x1 1.83, 8x1 2.00 (2x4, 4x2 and 8x1 spill).  Down with gate/up 4x1, the layer:
+// 2x2 2.83, 4x1 2.78, 4x2 2.79, 8x1 2.79, 2x4 2.84, 1x4 3.05.
+#ifndef MOE_F8_GU_NF
+#define MOE_F8_GU_NF 4
+#endif
+#ifndef MOE_F8_GU_KB
+#define MOE_F8_GU_KB 1
+#endif
+constexpr int kSkinnyF8GuNF = MOE_F8_GU_NF;
+constexpr int kSkinnyF8GuKB = MOE_F8_GU_KB;
+#ifndef MOE_F8_DN_NF
+#define MOE_F8_DN_NF 4
+#endif
+#ifndef MOE_F8_DN_KB
+#define MOE_F8_DN_KB 1
+#endif
+constexpr int kSkinnyF8DnNF = MOE_F8_DN_NF;
+constexpr int kSkinnyF8DnKB = MOE_F8_DN_KB;
 
 FfnArgs fp8_args(const FfnShape& sh, const Fp8Weights& w, bool gateup, Tile* tiles,
                  int32_t* ntiles) {
@@ -423,8 +442,8 @@ hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32
     hipLaunchKernelGGL(ffn_stream_fp8_kernel<kSwiGLU>, grid_for(sh, BM, kWideBNGateUp, a.N),
                        dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((ffn_skinny_fp8_kernel<kSkinnyNF, kSkinnyF8KB, kSwiGLU>),
-                       grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_skinny_fp8_kernel<kSkinnyF8GuNF, kSkinnyF8GuKB, kSwiGLU>),
+                       grid_for(sh, BM, 64 * kSkinnyF8GuNF, a.N), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -448,8 +467,8 @@ hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t*
     hipLaunchKernelGGL(ffn_stream_fp8_kernel<kF32>, grid_for(sh, BM, kWideBNDown, a.N),
                        dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((ffn_skinny_fp8_kernel<kSkinnyNF, kSkinnyF8KB, kF32>),
-                       grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_skinny_fp8_kernel<kSkinnyF8DnNF, kSkinnyF8DnKB, kF32>),
+                       grid_for(sh, BM, 64 * kSkinnyF8DnNF, a.N), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
