@@ -466,7 +466,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              "(the layer is measured on one GPU; see DESIGN.md for how it would shard)",
+              "(the layer is measured on one GPU's share; across GPUs it would shard by expert "
+              "parallelism, which is not built)",
               file=sys.stderr)
         sys.exit(2)
     import torch

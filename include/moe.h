@@ -31,7 +31,7 @@
  *   - Every output is fully overwritten.  tokens == 0 is a valid no-op.
  *   - Errors are status codes, checked on the host BEFORE anything is launched:
  *       MOE_EINVAL       null / misaligned (16 B) pointer, impossible dims
- *       MOE_EUNSUPPORTED dims this build does not handle (d, I not multiples of 64,
+ *       MOE_EUNSUPPORTED dims this library does not handle (d, I not multiples of 64,
  *                        top_k > 8, E > 1024, Is not 0 or I, x or one weight matrix
  *                        of 2 GiB or more, T above 2^23)
  *       MOE_EWORKSPACE   ws_bytes smaller than moe_workspace_bytes()

@@ -393,7 +393,7 @@ const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";
     case MOE_EINVAL: return "MOE_EINVAL: invalid argument (null or misaligned pointer, bad dims)";
-    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: dims not handled by this build";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: dims this library does not handle";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace smaller than moe_workspace_bytes()";
     case MOE_EHIP: return "MOE_EHIP: HIP launch error";
     default: return "unknown moe_status";

@@ -24,7 +24,7 @@ Sources (the pages this follows; cited by page title and the part of the page):
   group the (token, slot) pairs by expert, run each expert on its group, put the
   outputs back in slot order and take the weighted sum over the k slots in fp32.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * Weights are stored [out, in] (the K3 page states this for its projection); so
   ``w_r`` is [E, d], ``w1``/``w3`` are [E, I, d], ``w2`` is [E, d, I].
