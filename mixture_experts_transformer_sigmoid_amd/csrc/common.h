@@ -114,7 +114,8 @@ struct Tile {
   int32_t pad[3];
 };
 
-// Router: w_split [3E, d] bf16 and z_part (router_zpart_floats) fp32 are workspace;
+// Router: w_split [3 router_part_rows(E), d] bf16 and z_part (router_zpart_floats) fp32
+// are workspace;
 // logits may be null.  Up to kRouterSmallT tokens take the K-sliced small kernel, whose
 // partial logits need kRouterKSplit times the room.
 constexpr int64_t kRouterSmallT = 512;
@@ -122,6 +123,9 @@ constexpr int64_t kRouterSmallT = 512;
 #define MOE_ROUTER_KSPLIT 8
 #endif
 constexpr int kRouterKSplit = MOE_ROUTER_KSPLIT;
+// Rows per part (hi, mid, lo) of the split router weights and of the partial logits the
+// 256-row kernel writes: E rounded up to a multiple of 4 (the padding rows are zero).
+inline int router_part_rows(int E) { return (E + 3) / 4 * 4; }
 // Above kRouterSmallT tokens the logits GEMM runs on the 256-row kernel, one workgroup per
 // 256 tokens x 256 outputs: 160 workgroups at 8,192 tokens and E = 384, 80 at 4,096, for
 // 256 CUs.  K is then cut into S slices, each writing its own partial logits, with S the
@@ -130,7 +134,7 @@ constexpr int kRouterKSplit = MOE_ROUTER_KSPLIT;
 // 8,192 and 4,096 tokens at K2 width.
 inline int router_ksplit(int64_t T, int E, int d) {
   if (T <= kRouterSmallT) return 1;
-  const int64_t wgs = ((T + 255) / 256) * ((3 * (int64_t)E + 255) / 256);
+  const int64_t wgs = ((T + 255) / 256) * ((3 * (int64_t)router_part_rows(E) + 255) / 256);
   const int chunks = d / 64;
   int best = 1;
   double best_cost = 1e30;
@@ -145,7 +149,8 @@ inline int router_ksplit(int64_t T, int E, int d) {
   return best;
 }
 inline int64_t router_zpart_floats(int64_t T, int E, int d) {
-  return T * 3 * E * (T <= kRouterSmallT ? kRouterKSplit : router_ksplit(T, E, d));
+  return T <= kRouterSmallT ? T * 3 * E * kRouterKSplit
+                            : T * 3 * router_part_rows(E) * router_ksplit(T, E, d);
 }
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
                          int E, int k, float alpha, uint16_t* w_split, float* z_part,

@@ -126,14 +126,15 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
 // the prefill GEMMs run at the power limit, and both choices cut the energy per flop.
 //
 // K goes in chunks of 64.  Per chunk a workgroup moves 32 KiB of weights and 32 KiB of
-// activations (gate/up: rows of x gathered through perm), 8 rows x 128 contiguous bytes
-// per wave-wide 16-byte-per-lane load:
-//   - weights go from HBM straight into LDS (buffer loads that write LDS), three chunk
-//     buffers, requested two chunks ahead;
-//   - activations (mostly L2 hits) go through registers into two LDS chunk buffers,
-//     requested one chunk ahead.
-// 160 KiB of LDS in all.  Loads retire in order, so once a wave has its activation
-// registers for chunk c + 1 its weight transfers for chunk c + 1 have landed too.
+// activations (gate/up: rows of x gathered through perm, each lane's offset naming its
+// row), 8 rows x 128 contiguous bytes per wave-wide 16-byte-per-lane transfer, all of them
+// straight into LDS (buffer loads that write LDS, no registers):
+//   - weights from HBM, three chunk buffers, requested two chunks ahead;
+//   - activations (mostly L2 hits), two chunk buffers, requested one chunk ahead, at the
+//     start of the chunk before.
+// 160 KiB of LDS in all, five separate arrays.  Against activations staged through
+// registers this took the prefill layer from 8.70-8.79 to 8.59-8.60 ms and the skewed
+// 4,096-token layer from 3.33-3.36 to 3.19-3.20 ms (one box, alternating runs).
 //
 // LDS layout of a chunk operand (256 rows x 8 pieces of 16 bytes): the 1 KiB unit u holds
 // rows 8u .. 8u+7; piece p of row m sits in slot 8 (m & 7) + (p ^ sigma(m)) of its unit,
@@ -157,58 +158,13 @@ struct LdsCtx {
   int nc;                      // chunks
 };
 
-// Whole-chunk moves, for the prologue: the wave's 8 weight transfers of chunk c (units
-// 8 wave .. 8 wave + 7), its 8 activation loads, and their store to LDS.
+// Whole-chunk weight move, for the prologue: the wave's 8 weight transfers of chunk c
+// (units 8 wave .. 8 wave + 7).
 __device__ __forceinline__ void lds_fetch_w(const LdsCtx& x, u32x4_t* wgt, int wave, int c) {
   const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.woob;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     dma16(x.wgt, wgt + (wave * 8 + j) * 64, x.woff[j & 1], soff + (uint32_t)j * x.wstride);
-}
-
-__device__ __forceinline__ void lds_load_a(const LdsCtx& x, u32x4_t (&ar)[8], int c) {
-  const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.aoob;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ar[j] = bload16(x.act, x.aoff[j], soff);
-}
-
-__device__ __forceinline__ void lds_store_a(u32x4_t* act, const u32x4_t (&ar)[8], int wave) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) act[(wave * 8 + j) * 64 + lane] = ar[j];
-}
-
-// Data movement of sub-step kk (of 4) of a chunk, spread so that no wave issues a burst
-// of loads (bursts from four waves at once fill the texture unit's queues and stall the
-// MFMA stream behind them): the activation pieces 2kk, 2kk+1 of the next chunk go from
-// registers to LDS, the same registers are refilled with the pieces of the chunk after it,
-// and the weight units 2kk, 2kk+1 of that chunk are requested (they land in LDS two chunks
-// ahead).  Loads past the last chunk read nothing.
-__device__ __forceinline__ void lds_move(const LdsCtx& x, u32x4_t* act_next, u32x4_t* wnext2,
-                                         u32x4_t (&ar)[8], int wave, int c2, int kk) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t asoff = c2 < x.nc ? (uint32_t)c2 * (kLdsChunkK * 2) : x.aoob;
-  const uint32_t wsoff = c2 < x.nc ? (uint32_t)c2 * (kLdsChunkK * 2) : x.woob;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int j = 2 * kk + e;
-    act_next[(wave * 8 + j) * 64 + lane] = ar[j];
-    ar[j] = bload16(x.act, x.aoff[j], asoff);
-  }
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int j = 2 * kk + e;
-    dma16(x.wgt, wnext2 + (wave * 8 + j) * 64, x.woff[j & 1], wsoff + (uint32_t)j * x.wstride);
-  }
-}
-
-// Every wave has stored the activations of this chunk and finished reading the buffers of
-// the previous one, and its weight transfers of this chunk have landed (only the 16 loads
-// issued during the previous chunk may still be in flight).
-__device__ __forceinline__ void lds_sync() {
-  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Sub-step kk reads weight fragment o at slot wrd[kk] + 8 wfrag_row(o) and row fragment t
@@ -221,32 +177,54 @@ __device__ __forceinline__ constexpr int wfrag_row(int o) {
   return GATEUP ? 128 * (o >> 1) + 32 * (o & 1) : 32 * o;
 }
 
-// Chunk c (weights in wcur): wait, then four sub-steps of 16 k, each moving its share of
-// the next chunks' data, then reading the operands of the following sub-step while its
-// own MFMAs run.
+// Chunk c reads activation buffer Acur and weight buffer Wcur; during it the activations
+// of chunk c + 1 go to Anext (sub-steps 0 and 1, four units each) and the weights of chunk
+// c + 2 to Wnext2 (sub-steps 2 and 3).  All buffers are separate LDS arrays, so the
+// compiler can tell which pending transfer an LDS read depends on.  At the barrier before chunk c + 1 only the 8 weight transfers of
+// chunk c + 2 may still be in flight: the activation transfers of chunk c + 1 were issued
+// before them, and transfers complete in order.
+__device__ __forceinline__ void lds_sync8() {
+  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void lds_fetch_a(const LdsCtx& x, u32x4_t* act, int wave, int c,
+                                            int j0) {
+  const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.aoob;
+#pragma unroll
+  for (int j = j0; j < j0 + 4; ++j) dma16(x.act, act + (wave * 8 + j) * 64, x.aoff[j], soff);
+}
+
+__device__ __forceinline__ void lds_fetch_w4(const LdsCtx& x, u32x4_t* wgt, int wave, int c,
+                                             int j0) {
+  const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.woob;
+#pragma unroll
+  for (int j = j0; j < j0 + 4; ++j)
+    dma16(x.wgt, wgt + (wave * 8 + j) * 64, x.woff[j & 1], soff + (uint32_t)j * x.wstride);
+}
+
 template <bool GATEUP, int NF>
-__device__ __forceinline__ void lds_chunk(const LdsCtx& x, u32x4_t* Ab, const u32x4_t* wcur,
-                                          u32x4_t* wnext2, u32x4_t (&ar)[8], int wave, int c,
-                                          f32x16_t (&acc)[NF > 0 ? NF : 1][4]) {
-  lds_sync();
-  const u32x4_t* act = Ab + (c & 1) * 2048;
-  u32x4_t* act_next = Ab + ((c + 1) & 1) * 2048;
+__device__ __forceinline__ void lds_chunk_dma(const LdsCtx& x, const u32x4_t* acur,
+                                              u32x4_t* anext, const u32x4_t* wcur,
+                                              u32x4_t* wnext2, int wave, int c,
+                                              f32x16_t (&acc)[NF > 0 ? NF : 1][4]) {
+  lds_sync8();
   constexpr int NA = NF > 0 ? NF : 1;
   u32x4_t wv[2][4], av[2][NA];
   auto read = [&](int kk, int b) {
 #pragma unroll
     for (int o = 0; o < 4; ++o) wv[b][o] = wcur[x.wrd[kk] + 8 * wfrag_row<GATEUP>(o)];
 #pragma unroll
-    for (int t = 0; t < NF; ++t) av[b][t] = act[x.ard[kk] + 512 * t];
+    for (int t = 0; t < NF; ++t) av[b][t] = acur[x.ard[kk] + 512 * t];
   };
   if constexpr (NF > 0) read(0, 0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    lds_move(x, act_next, wnext2, ar, wave, c + 2, kk);
+    if (kk < 2) lds_fetch_a(x, anext, wave, c + 1, 4 * kk);
+    else lds_fetch_w4(x, wnext2, wave, c + 2, 4 * (kk - 2));
     if constexpr (NF > 0) {
       if (kk < 3) read(kk + 1, (kk + 1) & 1);
-      // keep this sub-step's data movement and the next sub-step's reads ahead of its
-      // MFMAs
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < NF; ++t)
@@ -258,9 +236,8 @@ __device__ __forceinline__ void lds_chunk(const LdsCtx& x, u32x4_t* Ab, const u3
 }
 
 struct LdsBufs {
-  u32x4_t* A;     // two activation chunk buffers, 2048 slots each (one LDS array, indexed
-                  // by chunk parity: a pointer picked from a table would lose its address
-                  // space)
+  u32x4_t* A;     // activation chunk buffers of even and odd chunks (2048 slots each;
+  u32x4_t* A1;    // separate LDS arrays, like the weight buffers)
   u32x4_t* W0;    // weight chunk buffers (named separately so that the compiler can tell
   u32x4_t* W1;    // which transfers a read depends on)
   u32x4_t* W2;
@@ -283,28 +260,36 @@ __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, cons
       for (int e = 0; e < 16; ++e) acc[t][o][e] = 0.f;
 
   const int nc = x.nc;
-  u32x4_t ar[8];
-  // prologue: activations of chunk 0 to LDS, weights of chunks 0 and 1 requested,
-  // activations of chunk 1 in registers
-  lds_load_a(x, ar, 0);
+  // prologue: activations of chunk 0, then the weights of chunks 0 and 1 (the first
+  // barrier leaves only chunk 1's weights in flight)
+  lds_fetch_a(x, b.A, wave, 0, 0);
+  lds_fetch_a(x, b.A, wave, 0, 4);
   lds_fetch_w(x, b.W0, wave, 0);
   lds_fetch_w(x, b.W1, wave, 1);
-  lds_store_a(b.A, ar, wave);
-  lds_load_a(x, ar, 1);
+  // chunk parity picks the activation buffer, chunk mod 3 the weight buffer: period 6
   int c = 0;
-  for (; c + 3 <= nc; c += 3) {
-    lds_chunk<GATEUP, NF>(x, b.A, b.W0, b.W2, ar, wave, c, acc);
-    lds_chunk<GATEUP, NF>(x, b.A, b.W1, b.W0, ar, wave, c + 1, acc);
-    lds_chunk<GATEUP, NF>(x, b.A, b.W2, b.W1, ar, wave, c + 2, acc);
+  for (; c + 6 <= nc; c += 6) {
+    lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W2, b.W1, wave, c + 5, acc);
   }
-  if (c < nc) lds_chunk<GATEUP, NF>(x, b.A, b.W0, b.W2, ar, wave, c, acc);
-  if (c + 1 < nc) lds_chunk<GATEUP, NF>(x, b.A, b.W1, b.W0, ar, wave, c + 1, acc);
-  // the requests past the last chunk read nothing but still write LDS: let every wave's
-  // land, and every wave finish its last operand reads, before the buffers are reused
+  if (c < nc) lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
+  if (c + 1 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
+  if (c + 2 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
+  if (c + 3 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
+  if (c + 4 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
-  if constexpr (NF > 0)
-    lds_epilogue<EPI, NF>(a, b.A + wave * 1024, acc, arow, 64, tile, nbase, col0);
+  if constexpr (NF > 0) {
+    // staging: waves 0-1 in the even buffer, 2-3 in the odd one, 16 KiB each
+    if (wave < 2)
+      lds_epilogue<EPI, NF>(a, b.A + (wave & 1) * 1024, acc, arow, 64, tile, nbase, col0);
+    else
+      lds_epilogue<EPI, NF>(a, b.A1 + (wave & 1) * 1024, acc, arow, 64, tile, nbase, col0);
+  }
 }
 
 template <int EPI>
@@ -312,7 +297,8 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int BM = 256;
   constexpr int FEAT = GATEUP ? 128 : 256;  // features of N per workgroup
-  __shared__ __attribute__((aligned(1024))) u32x4_t Ab[2 * BM * 8];
+  __shared__ __attribute__((aligned(1024))) u32x4_t Ab[BM * 8];
+  __shared__ __attribute__((aligned(1024))) u32x4_t Ab1[BM * 8];
   __shared__ __attribute__((aligned(1024))) u32x4_t W0[BM * 8];
   __shared__ __attribute__((aligned(1024))) u32x4_t W1[BM * 8];
   __shared__ __attribute__((aligned(1024))) u32x4_t W2[BM * 8];
@@ -397,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
 
   // live 32-row fragments of this wave's half of the tile (wave-uniform)
   const int nf = min(4, max(0, (nrows - arow + 63) / 64));
-  const LdsBufs bufs{Ab, W0, W1, W2};
+  const LdsBufs bufs{Ab, Ab1, W0, W1, W2};
   const int col0 = ks * N;  // this slice's columns in a row of Ys
   switch (nf) {
     case 0: lds_tile<EPI, 0>(a, x, bufs, wave, arow, tile, nbase, col0); break;
@@ -421,6 +407,8 @@ void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a) {
 hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
                         DenseOut mode, float* Cf, uint16_t* Cb, const float* R, Tile* tiles,
                         int32_t* ntiles, hipStream_t s, int ksplit) {
+  // the epilogues store whole 4-output groups: an output row must be a multiple of 4
+  if ((N & 3) != 0) return hipErrorInvalidValue;
   // one group (the "shared" slot of the tile list) whose rows are all the rows of A
   const FfnShape sh{rows, K, 0, 0, N, true};
   const bool wide = rows > 512;

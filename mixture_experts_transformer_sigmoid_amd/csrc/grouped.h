@@ -186,11 +186,11 @@ __device__ __forceinline__ void store_gateup(uint16_t* dst, f32x4_t g, f32x4_t u
   *reinterpret_cast<u32x2_t*>(dst) = packed;
 }
 
-// Store four consecutive outputs (features nn .. nn+3) of grouped row p.  N is a
-// multiple of 64 for every bf16 output (d, I and the latent width are); only the fp32
-// output of the router GEMM (N = 3E) can have N % 4 != 0, and then the row is neither
-// 16-byte aligned nor a whole number of 4-feature groups, so it is stored one float at a
-// time and features >= N are dropped (they would land on the next row).
+// Store four consecutive outputs (features nn .. nn+3) of grouped row p.  Every output
+// row is a whole number of 4-feature groups: N is a multiple of 64 for every bf16 output
+// (d, I and the latent width are), and the fp32 outputs are the down GEMM's (N = d) and
+// the router's partial logits, whose parts are padded to a multiple of 4 (checked on the
+// host by launch_dense).
 template <int EPI>
 __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x4_t v,
                                        f32x4_t u, int col0 = 0) {
@@ -200,13 +200,7 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
   } else if (EPI == kF32) {
     float* yrow = p < a.routed_rows ? a.Y + p * N
                                     : a.Ys + (p - a.routed_rows) * (a.ldc ? a.ldc : N) + col0;
-    if ((N & 3) == 0) {
-      *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (nn + i < N) yrow[nn + i] = v[i];
-    }
+    *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
   } else {
     if (EPI == kAddBF16) v += *reinterpret_cast<const f32x4_t*>(a.R + p * N + nn);
     u32x2_t packed;
@@ -257,25 +251,6 @@ __device__ __forceinline__ void lds_epilogue(const FfnArgs& a, u32x4_t* stage,
   constexpr int RPI = 64 / PPR;       // rows per read-back instruction
   const int lane = threadIdx.x & 63, hl = lane >> 5;
   const int nrows = tile.row_end - tile.row_begin;
-  // fp32 rows of 3E router logits need not be whole 4-output groups: per-output stores
-  if (EPI == kF32 && (a.N & 3) != 0) {
-#pragma unroll
-    for (int t = 0; t < NF; ++t) {
-      const int m = arow + tstride * t + (lane & 31);
-      if (m >= nrows) continue;
-#pragma unroll
-      for (int oo = 0; oo < FO; ++oo)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nn = nbase + 32 * oo + 8 * q + 4 * hl;
-          const f32x16_t& g = acc[t][oo];
-          store4<EPI>(a, tile.row_begin + m, nn,
-                      f32x4_t{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]}, f32x4_t{},
-                      col0);
-        }
-    }
-    return;
-  }
   const int rw = lane & 31;
   const int rr = lane / PPR, pr = lane % PPR;  // read side: row within the group, piece
 #pragma unroll

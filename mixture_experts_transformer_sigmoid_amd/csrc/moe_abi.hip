@@ -44,7 +44,7 @@ moe_status check_dims(const moe_dims* dp) {
   if ((uint64_t)d.tokens * d.d_model * 2 >= kMaxBuffer) return MOE_EUNSUPPORTED;
   if (!matrix_ok(d.d_expert, d.d_model) || !matrix_ok(d.d_model, d.d_expert))
     return MOE_EUNSUPPORTED;
-  if (!matrix_ok(3 * d.n_experts, d.d_model)) return MOE_EUNSUPPORTED;
+  if (!matrix_ok(3 * moe::router_part_rows(d.n_experts), d.d_model)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -68,7 +68,7 @@ Layout layout(const moe_dims& d) {
     return o;
   };
   L.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
-  L.wsplit = take(3 * E * (size_t)d.d_model * 2);
+  L.wsplit = take(3 * (size_t)moe::router_part_rows(d.n_experts) * d.d_model * 2);
   L.idx = take(slots * 4);
   L.w = take(slots * 4);
   L.counts = take(E * 4);
@@ -193,7 +193,7 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
     return o;
   };
   P.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
-  P.wsplit = take(3 * E * (size_t)d.d_model * 2);
+  P.wsplit = take(3 * (size_t)moe::router_part_rows(d.n_experts) * d.d_model * 2);
   P.idx = take(slots * 4);
   P.w = take(slots * 4);
   P.counts = take(E * 4);

@@ -19,19 +19,22 @@
 namespace moe {
 namespace {
 
-// w_split[p][e][j], p = 0 (hi), 1 (mid), 2 (lo)
+// w_split[p][e][j], p = 0 (hi), 1 (mid), 2 (lo), each part Ep = router_part_rows(E) rows
+// of d: rows E .. Ep - 1 are zero, so that every part, and every row of partial logits the
+// GEMM writes, is a whole number of 4-float groups
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ w_r,
-                                                           int64_t n,
+                                                           int64_t n, int64_t np_,
                                                            uint16_t* __restrict__ w_split) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const float w = w_r[i];
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < np_;
+       i += (int64_t)gridDim.x * 256) {
+    const float w = i < n ? w_r[i] : 0.0f;
     const uint32_t hi = f32_to_bf16(w);
     const float r1 = w - bf16_to_f32(hi);
     const uint32_t mid = f32_to_bf16(r1);
     const float r2 = r1 - bf16_to_f32(mid);
     w_split[i] = (uint16_t)hi;
-    w_split[n + i] = (uint16_t)mid;
-    w_split[2 * n + i] = (uint16_t)f32_to_bf16(r2);
+    w_split[np_ + i] = (uint16_t)mid;
+    w_split[2 * np_ + i] = (uint16_t)f32_to_bf16(r2);
   }
 }
 
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
 // gates use the sigmoid without the bias.
 template <int EPL>
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ z_part,
-                                                            int np, int row_parts,
+                                                            int np, int row_parts, int pstride,
                                                             const float* __restrict__ bias,
                                                             int64_t T, int E, int k, float alpha,
                                                             float* __restrict__ logits,
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* zp = z_part + t * (int64_t)row_parts * E;
+  const float* zp = z_part + t * (int64_t)row_parts * pstride;
 
   // the np partial logits of each expert, added in fp64 in part order.  Loads of 8 parts
   // are issued together: every load reads an in-range element (part and expert clamped)
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        v[j][i] = zp[min(p0 + j, np - 1) * E + min(lane + 64 * i, E - 1)];
+        v[j][i] = zp[min(p0 + j, np - 1) * pstride + min(lane + 64 * i, E - 1)];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -238,12 +241,12 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
 }
 
 template <int EPL>
-void select_launch(const float* z_part, int np, int row_parts, const float* bias, int64_t T,
-                   int E, int k, float alpha, float* logits, int32_t* idx, float* w,
+void select_launch(const float* z_part, int np, int row_parts, int pstride, const float* bias,
+                   int64_t T, int E, int k, float alpha, float* logits, int32_t* idx, float* w,
                    hipStream_t s) {
   const unsigned grid = (unsigned)((T + 3) / 4);
   hipLaunchKernelGGL(router_select_kernel<EPL>, dim3(grid), dim3(256), 0, s, z_part, np,
-                     row_parts, bias, T, E, k, alpha, logits, idx, w);
+                     row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
 }
 
 }  // namespace
@@ -254,7 +257,7 @@ hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias,
                          float* topk_w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   hipError_t err;
-  int np, row_parts;
+  int np, row_parts, pstride;
   if (T <= kRouterSmallT) {
     const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 63) / 64), kRouterKSplit);
     hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, x, w_r, T, d, E, z_part);
@@ -264,35 +267,38 @@ hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias,
     // slice
     np = 3 * kRouterKSplit;
     row_parts = 3 * kRouterKSplit;
+    pstride = E;
   } else {
-    const int64_t n = (int64_t)E * d;
-    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w_r, n,
+    const int Ep = router_part_rows(E);
+    const int64_t n = (int64_t)E * d, np_ = (int64_t)Ep * d;
+    const int64_t blocks = (np_ + 255) / 256 < 4096 ? (np_ + 255) / 256 : 4096;
+    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w_r, n, np_,
                        w_split);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     // K cut into S slices (router_ksplit): every token's row holds S x (hi, mid, lo)
-    // partial logits, which the selection adds in fp64 in that order
+    // partial logits, Ep apart, which the selection adds in fp64 in that order
     const int S = router_ksplit(T, E, d);
-    err = launch_dense(x, T, d, w_split, 3 * E, DenseOut::kF32, z_part, nullptr, nullptr, tiles,
+    err = launch_dense(x, T, d, w_split, 3 * Ep, DenseOut::kF32, z_part, nullptr, nullptr, tiles,
                        ntiles, s, S);
     if (err != hipSuccess) return err;
     np = 3 * S;
     row_parts = 3 * S;
+    pstride = Ep;
   }
   const int epl = (E + 63) / 64;
   if (epl <= 1)
-    select_launch<1>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<1>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else if (epl <= 2)
-    select_launch<2>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<2>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else if (epl <= 4)
-    select_launch<4>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<4>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else if (epl <= 6)
-    select_launch<6>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<6>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else if (epl <= 8)
-    select_launch<8>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<8>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   else
-    select_launch<16>(z_part, np, row_parts, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+    select_launch<16>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
   return hipGetLastError();
 }
 
