@@ -141,22 +141,27 @@ def algorithmic(cfg, active, T):
                 gateup_flops=gateup_flops, gateup_units=gateup_units)
 
 
-def time_forward(M, torch, dims, inp, out, ws, steps, warmup):
+def time_forward(M, torch, dims, inp, out, ws, steps, warmup, per_step=None):
+    """Mean ms per moe_forward over `steps` back-to-back calls (HIP events on the launch
+    stream around all of them).  With per_step a list, an event between consecutive calls
+    also gives each call's own time (appended to it)."""
     for _ in range(warmup):
         M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
                       inp["ws1"], inp["ws3"], inp["ws2"], out, ws)
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     wall = time.perf_counter()
-    t0.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
                       inp["ws1"], inp["ws3"], inp["ws2"], out, ws)
-    t1.record()
+        if per_step is not None or i == steps - 1:
+            ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall
-    return t0.elapsed_time(t1) / steps, wall
+    if per_step is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[steps]) / steps, wall
 
 
 def time_block(M, torch, S, cfg, weights, steps, warmup):
@@ -492,7 +497,8 @@ def main():
     time.sleep(SETTLE_S)
 
     log(f"timing moe_forward, {args.workload}, T={T}")
-    ms, wall = time_forward(M, torch, dims, inp, out, ws, args.steps, args.warmup)
+    steps_ms = []
+    ms, wall = time_forward(M, torch, dims, inp, out, ws, args.steps, args.warmup, steps_ms)
     st = split_state(M, torch, dims, inp, ws)
     active = int((st["counts"] > 0).sum())
     alg = algorithmic(cfg, active, T)
@@ -522,6 +528,8 @@ def main():
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": GATEUP_KERNEL[args.workload] + " (+ its tile-list launch)",
                      "ms_per_launch": gu_ms, "bytes_per_launch": alg["gateup_bytes"]},
+        "step_ms": {"median": sorted(steps_ms)[len(steps_ms) // 2], "min": min(steps_ms),
+                    "max": max(steps_ms)},
         "layer": {"hbm_gbs": layer_gbs, "hbm_frac": layer_gbs / HBM_PEAK_GBS,
                   "mfma_tflops": layer_tfs, "mfma_frac": layer_tfs / MFMA_BF16_PEAK_TFLOPS,
                   "algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"]},
@@ -547,7 +555,8 @@ def main():
         pout = torch.empty(pcfg["tokens"], pcfg["d_model"], dtype=torch.bfloat16, device=dev)
         log("timing moe_forward, k2_prefill, T=8192")
         psteps = max(3, min(args.steps, 10))
-        pms, _ = time_forward(M, torch, pdims, pin, pout, pws, psteps, 1)
+        psteps_ms = []
+        pms, _ = time_forward(M, torch, pdims, pin, pout, pws, psteps, 1, psteps_ms)
         pst = split_state(M, torch, pdims, pin, pws)
         pact = int((pst["counts"] > 0).sum())
         palg = algorithmic(pcfg, pact, pcfg["tokens"])
@@ -560,6 +569,8 @@ def main():
             pws = None
         res["prefill"] = {"workload": "k2_prefill: T=8192 (4 x 2048), same layer", "steps": psteps,
                           "ms_per_step": pms, "tokens_per_s": pcfg["tokens"] / (pms * 1e-3),
+                          "step_ms": {"median": sorted(psteps_ms)[len(psteps_ms) // 2],
+                                      "min": min(psteps_ms), "max": max(psteps_ms)},
                           "mfma_tflops": ptf, "mfma_frac": ptf / MFMA_BF16_PEAK_TFLOPS,
                           "hbm_gbs": pgb, "hbm_frac": pgb / HBM_PEAK_GBS, "active_experts": pact}
         if power is not None:
