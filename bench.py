@@ -10,7 +10,9 @@ line: whole-layer tokens/s for the main workload (128-token decode by default), 
 roofline of the dominant kernel (the gate/up grouped GEMM) timed with HIP events on
 the stream it runs on, the 8192-token prefill figure, the 4096-token skewed-routing figure,
 the block, FP8-weight and latent variants, measured ceilings (read-only stream, copy,
-vendor GEMM), and the CPU oracle timed on a bounded sample on the host cores.
+vendor GEMM), the committed rocprofv3 counter summaries for the measured kernels (HBM bytes,
+MFMA utilisation) while the kernel sources match them, and the CPU oracle timed on a
+bounded sample on the host cores.
 """
 from __future__ import annotations
 
@@ -76,6 +78,61 @@ def write_traffic(fetch_csv, write_csv):
     print(json.dumps(out, indent=1))
 
 
+MFMA_JSON = os.path.join(ROOT, "profiles", "mfma_util.json")
+XCDS = 8          # MI355X: 8 accelerator complex dies (GRBM_GUI_ACTIVE is summed over them)
+SIMDS = 1024      # 256 CUs x 4 SIMDs
+MFMA_FLOP_PER_SIMD_CYCLE = 1024   # dense bf16: 2.5 PFLOP/s = 1024 SIMDs x 2.4 GHz x 1024
+
+
+def write_mfma(csv_path):
+    """Turn a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 counter CSV into profiles/mfma_util.json: per kernel and
+    grid, the MFMA-busy fraction of the active cycles (busy cycles summed over the SIMDs
+    / (active cycles per XCD x SIMDs)), the bf16 MFMA flops the hardware counted (MOPS x
+    512), the kernel time and the clock that the active cycles imply."""
+    import csv
+    import collections
+    per = collections.defaultdict(dict)
+    for r in csv.DictReader(open(csv_path)):
+        key = (r["Kernel_Name"], r["Grid_Size"], r["Dispatch_Id"])
+        per[key][r["Counter_Name"]] = float(r["Counter_Value"])
+        per[key]["_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    groups = collections.defaultdict(list)
+    for (name, grid, _), v in per.items():
+        if v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) > 0 and "GRBM_GUI_ACTIVE" in v:
+            groups[(name, grid)].append(v)
+    out = {"source_sha256": kernel_source_hash(), "kernels": {}}
+    for (name, grid), vs in groups.items():
+        n = len(vs)
+        sec = sum(v["_s"] for v in vs) / n
+        active = sum(v["GRBM_GUI_ACTIVE"] for v in vs) / n / XCDS
+        busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in vs) / n
+        flops = sum(v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for v in vs) / n * 512
+        out["kernels"].setdefault(name, {})[grid] = {
+            "launches": n, "ms": sec * 1e3, "clock_ghz": active / sec / 1e9,
+            "mfma_busy_frac": busy / (active * SIMDS), "mfma_flops": flops,
+            "mfma_tflops": flops / sec / 1e12}
+    with open(MFMA_JSON, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1))
+
+
+def mfma_for(kernel_substr, grid):
+    """The committed MFMA counters of one kernel launch shape, or None when missing or the
+    kernel sources changed since they were taken."""
+    try:
+        with open(MFMA_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    for name, grids in t["kernels"].items():
+        if kernel_substr in name and str(grid) in grids:
+            return grids[str(grid)]
+    return None
+
+
 def traffic_for(kernel_substr):
     """HBM bytes per launch of a kernel from the committed counter summary, or None when it
     is missing, the kernel ran with more than one grid there (several workloads), or the
@@ -113,6 +170,9 @@ def parse():
                     help="skip sampling socket power / clock during the prefill loop")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured HBM-copy and vendor-GEMM peaks")
+    ap.add_argument("--write-mfma", metavar="COUNTER_CSV",
+                    help="write profiles/mfma_util.json from a --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                         "GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 counter CSV and exit")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two --pmc counter CSVs and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -469,6 +529,9 @@ def main():
     if args.write_traffic:
         write_traffic(*args.write_traffic)
         return
+    if args.write_mfma:
+        write_mfma(args.write_mfma)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the layer is measured on one GPU's share; across GPUs it would shard by expert "
@@ -573,6 +636,14 @@ def main():
                                       "min": min(psteps_ms), "max": max(psteps_ms)},
                           "mfma_tflops": ptf, "mfma_frac": ptf / MFMA_BF16_PEAK_TFLOPS,
                           "hbm_gbs": pgb, "hbm_frac": pgb / HBM_PEAK_GBS, "active_experts": pact}
+        # MFMA counters of the prefill GEMMs (committed rocprofv3 --pmc summary, taken on
+        # the current kernel sources): busy fraction of the active cycles, implied clock
+        ctr = {role: mfma_for("ffn_lds_kernel<%d>" % epi, grid) for role, epi, grid in
+               (("gate_up", 0, 2756608), ("down", 1, 4825088))}
+        if all(ctr.values()):
+            res["prefill"]["mfma_counters"] = {
+                role: {"busy_frac": c["mfma_busy_frac"], "clock_ghz": c["clock_ghz"],
+                       "counted_tflops": c["mfma_tflops"]} for role, c in ctr.items()}
         if power is not None:
             res["prefill"]["power"] = power
             log(f"prefill power: {power['socket_power_w']:.0f} W socket, "
