@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
 // Lane l holds experts l, l + 64, ...; k rounds of a wave-wide argmax over (score,
 // -index) pick the experts (ties to the lower index, NaN scores treated as -inf); the
 // gates use the sigmoid without the bias.
-template <int EPL>
+template <int EPL, int PB>
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ z_part,
                                                             int np, int row_parts, int pstride,
                                                             const float* __restrict__ bias,
@@ -148,22 +148,26 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   if (t >= T) return;
   const float* zp = z_part + t * (int64_t)row_parts * pstride;
 
-  // the np partial logits of each expert, added in fp64 in part order.  Loads of 8 parts
-  // are issued together: every load reads an in-range element (part and expert clamped)
-  // and the out-of-range ones are dropped afterwards, so that no load sits behind a branch
-  // (a guarded load compiles to a branch and a wait per load)
+  // the np partial logits of each expert, added in fp64 in part order.  Loads of PB parts
+  // are issued together (the host picks PB >= np where the registers allow, so that the
+  // wave waits for one round trip): every load reads an in-range element (part and expert
+  // clamped) and the out-of-range ones are dropped afterwards, so that no load sits behind
+  // a branch (a guarded load compiles to a branch and a wait per load)
   double zd[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) zd[i] = 0.0;
-  for (int p0 = 0; p0 < np; p0 += 8) {
-    float v[8][EPL];
+  for (int p0 = 0; p0 < np; p0 += PB) {
+    float v[PB][EPL];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < PB; ++j)
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
         v[j][i] = zp[min(p0 + j, np - 1) * pstride + min(lane + 64 * i, E - 1)];
+    // all of the batch's loads before the first add (left alone, the compiler interleaves
+    // them and keeps only about 32 in flight)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < PB; ++j)
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
         zd[i] += (p0 + j < np) ? (double)v[j][i] : 0.0;
@@ -240,13 +244,22 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   }
 }
 
+// Parts per batch of loads: every part in one batch (np is at most 24: 3 per K slice, at
+// most 8 slices) while the loaded values fit in 144 registers, else batches of 8.
 template <int EPL>
 void select_launch(const float* z_part, int np, int row_parts, int pstride, const float* bias,
                    int64_t T, int E, int k, float alpha, float* logits, int32_t* idx, float* w,
                    hipStream_t s) {
   const unsigned grid = (unsigned)((T + 3) / 4);
-  hipLaunchKernelGGL(router_select_kernel<EPL>, dim3(grid), dim3(256), 0, s, z_part, np,
-                     row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
+  if (EPL <= 6 && np <= 12)
+    hipLaunchKernelGGL((router_select_kernel<EPL, 12>), dim3(grid), dim3(256), 0, s, z_part, np,
+                       row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
+  else if (EPL <= 6)
+    hipLaunchKernelGGL((router_select_kernel<EPL, 24>), dim3(grid), dim3(256), 0, s, z_part, np,
+                       row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
+  else
+    hipLaunchKernelGGL((router_select_kernel<EPL, 8>), dim3(grid), dim3(256), 0, s, z_part, np,
+                       row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
 }
 
 }  // namespace
