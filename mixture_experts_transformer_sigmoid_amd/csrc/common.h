@@ -114,6 +114,17 @@ struct Tile {
   int32_t pad[3];
 };
 
+// How a grouped launch cuts its groups into row tiles; passed by value to the kernels that
+// build the list.
+struct TileSpec {
+  int32_t E;            // routed groups, rows given by the offsets
+  int32_t BM;           // rows per tile
+  int32_t parts;        // the shared expert's tiles are cut into this many parts
+  int64_t routed_rows;  // T*k
+  int64_t shared_rows;  // T with a shared expert, else 0
+  int64_t capacity;     // entries the list has room for
+};
+
 // Router: w_split [3 router_part_rows(E), d] bf16 and z_part (router_zpart_floats) fp32
 // are workspace;
 // logits may be null.  Up to kRouterSmallT tokens take the K-sliced small kernel, whose
@@ -157,9 +168,12 @@ hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias,
                          Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,
                          float* topk_w, hipStream_t s);
 
+// ts (or null): also build the tile list of a grouped launch for the new offsets into
+// tiles / ntiles, so that the launch can skip building it.
 hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* hist,
                           int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm,
-                          int32_t* inv, hipStream_t s);
+                          int32_t* inv, hipStream_t s, const TileSpec* ts = nullptr,
+                          Tile* tiles = nullptr, int32_t* ntiles = nullptr);
 int64_t permute_blocks(int64_t T);
 
 struct FfnShape {
@@ -172,6 +186,10 @@ struct FfnShape {
 };
 
 int64_t ffn_max_tiles(const FfnShape& sh);
+// The tiles of the bf16 and of the FP8 gate/up and down launches at this shape (both
+// projections use the same list).
+TileSpec ffn_tile_spec(const FfnShape& sh);
+TileSpec ffn_tile_spec_fp8(const FfnShape& sh);
 
 // Dense C[rows, N] = A[rows, K] . W[N, K]^T with the grouped-GEMM kernels (one group):
 // fp32 into Cf; bf16 into Cb; or bf16(C + R) into Cb with R [rows, N] fp32.
@@ -186,10 +204,10 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
 hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                           const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, Tile* tiles,
-                          int32_t* ntiles, hipStream_t s);
+                          int32_t* ntiles, hipStream_t s, bool tiles_ready = false);
 
-// tiles_ready: the tile list already holds this shape's tiles for the same offsets (the
-// gate/up launch just before built it), so the down launch skips rebuilding it.
+// tiles_ready: the tile list already holds this shape's tiles for the same offsets (built
+// by the permutation or by the gate/up launch just before), so the launch skips building it.
 hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
                        const uint16_t* w2, const uint16_t* ws2, float* y_routed,
                        float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s,
@@ -215,7 +233,8 @@ constexpr int kFp8MaxK = 16384;  // the FP8 kernels keep a row of K/128 scales i
 
 hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                               const int32_t* offsets, const Fp8Weights& w, uint16_t* h,
-                              Tile* tiles, int32_t* ntiles, hipStream_t s);
+                              Tile* tiles, int32_t* ntiles, hipStream_t s,
+                              bool tiles_ready = false);
 
 hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
                            const Fp8Weights& w, float* y_routed, float* y_shared, Tile* tiles,

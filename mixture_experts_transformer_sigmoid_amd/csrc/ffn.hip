@@ -398,6 +398,10 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
 
 int64_t ffn_max_tiles(const FfnShape& sh) { return max_tiles_for(sh, kSkinnyBM); }
 
+TileSpec ffn_tile_spec(const FfnShape& sh) {
+  return tile_spec_for(sh, use_wide(sh) ? kWideBM : kSkinnyBM);
+}
+
 // The 256-row-tile kernel covers 128 (gate/up) or 256 (otherwise) features of N per block.
 template <int EPI>
 void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a) {
@@ -457,11 +461,13 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
 hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                           const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, Tile* tiles,
-                          int32_t* ntiles, hipStream_t s) {
+                          int32_t* ntiles, hipStream_t s, bool tiles_ready) {
   const bool wide = use_wide(sh);
   const int BM = wide ? kWideBM : kSkinnyBM;
-  hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
-  if (err != hipSuccess) return err;
+  if (!tiles_ready) {
+    hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
+    if (err != hipSuccess) return err;
+  }
   FfnArgs a{};
   a.A = x;
   a.a_rows = sh.T;

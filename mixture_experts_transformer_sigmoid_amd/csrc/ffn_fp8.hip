@@ -424,13 +424,19 @@ FfnArgs fp8_args(const FfnShape& sh, const Fp8Weights& w, bool gateup, Tile* til
 
 }  // namespace
 
+TileSpec ffn_tile_spec_fp8(const FfnShape& sh) {
+  return tile_spec_for(sh, use_wide(sh) ? kF8BM : kSkinnyBM);
+}
+
 hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                               const int32_t* offsets, const Fp8Weights& w, uint16_t* h,
-                              Tile* tiles, int32_t* ntiles, hipStream_t s) {
+                              Tile* tiles, int32_t* ntiles, hipStream_t s, bool tiles_ready) {
   const bool wide = use_wide(sh);
   const int BM = wide ? kF8BM : kSkinnyBM;
-  hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
-  if (err != hipSuccess) return err;
+  if (!tiles_ready) {
+    hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
+    if (err != hipSuccess) return err;
+  }
   FfnArgs a = fp8_args(sh, w, true, tiles, ntiles);
   a.A = x;
   a.a_rows = sh.T;

@@ -122,25 +122,30 @@ moe_status route_impl(const moe_dims& d, const uint16_t* x, const float* w_r, co
                                        at<int32_t>(ws, L.ntiles), logits, idx, w, s));
 }
 
+// ts (or null): the permutation also builds this tile list in the workspace, for the
+// grouped launches that follow on the same offsets
 moe_status permute_impl(const moe_dims& d, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                        int32_t* perm, int32_t* inv, void* ws, hipStream_t s) {
+                        int32_t* perm, int32_t* inv, void* ws, hipStream_t s,
+                        const moe::TileSpec* ts = nullptr) {
   const Layout L = layout(d);
   return hip_status(moe::launch_permute(idx, d.tokens, d.n_experts, d.top_k,
                                         at<int32_t>(ws, L.hist), at<int32_t>(ws, L.base), counts,
-                                        offsets, perm, inv, s));
+                                        offsets, perm, inv, s, ts, at<Tile>(ws, L.tiles),
+                                        at<int32_t>(ws, L.ntiles)));
 }
 
+// tiles_ready: the workspace already holds this launch's tile list for these offsets
+// (built by the permutation, or by the gate/up launch just before; both GEMMs share it)
 moe_status gate_up_impl(const moe_dims& d, const uint16_t* x, const int32_t* perm,
                         const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                         const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, void* ws,
-                        hipStream_t s) {
+                        hipStream_t s, bool tiles_ready = false) {
   const Layout L = layout(d);
   return hip_status(moe::launch_gate_up(ffn_shape(d), x, perm, offsets, w1, w3, ws1, ws3, h,
-                                        at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles), s));
+                                        at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles), s,
+                                        tiles_ready));
 }
 
-// tiles_ready: called right after gate_up_impl on the same offsets and workspace, whose
-// tile list the down GEMM shares
 moe_status down_impl(const moe_dims& d, const uint16_t* h, const int32_t* offsets,
                      const uint16_t* w2, const uint16_t* ws2, float* y_routed,
                      float* y_shared, void* ws, hipStream_t s, bool tiles_ready = false) {
@@ -231,9 +236,10 @@ moe_status forward_impl(const moe_dims& d, const uint16_t* x, const float* w_rou
   uint16_t* h = at<uint16_t>(ws, L.h);
   float* y_routed = at<float>(ws, L.y);
   float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
+  const moe::TileSpec ts = moe::ffn_tile_spec(ffn_shape(d));
   MOE_TRY(route_impl(d, x, w_router, bias, idx, w, nullptr, ws, s));
-  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s));
-  MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s));
+  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s, &ts));
+  MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s, true));
   MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s, true));
   return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, residual, out, d.tokens,
                                         d.d_model, d.top_k, s));
@@ -351,11 +357,12 @@ moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float*
   float* y_routed = at<float>(ws, L.y);
   float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
   const moe::Fp8Weights fw = fp8_of(*w);
+  const moe::TileSpec ts = moe::ffn_tile_spec_fp8(ffn_shape(d));
   MOE_TRY(route_impl(d, x, w_router, bias, idx, gw, nullptr, ws, s));
-  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s));
+  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s, &ts));
   MOE_TRY(hip_status(moe::launch_gate_up_fp8(ffn_shape(d), x, perm, offsets, fw, h,
                                              at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
-                                             s)));
+                                             s, true)));
   MOE_TRY(hip_status(moe::launch_down_fp8(ffn_shape(d), h, offsets, fw, y_routed, y_shared,
                                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
                                           s, true)));

@@ -10,7 +10,11 @@
 //   scatter rebuilds the masks; a slot's row is offsets[e] + base[b][e] + the tokens of
 //           earlier waves of the block + popcount(mask & lanes-below): token-ascending
 //           order inside every segment, with no sequential loop anywhere.
+// Up to 256 tokens (one count block, decode) one workgroup runs the three phases in a
+// single launch, and can build the grouped GEMMs' tile list from the new offsets at its
+// end: each of those launches costs a few microseconds of latency for far less work.
 #include "common.h"
+#include "tiles.h"
 
 namespace moe {
 namespace {
@@ -140,13 +144,110 @@ __global__ __launch_bounds__(kTokPerBlock) void permute_scatter_kernel(
   }
 }
 
+// All three phases for T <= 256 in one workgroup of 1024 threads: the first 256 threads
+// (waves 0-3) own one token each, as in the count and scatter blocks, and with a single
+// block every base is 0.  The results equal the three-launch path's, element by element.
+// With tiles non-null the workgroup then builds the tile list of ts from the offsets.
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t T, int E, int k, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    TileSpec ts, Tile* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+  __shared__ unsigned long long masks[4][kMaxExperts];
+  __shared__ int32_t soff[kMaxExperts + 1];
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 4 * E; i += 1024) masks[i / E][i % E] = 0ull;
+  __syncthreads();
+  const bool tok = tid < kTokPerBlock && tid < T;
+  int slot_e[kMaxTopK];
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    slot_e[s] = -1;
+    if (s < k && tok) {
+      const int e = topk_idx[(int64_t)tid * k + s];
+      bool ok = (e >= 0 && e < E);
+#pragma unroll
+      for (int q = 0; q < kMaxTopK; ++q)
+        if (q < s && slot_e[q] == e) ok = false;
+      if (ok) {
+        slot_e[s] = e;
+        atomicOr(&masks[wave][e], 1ull << lane);
+      }
+    }
+  }
+  __syncthreads();
+  // counts, then their exclusive scan over experts (wave scans, then across the waves)
+  int32_t c = 0;
+  if (tid < E)
+    c = __popcll(masks[0][tid]) + __popcll(masks[1][tid]) + __popcll(masks[2][tid]) +
+        __popcll(masks[3][tid]);
+  int32_t v = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t acc = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int32_t x = wsum[w];
+      wsum[w] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  const int32_t incl = v + wsum[wave];
+  if (tid < E) {
+    counts[tid] = c;
+    offsets[tid] = incl - c;
+    soff[tid] = incl - c;
+  }
+  if (tid == E - 1) {
+    offsets[E] = incl;
+    soff[E] = incl;
+  }
+  __syncthreads();
+  const int64_t slots = T * k;
+  for (int64_t p = soff[E] + tid; p < slots; p += 1024) perm[p] = -1;
+  if (tok) {
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+      if (s >= k) break;
+      const int e = slot_e[s];
+      const int64_t slot = (int64_t)tid * k + s;
+      if (e < 0) {
+        inv[slot] = -1;
+        continue;
+      }
+      int r = __popcll(masks[wave][e] & below);
+      for (int w = 0; w < wave; ++w) r += __popcll(masks[w][e]);
+      const int32_t pos = soff[e] + r;
+      perm[pos] = (int32_t)slot;
+      inv[slot] = pos;
+    }
+  }
+  if (tiles != nullptr)
+    build_tiles_block(soff, ts.E, ts.routed_rows, ts.shared_rows, ts.BM, ts.parts, ts.capacity,
+                      tiles, ntiles);
+}
+
 }  // namespace
 
 int64_t permute_blocks(int64_t T) { return (T + kTokPerBlock - 1) / kTokPerBlock; }
 
 hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* hist,
                           int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm,
-                          int32_t* inv, hipStream_t s) {
+                          int32_t* inv, hipStream_t s, const TileSpec* ts, Tile* tiles,
+                          int32_t* ntiles) {
+  if (T <= kTokPerBlock) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s, topk_idx, T, E, k, counts,
+                       offsets, perm, inv, ts != nullptr ? *ts : TileSpec{},
+                       ts != nullptr ? tiles : nullptr, ntiles);
+    return hipGetLastError();
+  }
   const int64_t nb = permute_blocks(T);
   if (nb > 0) {
     hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)nb), dim3(kTokPerBlock), 0, s,
@@ -160,6 +261,9 @@ hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int E, int k, int3
   if (err != hipSuccess || nb == 0) return err;
   hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nb), dim3(kTokPerBlock), 0, s,
                      topk_idx, T, E, k, base, offsets, perm, inv);
+  err = hipGetLastError();
+  if (err != hipSuccess || ts == nullptr) return err;
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, *ts, tiles, ntiles);
   return hipGetLastError();
 }
 
