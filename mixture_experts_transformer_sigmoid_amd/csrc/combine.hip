@@ -185,6 +185,11 @@ hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float
 // then the scaling), rounded once to fp32 and then to bf16: the normalised row feeds the
 // router, whose top-k decision would turn on a one-ulp difference in any element, and in
 // fp64 the result does not depend on the summation order to within bf16 rounding.
+// The first kNormVec 8-element pieces of each thread (the whole row up to d = 8192) are
+// requested at once and kept in registers for the scaling pass; loads at clamped in-range
+// addresses, so that none sits behind a branch.  Wider rows loop over the rest.
+constexpr int kNormVec = 4;
+
 __global__ __launch_bounds__(kCombineThreads) void rmsnorm_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, uint16_t* __restrict__ out,
     int d, float eps) {
@@ -192,16 +197,24 @@ __global__ __launch_bounds__(kCombineThreads) void rmsnorm_kernel(
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   const uint16_t* row = x + t * d;
-  double ss = 0.0;
-  for (int c = tid * 8; c < d; c += kCombineThreads * 8) {
-    const u32x4_t v = load16(row + c);
+  constexpr int kSpan = kCombineThreads * 8;  // elements per pass of the workgroup
+  u32x4_t v[kNormVec];
+#pragma unroll
+  for (int j = 0; j < kNormVec; ++j) v[j] = load16(row + min(tid * 8 + j * kSpan, d - 8));
+  auto sumsq = [](const u32x4_t& w, double acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const double a = bf16_to_f32(v[i] & 0xffffu), b = bf16_to_f32(v[i] >> 16);
-      ss = fma(a, a, ss);
-      ss = fma(b, b, ss);
+      const double a = bf16_to_f32(w[i] & 0xffffu), b = bf16_to_f32(w[i] >> 16);
+      acc = fma(a, a, acc);
+      acc = fma(b, b, acc);
     }
-  }
+    return acc;
+  };
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < kNormVec; ++j)
+    if (tid * 8 + j * kSpan < d) ss = sumsq(v[j], ss);
+  for (int c = tid * 8 + kNormVec * kSpan; c < d; c += kSpan) ss = sumsq(load16(row + c), ss);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
   if ((tid & 63) == 0) wsum[tid >> 6] = ss;
@@ -210,17 +223,20 @@ __global__ __launch_bounds__(kCombineThreads) void rmsnorm_kernel(
 #pragma unroll
   for (int i = 0; i < kCombineThreads / 64; ++i) tot += wsum[i];
   const double inv_rms = 1.0 / sqrt(tot / (double)d + (double)eps);
-  for (int c = tid * 8; c < d; c += kCombineThreads * 8) {
-    const u32x4_t v = load16(row + c);
+  auto scale_store = [&](const u32x4_t& w, int c) {
     u32x4_t o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float a = (float)((double)bf16_to_f32(v[i] & 0xffffu) * inv_rms * (double)gain[c + 2 * i]);
-      const float b = (float)((double)bf16_to_f32(v[i] >> 16) * inv_rms * (double)gain[c + 2 * i + 1]);
+      const float a = (float)((double)bf16_to_f32(w[i] & 0xffffu) * inv_rms * (double)gain[c + 2 * i]);
+      const float b = (float)((double)bf16_to_f32(w[i] >> 16) * inv_rms * (double)gain[c + 2 * i + 1]);
       o[i] = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
     }
     *reinterpret_cast<u32x4_t*>(out + t * d + c) = o;
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < kNormVec; ++j)
+    if (tid * 8 + j * kSpan < d) scale_store(v[j], tid * 8 + j * kSpan);
+  for (int c = tid * 8 + kNormVec * kSpan; c < d; c += kSpan) scale_store(load16(row + c), c);
 }
 
 hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, uint16_t* out, int64_t T, int d,
