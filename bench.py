@@ -35,7 +35,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_transformer_sigmoid_amd", "csrc", f)
-                  for f in ("ffn.hip", "grouped.h", "common.h")]
+                  for f in ("ffn.hip", "grouped.h", "tiles.h", "common.h")]
 COPY_BYTES = 1 << 30
 SETTLE_S = 2.0                  # idle pause between input generation and timing
 READ_BYTES = 4 << 30

@@ -51,6 +51,16 @@ __global__ __launch_bounds__(kGatherThreads) void combine_kernel(
       w[s] = 0.0f;
     }
   }
+  // the shared expert's row and the residual are requested before any of the loads above
+  // is waited for (issued after the sums, they would cost a second round trip)
+  f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (y_shared != nullptr) {
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y_shared + t * d + c);
+    sa = src[0];
+    sb = src[1];
+  }
+  if (residual != nullptr) v = load16(residual + t * d + c);
   f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < KMAX; ++s) {
@@ -62,13 +72,11 @@ __global__ __launch_bounds__(kGatherThreads) void combine_kernel(
     }
   }
   if (y_shared != nullptr) {
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y_shared + t * d + c);
-    lo += src[0];
-    hi += src[1];
+    lo += sa;
+    hi += sb;
   }
   if (residual != nullptr) {
     // x_{n+1} = x'_n + Delta_ffn, added in fp32 before the one bf16 rounding
-    const u32x4_t v = load16(residual + t * d + c);
     lo[0] += bf16_to_f32(v[0] & 0xffffu);
     lo[1] += bf16_to_f32(v[0] >> 16);
     lo[2] += bf16_to_f32(v[1] & 0xffffu);
