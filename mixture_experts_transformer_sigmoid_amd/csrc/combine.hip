@@ -124,21 +124,32 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rmsnorm_kernel(
       }
     }
   }
+  // every row piece of the token is requested before the first add: loads at clamped
+  // in-range addresses (a dropped slot reads row 0 and its value is replaced by 0), so
+  // that no load sits behind a branch and waits alone
+  f32x4_t v[CPT][KMAX];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = min(tid + kCombineThreads * j, nch - 1);
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s)
+      v[j][s] = *reinterpret_cast<const f32x4_t*>(y_routed + (int64_t)max(p[s], 0) * L + 4 * c);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   f32x4_t acc[CPT];
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int c = tid + kCombineThreads * j;
-    if (c < nch) {
 #pragma unroll
-      for (int s = 0; s < KMAX; ++s) {
-        if (s >= k) break;
-        if (p[s] < 0) continue;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(y_routed + (int64_t)p[s] * L + 4 * c);
+    for (int s = 0; s < KMAX; ++s) {
+      // a dropped slot, or one past k (weight 0, index -1), adds fma(0, 0, acc) = acc: the
+      // same bits as skipping it
+      const bool ok = p[s] >= 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(w[s], v[i], acc[j][i]);
-      }
+      for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(w[s], ok ? v[j][s][i] : 0.0f, acc[j][i]);
+    }
+    if (tid + kCombineThreads * j < nch) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ss = fmaf(acc[j][i], acc[j][i], ss);
     }
