@@ -377,6 +377,43 @@ def test_permute_drops_invalid_entries():
     np.testing.assert_array_equal(p[:len(valid)], np.array(valid)[np.argsort(flat[valid], kind="stable")])
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 7, 3), (255, 16, 2), (256, 384, 8), (257, 384, 8),
+                                   (256, 1024, 8), (600, 1024, 8)])
+def test_permute_both_paths_against_definition(T, E, k):
+    """Up to 256 tokens the permutation runs in one workgroup, above that in three launches:
+    both, and the boundary between them, against the definition written with numpy
+    (valid slots in order of expert, stable; dropped slots as in the reading for invalid
+    routing input), with out-of-range and repeated indices planted."""
+    rng = np.random.default_rng(1000 * T + E)
+    idx = rng.integers(0, E, size=(T, k))
+    m = rng.random((T, k))
+    idx[m < 0.03] = -1
+    idx[(m >= 0.03) & (m < 0.05)] = E
+    cfg = S.with_overrides("tiny", n_experts=E, top_k=k)
+    dims = M.dims_for(cfg, tokens=T)
+    ws = M.workspace(dims)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    perm = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    inv = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    M.moe_permute(dims, torch.tensor(idx, dtype=torch.int32, device=DEV), counts, offsets, perm,
+                  inv, ws)
+    torch.cuda.synchronize()
+    flat = idx.reshape(-1)
+    valid = np.array([t * k + s for t in range(T) for s in range(k)
+                      if 0 <= idx[t, s] < E and idx[t, s] not in idx[t, :s]], dtype=np.int64)
+    want_counts = np.bincount(flat[valid], minlength=E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), want_counts)
+    np.testing.assert_array_equal(offsets.cpu().numpy(),
+                                  np.concatenate([[0], np.cumsum(want_counts)]))
+    want_perm = np.full(T * k, -1, dtype=np.int64)
+    want_perm[:len(valid)] = valid[np.argsort(flat[valid], kind="stable")]
+    np.testing.assert_array_equal(perm.cpu().numpy(), want_perm)
+    want_inv = np.full(T * k, -1, dtype=np.int64)
+    want_inv[want_perm[:len(valid)]] = np.arange(len(valid))
+    np.testing.assert_array_equal(inv.cpu().numpy(), want_inv)
+
+
 def test_zero_tokens_leaves_output_alone():
     cfg = S.CONFIGS["tiny"]
     inp = to_dev(S.make_inputs(cfg, "cpu"))
