@@ -398,8 +398,15 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
 
 int64_t ffn_max_tiles(const FfnShape& sh) { return max_tiles_for(sh, kSkinnyBM); }
 
+// bf16 weights: the 256-row kernel from 5 rows per group on.  The whole K2-shape layer
+// (d 7168, 384 experts, top-8, I 2048) over T = 64..640, each kernel forced (one box, two
+// passes, ms): T 64 4.16 skinny / 4.31 256-row, 128 5.25 / 5.25, 192 5.55 / 5.55,
+// 224 5.64 / 5.58, 256 5.67 / 5.61, 448 6.14 / 5.83, 640 7.37 / 6.01.  Switching at 16 rows
+// per group, as before, left T = 200..680 up to 18% slow.
+constexpr int kWideRowsBf16 = 5;
+
 TileSpec ffn_tile_spec(const FfnShape& sh) {
-  return tile_spec_for(sh, use_wide(sh) ? kWideBM : kSkinnyBM);
+  return tile_spec_for(sh, use_wide(sh, kWideRowsBf16) ? kWideBM : kSkinnyBM);
 }
 
 // The 256-row-tile kernel covers 128 (gate/up) or 256 (otherwise) features of N per block.
@@ -462,7 +469,7 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                           const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, Tile* tiles,
                           int32_t* ntiles, hipStream_t s, bool tiles_ready) {
-  const bool wide = use_wide(sh);
+  const bool wide = use_wide(sh, kWideRowsBf16);
   const int BM = wide ? kWideBM : kSkinnyBM;
   if (!tiles_ready) {
     hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
@@ -496,7 +503,7 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
                        const uint16_t* w2, const uint16_t* ws2, float* y_routed,
                        float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s,
                        bool tiles_ready) {
-  const bool wide = use_wide(sh);
+  const bool wide = use_wide(sh, kWideRowsBf16);
   const int BM = wide ? kWideBM : kSkinnyBM;
   if (!tiles_ready) {
     hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);

@@ -424,14 +424,19 @@ FfnArgs fp8_args(const FfnShape& sh, const Fp8Weights& w, bool gateup, Tile* til
 
 }  // namespace
 
+// FP8 weights: the 128-row stream kernel above 16 rows per group.  Its tiles are half as
+// tall and it converts every weight, so the skinny kernel stays ahead longer: K2-shape layer,
+// ms, skinny / 128-row: T 128 2.88 / 3.51, 256 3.16 / 3.80, 448 3.42 / 3.89, 640 3.81 / 3.93.
+constexpr int kWideRowsFp8 = 16;
+
 TileSpec ffn_tile_spec_fp8(const FfnShape& sh) {
-  return tile_spec_for(sh, use_wide(sh) ? kF8BM : kSkinnyBM);
+  return tile_spec_for(sh, use_wide(sh, kWideRowsFp8) ? kF8BM : kSkinnyBM);
 }
 
 hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                               const int32_t* offsets, const Fp8Weights& w, uint16_t* h,
                               Tile* tiles, int32_t* ntiles, hipStream_t s, bool tiles_ready) {
-  const bool wide = use_wide(sh);
+  const bool wide = use_wide(sh, kWideRowsFp8);
   const int BM = wide ? kF8BM : kSkinnyBM;
   if (!tiles_ready) {
     hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);
@@ -456,7 +461,7 @@ hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32
 hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
                            const Fp8Weights& w, float* y_routed, float* y_shared, Tile* tiles,
                            int32_t* ntiles, hipStream_t s, bool tiles_ready) {
-  const bool wide = use_wide(sh);
+  const bool wide = use_wide(sh, kWideRowsFp8);
   const int BM = wide ? kF8BM : kSkinnyBM;
   if (!tiles_ready) {
     hipError_t err = tiles_launch(sh, offsets, BM, tiles, ntiles, s);

@@ -217,12 +217,13 @@ int64_t max_tiles_for(const FfnShape& sh, int BM) {
   return sh.T * sh.k / BM + sh.E + (sh.shared ? (sh.T + BM - 1) / BM : 0) + 1;
 }
 
-// Average rows per group (routed experts plus the shared expert) decides the kernel: a
-// few (decode) -> skinny kernel; many (prefill) -> a 256-row kernel.
-bool use_wide(const FfnShape& sh) {
+// Average rows per group (routed experts plus the shared expert) decides the kernel: up to
+// rows_per_group (decode) -> skinny kernel; more -> the 256-row (bf16) or 128-row (FP8)
+// kernel.  Each weight type passes its own crossover.
+bool use_wide(const FfnShape& sh, int rows_per_group) {
   const int64_t rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
   const int64_t groups = sh.E + (sh.shared ? 1 : 0);
-  return rows > (int64_t)16 * groups;
+  return rows > (int64_t)rows_per_group * groups;
 }
 
 TileSpec tile_spec_for(const FfnShape& sh, int BM) {

@@ -275,6 +275,25 @@ def test_ragged_shapes(T):
     full_check(cfg, inp, intermediates=True)
 
 
+@pytest.mark.parametrize("T,concentrated", [(37, False), (150, False), (150, True)])
+def test_skinny_kernel_ragged(T, concentrated):
+    """The skinny (16-row tile) GEMMs on ragged shapes.  A bf16 layer takes them up to 5
+    rows per group on average: here at most 150 * 3 / 97 = 4.6.  N = 192 and 320 are not
+    multiples of the 64- and 128-feature blocks.  Concentrated: every token on experts 0
+    and 1, which then span ten 16-row tiles each, the last one partly filled."""
+    cfg = dict(tokens=T, d_model=320, n_experts=96, top_k=2, d_expert=192, d_shared=192,
+               routed_scale=2.827, bias="uniform")
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=40 + T))
+    if concentrated:
+        b = torch.zeros(cfg["n_experts"])
+        b[:2] = 10.0
+        inp["b"] = b.to(DEV)
+    g, _ = full_check(cfg, inp, intermediates=True)
+    if concentrated:
+        c = g["counts"].cpu().numpy()
+        assert np.all(c[:2] == T) and c[2:].sum() == 0
+
+
 def test_no_shared_expert():
     cfg = S.with_overrides("tiny", d_shared=0)
     inp = to_dev(S.make_inputs(cfg, "cpu", seed=5))
