@@ -211,13 +211,13 @@ moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float*
                            const float* bias, const moe_fp8_weights* w, uint16_t* out,
                            void* ws, size_t ws_bytes, void* stream);
 
-/* Latent mixture of experts ("Kimi K3 · Latent up-projection": the router scores the
- * full-width input; the input is projected down to the latent width; the routed experts
- * run on the latent; their gate-weighted sum is RMS-normalised and projected back up; the
- * shared expert runs on the full-width input and is added):
- *   z, s, sel, G as in moe_route on x;  l = x W_down^T  [T, L] (bf16);
- *   u = sum_i G_i E_i(l) (experts on width L);  u_hat = u / sqrt(mean(u^2) + 1e-6)
- *   (unit gain);  out = bf16(u_hat W_up^T + y_shared(x))
+/* Latent mixture of experts ("Kimi K3 · Latent up-projection", the module's forward and its
+ * projection parameters):
+ *   z, s, sel, G as in moe_route, computed on the full-width x;
+ *   l = x W_down^T  [T, L] (bf16);
+ *   u = sum_i G_i E_i(l)  (SwiGLU experts of input and output width L);
+ *   u_hat = u / sqrt(mean(u^2) + 1e-6)  (unit gain; the norm precedes W_up);
+ *   out = bf16(u_hat W_up^T + y_shared(x))  (shared expert on the full width).
  *   w_down [L, d] bf16; w1, w3 [E, I, L]; w2 [E, L, I]; w_up [d, L] bf16; shared expert
  *   [Is, d] / [d, Is] on the full width; out [T, d] bf16.  d_latent: multiple of 64,
  *   at most 8192.  Workspace from moe_latent_workspace_bytes. */

@@ -327,11 +327,16 @@ def moe_sparse(x, w_r, b, top_k, alpha=ALPHA_K2, *, get_expert=None, w1=None, w3
 # ------------------------------------------------------------------ latent variant
 def moe_latent(x, w_r, b, w_down, w1, w3, w2, w_up, ws1, ws3, ws2, top_k,
                alpha=ALPHA_K2, eps=1e-6, tokens=None, get_expert=None):
-    """Latent mixture of experts ("Kimi K3 · Latent up-projection", the printed forward):
-    the router scores the full-width input; the input is projected down to the latent
-    width; the selected latent experts run and are gate-weighted and summed; the sum is
-    RMS-normalised and projected back up (y_routed = u_hat W_up); the shared expert
-    runs on the full-width input and is added."""
+    """Latent mixture of experts ("Kimi K3 · Latent up-projection", the module's forward):
+
+        z, s, sel, G = route(x)               on the full width d
+        l = x W_down^T                        [T, L]
+        u = sum_{i in sel} G_i E_i(l)         experts of width L
+        u_hat = RMSNorm(u)                    unit gain, on the latent width
+        out = u_hat W_up^T + y_shared(x)      shared expert on the full width
+
+    The norm comes before the up-projection, in the order the page's forward applies its
+    routed-expert norm and routed-expert up-projection."""
     r = route(x, w_r, b, top_k, alpha)
     x64 = _f64(x)
     rows = np.arange(x64.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)

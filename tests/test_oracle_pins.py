@@ -312,6 +312,83 @@ def test_latent_reduces_to_normalised_k2_layer():
     np.testing.assert_allclose(lat["out"], ref + sp["y_shared"], rtol=1e-12, atol=1e-13)
 
 
+def _latent_layer(rng, T=12, d=32, Lw=24, E=8, I=16, k=2):
+    """A latent layer with non-square, non-orthogonal projections: W_down [Lw, d] and
+    W_up [d, Lw] (Lw != d), experts on the latent width, shared expert on the full width."""
+    base = _layer(rng, T=T, d=d, E=E, I=I, Is=I, k=k)
+    base["w_down"] = _bf16_round(rng.standard_normal((Lw, d)) / math.sqrt(d) * 1.7 + 0.05)
+    base["w_up"] = _bf16_round(rng.standard_normal((d, Lw)) / math.sqrt(Lw) * 0.6 - 0.03)
+    base["w1"] = _bf16_round(rng.standard_normal((E, I, Lw)) / math.sqrt(Lw))
+    base["w3"] = _bf16_round(rng.standard_normal((E, I, Lw)) / math.sqrt(Lw))
+    base["w2"] = _bf16_round(rng.standard_normal((E, Lw, I)) / math.sqrt(I))
+    return base
+
+
+def _latent_torch_reference(L, eps=1e-6, alpha=2.827):
+    """The latent forward written with torch's functional ops, token by token: the router
+    picks on the full-width x; the chosen experts run on l = x W_down^T; their gate-weighted
+    sum is RMS-normalised on the latent width FIRST and projected up SECOND; the shared
+    expert runs on the full-width x ("Kimi K3 · Latent up-projection", the printed forward:
+    the routed-expert norm is applied before the routed-expert up-projection)."""
+    F = torch.nn.functional
+    t64 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))  # noqa: E731
+    x = t64(L["x"])
+    r = oracle.route(L["x"], L["w_r"], L["b"], L["top_k"], alpha)   # routing pinned elsewhere
+    lat = F.linear(x, t64(L["w_down"]))
+    rows = []
+    for t in range(x.shape[0]):
+        acc = torch.zeros(lat.shape[1], dtype=torch.float64)
+        for j in range(L["top_k"]):
+            e = int(r["topk_idx"][t, j])
+            h = F.silu(F.linear(lat[t], t64(L["w1"][e]))) * F.linear(lat[t], t64(L["w3"][e]))
+            acc = acc + float(r["topk_w"][t, j]) * F.linear(h, t64(L["w2"][e]))
+        rows.append(acc)
+    y_lat = torch.stack(rows)
+    u_hat = F.rms_norm(y_lat, (y_lat.shape[1],), eps=eps)
+    shared = F.linear(F.silu(F.linear(x, t64(L["ws1"]))) * F.linear(x, t64(L["ws3"])),
+                      t64(L["ws2"]))
+    return (F.linear(u_hat, t64(L["w_up"])) + shared).numpy()
+
+
+def _latent_of(L, fn=None):
+    fn = fn or oracle.moe_latent
+    return fn(L["x"], L["w_r"], L["b"], L["w_down"], L["w1"], L["w3"], L["w2"], L["w_up"],
+              L["ws1"], L["ws3"], L["ws2"], L["top_k"])["out"]
+
+
+def test_latent_norm_before_up_projection_against_torch():
+    """Non-square W_down / W_up: the oracle's latent layer equals the torch composition in
+    the page's order (route on x, project down, experts, weighted sum, RMSNorm on the
+    latent, project up, add the shared expert on x)."""
+    L = _latent_layer(np.random.default_rng(31))
+    np.testing.assert_allclose(_latent_of(L), _latent_torch_reference(L), rtol=1e-11, atol=1e-12)
+
+
+def _latent_norm_after_up(x, w_r, b, w_down, w1, w3, w2, w_up, ws1, ws3, ws2, top_k,
+                          alpha=2.827, eps=1e-6):
+    """A plausible mistake: the same pieces with the RMSNorm applied after the
+    up-projection (on the model width) instead of before it (on the latent width)."""
+    r = mo.route(x, w_r, b, top_k, alpha)
+    lat = np.asarray(x, dtype=np.float64) @ np.asarray(w_down, dtype=np.float64).T
+    sp = mo.moe_sparse(lat, w_r, b, top_k, alpha, w1=w1, w3=w3, w2=w2, shared=None, routing=r)
+    y = mo.rmsnorm(sp["y_routed"] @ np.asarray(w_up, dtype=np.float64).T, eps)
+    return dict(out=y + mo.swiglu(x, ws1, ws3, ws2))
+
+
+def test_latent_pin_catches_norm_after_up_projection():
+    """The swapped order is caught by the non-square pin above.  With identity
+    projections the two orders agree, so the identity pin alone would miss it."""
+    L = _latent_layer(np.random.default_rng(31))
+    want = _latent_torch_reference(L)
+    swapped = _latent_of(L, _latent_norm_after_up)
+    assert np.abs(swapped - want).max() > 1e-2 * np.abs(want).max()
+    # the same swap on square identity projections is invisible
+    Li = _layer(np.random.default_rng(13), T=20, d=32, E=8, I=16, Is=16, k=2)
+    Li["w_down"] = Li["w_up"] = np.eye(32)
+    np.testing.assert_allclose(_latent_of(Li, _latent_norm_after_up), _latent_of(Li),
+                               rtol=1e-12, atol=1e-13)
+
+
 def test_a_planted_mistake_is_caught(monkeypatch):
     """Plant a mistake in the oracle (on the CPU) and check the pins notice it."""
     rng = np.random.default_rng(14)
