@@ -37,6 +37,7 @@
  *       MOE_EWORKSPACE   ws_bytes smaller than moe_workspace_bytes()
  *       MOE_EHIP         a kernel launch failed (device faults surface at the caller's
  *                        next synchronisation, as usual for asynchronous work)
+ *       MOE_ESCRATCH     moe_forward_noalloc only: dims need more than its fixed scratch
  *   - Deterministic: the same inputs give bit-identical outputs (no float atomics).
  */
 #ifndef MOE_H
@@ -66,7 +67,8 @@ typedef enum moe_status {
   MOE_EINVAL = 1,
   MOE_EUNSUPPORTED = 2,
   MOE_EWORKSPACE = 3,
-  MOE_EHIP = 4
+  MOE_EHIP = 4,
+  MOE_ESCRATCH = 5
 } moe_status;
 
 /* Human-readable name of a status code (static string). */
@@ -148,6 +150,25 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
                        const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
                        const uint16_t* ws2, uint16_t* out, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, kernels and
+ * results as moe_forward, but no workspace argument: the intermediates live in a device
+ * array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on (from
+ * the module's load until the process ends).  The call itself allocates nothing.
+ *   - Limit: moe_workspace_bytes(dims) <= MOE_NOALLOC_SCRATCH_BYTES, else MOE_ESCRATCH
+ *     before anything is launched.  At the K2 shape (d 7168, 384 experts, top-8, I 2048,
+ *     shared expert) that admits up to 404 tokens.
+ *   - The array of the CURRENT device is used: `stream` must belong to it.
+ *   - Every call on one GPU shares that GPU's array.  Calls that overlap on one GPU (on
+ *     different streams, or from different host threads without ordering) race on it and
+ *     give undefined results; calls ordered on one stream are safe.  Nothing in the array
+ *     needs to start at zero: every call writes each intermediate before reading it. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status moe_forward_noalloc(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                               const float* bias, const uint16_t* w1, const uint16_t* w3,
+                               const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
+                               const uint16_t* ws2, uint16_t* out, void* stream);
 
 /* The MoE half of a transformer block, with the steps either side of the layer fused in
  * ("Kimi K2 · Transformer blocks", MoE transformer block: x_ffn = RMSNorm(x'_n), the

@@ -3,17 +3,17 @@
 The computation lives in libmoe.so (HIP kernels for gfx950, C ABI in include/moe.h);
 this package is its ctypes binding.
 """
-from .binding import (EXPORTS, LIB_PATH, MOE_EHIP, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE,
-                      MOE_OK, MoeDims, MoeError, MoeFp8Weights, block_workspace, dims_for,
+from .binding import (EXPORTS, LIB_PATH, MOE_EHIP, MOE_EINVAL, MOE_ESCRATCH, MOE_EUNSUPPORTED,
+                      MOE_EWORKSPACE, MOE_OK, NOALLOC_SCRATCH_BYTES, MoeDims, MoeError, MoeFp8Weights, block_workspace, dims_for,
                       fp8_weights, latent_workspace, lib, moe_expert_down_fp8,
                       moe_expert_gate_up_fp8, moe_forward_fp8,
                       moe_block_workspace_bytes, moe_combine, moe_dims, moe_expert_down,
                       moe_expert_ffn, moe_expert_gate_up, moe_forward, moe_forward_block,
-                      moe_forward_latent, moe_latent_workspace_bytes, moe_permute, moe_route,
+                      moe_forward_latent, moe_forward_noalloc, moe_latent_workspace_bytes, moe_permute, moe_route,
                       moe_workspace_bytes, status_str, workspace)
 
-__all__ = ["EXPORTS", "LIB_PATH", "MOE_EHIP", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE",
-           "MOE_OK", "MoeDims", "MoeError", "MoeFp8Weights", "block_workspace", "dims_for",
+__all__ = ["EXPORTS", "LIB_PATH", "MOE_EHIP", "MOE_EINVAL", "MOE_ESCRATCH", "MOE_EUNSUPPORTED",
+           "MOE_EWORKSPACE", "MOE_OK", "NOALLOC_SCRATCH_BYTES", "moe_forward_noalloc", "MoeDims", "MoeError", "MoeFp8Weights", "block_workspace", "dims_for",
            "fp8_weights", "latent_workspace", "moe_expert_down_fp8", "moe_expert_gate_up_fp8",
            "moe_forward_fp8",
            "lib", "moe_block_workspace_bytes", "moe_combine", "moe_forward_block",

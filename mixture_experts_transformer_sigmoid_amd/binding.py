@@ -14,14 +14,16 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = range(6)
+# moe.h's MOE_NOALLOC_SCRATCH_BYTES: the fixed device scratch of moe_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 # every exported symbol of include/moe.h
 EXPORTS = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_latent_workspace_bytes", "moe_forward_latent",
            "moe_block_workspace_bytes", "moe_forward_block", "moe_expert_gate_up_fp8",
-           "moe_expert_down_fp8", "moe_forward_fp8")
+           "moe_expert_down_fp8", "moe_forward_fp8", "moe_forward_noalloc")
 
 
 class MoeDims(ctypes.Structure):
@@ -77,6 +79,7 @@ def lib():
         "moe_expert_ffn": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
         "moe_combine": [D, _P, _P, _P, _P, _P, _P],
         "moe_forward": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+        "moe_forward_noalloc": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "moe_block_workspace_bytes": [D, ctypes.POINTER(ctypes.c_size_t)],
         "moe_forward_block": [D, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               _S, _P],
@@ -183,6 +186,14 @@ def moe_forward(dims, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, ws, str
     _check(lib().moe_forward(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w1),
                              _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out), wp,
                              wn, _stream(stream)))
+
+
+def moe_forward_noalloc(dims, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, stream=None):
+    """moe_forward without a workspace: the library's fixed device scratch holds the
+    intermediates (raises MoeError MOE_ESCRATCH when the dims need more)."""
+    _check(lib().moe_forward_noalloc(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias),
+                                     _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3),
+                                     _ptr(ws2), _ptr(out), _stream(stream)))
 
 
 def moe_block_workspace_bytes(dims: MoeDims) -> int:

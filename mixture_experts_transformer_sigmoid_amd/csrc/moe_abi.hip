@@ -2,8 +2,16 @@
 // Every check runs on the host before the first launch; nothing here synchronises.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "common.h"
+
+// Fixed device scratch of moe_forward_noalloc: each GPU the library runs on holds its own
+// copy from the module's load until the process ends.  Host code never passes this name to
+// a kernel or a copy: the name is a host-side stand-in, and its device address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -48,6 +56,13 @@ moe_status check_dims(const moe_dims* dp) {
   return MOE_OK;
 }
 
+// The bf16 (hi, mid, lo) copy of the router matrix, used only above kRouterSmallT tokens
+// (the small-batch router splits W_r in registers).
+size_t router_wsplit_bytes(const moe_dims& d) {
+  if (d.tokens <= moe::kRouterSmallT) return 0;
+  return 3 * (size_t)moe::router_part_rows(d.n_experts) * d.d_model * 2;
+}
+
 struct Layout {
   size_t zpart, wsplit, idx, w, counts, offsets, perm, inv, hist, base, tiles, ntiles, h, y,
       total;
@@ -68,7 +83,7 @@ Layout layout(const moe_dims& d) {
     return o;
   };
   L.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
-  L.wsplit = take(3 * (size_t)moe::router_part_rows(d.n_experts) * d.d_model * 2);
+  L.wsplit = take(router_wsplit_bytes(d));
   L.idx = take(slots * 4);
   L.w = take(slots * 4);
   L.counts = take(E * 4);
@@ -198,7 +213,7 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
     return o;
   };
   P.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
-  P.wsplit = take(3 * (size_t)moe::router_part_rows(d.n_experts) * d.d_model * 2);
+  P.wsplit = take(router_wsplit_bytes(d));
   P.idx = take(slots * 4);
   P.w = take(slots * 4);
   P.counts = take(E * 4);
@@ -281,6 +296,27 @@ moe_status check_forward_args(const moe_dims& d, const float* w_router, const fl
   return check_ws(d, ws, ws_bytes);
 }
 
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept: each GPU holds its own copy of the array at its own address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status noalloc_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +331,24 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
   if (d.tokens == 0) return MOE_OK;
   MOE_NEED(aligned(x, 16));
   MOE_TRY(check_forward_args(d, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, ws, ws_bytes));
+  (void)hipGetLastError();
+  return forward_impl(d, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, nullptr, out, ws,
+                      (hipStream_t)stream);
+}
+
+moe_status moe_forward_noalloc(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                               const float* bias, const uint16_t* w1, const uint16_t* w3,
+                               const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
+                               const uint16_t* ws2, uint16_t* out, void* stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& d = *dims;
+  if (d.tokens == 0) return MOE_OK;
+  MOE_NEED(aligned(x, 16) && aligned(w_router, 16) && aligned(bias, 4));
+  MOE_NEED(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(out, 16));
+  if (has_shared(d)) MOE_NEED(aligned(ws1, 16) && aligned(ws3, 16) && aligned(ws2, 16));
+  if (layout(d).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ESCRATCH;
+  void* ws = nullptr;
+  MOE_TRY(noalloc_scratch(&ws));
   (void)hipGetLastError();
   return forward_impl(d, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, nullptr, out, ws,
                       (hipStream_t)stream);
@@ -403,6 +457,9 @@ const char* moe_status_str(int status) {
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: dims this library does not handle";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace smaller than moe_workspace_bytes()";
     case MOE_EHIP: return "MOE_EHIP: HIP launch error";
+    case MOE_ESCRATCH:
+      return "MOE_ESCRATCH: moe_forward_noalloc needs moe_workspace_bytes(dims) <= "
+             "MOE_NOALLOC_SCRATCH_BYTES (its fixed device scratch)";
     default: return "unknown moe_status";
   }
 }

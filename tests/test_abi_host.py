@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(5):
+    for code in range(6):
         assert M.status_str(code).startswith("MOE_")
     assert "unknown" in M.status_str(99)
 
@@ -202,3 +202,26 @@ def test_fp8_arguments_checked():
                              None) == M.MOE_OK
     assert L.moe_expert_down_fp8(ctypes.byref(z), None, None, ctypes.byref(good), None, None,
                                  None, 0, None) == M.MOE_OK
+
+
+def test_noalloc_host_checks():
+    """moe_forward_noalloc rejects, before touching the GPU, null or misaligned pointers and
+    dims whose intermediates exceed its fixed scratch (MOE_ESCRATCH, with a message naming
+    the limit); T = 0 is a no-op."""
+    L = M.lib()
+    P = _fake(0x100000)
+    Q = _fake(0x100002)
+    assert B.NOALLOC_SCRATCH_BYTES == 128 << 20
+    d = _k2(128)
+    assert M.moe_workspace_bytes(d) <= B.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(d), None, P, P, P, P, P, P, P, P, P, None) == M.MOE_EINVAL
+    assert L.moe_forward_noalloc(ctypes.byref(d), P, P, P, Q, P, P, P, P, P, P, None) == M.MOE_EINVAL
+    # the largest K2 batch that fits, and the first that does not
+    assert M.moe_workspace_bytes(_k2(404)) <= B.NOALLOC_SCRATCH_BYTES < M.moe_workspace_bytes(_k2(405))
+    big = _k2(405)
+    assert L.moe_forward_noalloc(ctypes.byref(big), P, P, P, P, P, P, P, P, P, P, None) == M.MOE_ESCRATCH
+    assert "MOE_NOALLOC_SCRATCH_BYTES" in M.status_str(M.MOE_ESCRATCH)
+    z = _k2(0)
+    assert L.moe_forward_noalloc(ctypes.byref(z), None, None, None, None, None, None, None, None,
+                                 None, None, None) == M.MOE_OK
+    assert L.moe_forward_noalloc(None, P, P, P, P, P, P, P, P, P, P, None) == M.MOE_EINVAL
