@@ -75,7 +75,13 @@ typedef enum moe_status {
 const char* moe_status_str(int status);
 
 /* Bytes of device workspace every entry point below accepts for these dims (one size
- * serves them all).  Host only; launches nothing. */
+ * serves them all).  Host only; launches nothing.
+ * After moe_forward, moe_forward_block, moe_forward_fp8 or moe_forward_latent returns (and
+ * its work has completed), the workspace begins with that call's routing and permutation,
+ * each array starting at the next multiple of 256 bytes, in this order:
+ *   topk_idx [T, k] int32, topk_w [T, k] fp32, counts [E] int32, offsets [E+1] int32,
+ *   perm_rows [T*k] int32, inv_perm [T*k] int32
+ * with the meanings of moe_route and moe_permute.  The rest of the workspace is opaque. */
 moe_status moe_workspace_bytes(const moe_dims* dims, size_t* bytes);
 
 /* Router ("Kimi K2 · Transformer blocks", MoE equations z, s, E_sel, G_i).

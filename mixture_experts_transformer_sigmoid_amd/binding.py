@@ -139,6 +139,23 @@ def workspace(dims: MoeDims, device="cuda") -> torch.Tensor:
     return torch.empty(max(moe_workspace_bytes(dims), 256), dtype=torch.uint8, device=device)
 
 
+def routing_in_workspace(dims: MoeDims, ws: torch.Tensor) -> dict:
+    """Views of the routing and permutation arrays a layer entry point leaves at the start
+    of its workspace (moe.h, moe_workspace_bytes): topk_idx, topk_w, counts, offsets,
+    perm_rows, inv_perm."""
+    T, E, k = int(dims.tokens), int(dims.n_experts), int(dims.top_k)
+    out, off = {}, 0
+    for name, n, dt, shape in (("topk_idx", T * k, torch.int32, (T, k)),
+                               ("topk_w", T * k, torch.float32, (T, k)),
+                               ("counts", E, torch.int32, (E,)),
+                               ("offsets", E + 1, torch.int32, (E + 1,)),
+                               ("perm_rows", T * k, torch.int32, (T * k,)),
+                               ("inv_perm", T * k, torch.int32, (T * k,))):
+        out[name] = ws[off:off + 4 * n].view(dt).view(shape)
+        off += (4 * n + 255) // 256 * 256
+    return out
+
+
 def _ws(ws):
     return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
 

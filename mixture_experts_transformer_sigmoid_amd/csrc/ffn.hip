@@ -422,7 +422,7 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
   if ((N & 3) != 0) return hipErrorInvalidValue;
   // one group (the "shared" slot of the tile list) whose rows are all the rows of A
   const FfnShape sh{rows, K, 0, 0, N, true};
-  const bool wide = rows > 512;
+  const bool wide = rows > kSingleGroupWideRows;
   const int BM = wide ? kWideBM : kSkinnyBM;
   hipError_t err = tiles_launch(sh, nullptr, BM, tiles, ntiles, s);
   if (err != hipSuccess) return err;

@@ -217,12 +217,19 @@ int64_t max_tiles_for(const FfnShape& sh, int BM) {
   return sh.T * sh.k / BM + sh.E + (sh.shared ? (sh.T + BM - 1) / BM : 0) + 1;
 }
 
+// A launch with a single group (a dense projection, or the latent variant's shared expert
+// on its own) takes the tall-tile kernel above this many rows.  Below it, the skinny
+// kernel's tiles each read the one weight matrix, mostly from L2.
+constexpr int64_t kSingleGroupWideRows = 512;
+
 // Average rows per group (routed experts plus the shared expert) decides the kernel: up to
 // rows_per_group (decode) -> skinny kernel; more -> the 256-row (bf16) or 128-row (FP8)
-// kernel.  Each weight type passes its own crossover.
+// kernel.  Each weight type passes its own crossover, measured with the routed experts
+// present; a launch of one group uses kSingleGroupWideRows instead.
 bool use_wide(const FfnShape& sh, int rows_per_group) {
   const int64_t rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
   const int64_t groups = sh.E + (sh.shared ? 1 : 0);
+  if (groups <= 1) return rows > kSingleGroupWideRows;
   return rows > (int64_t)rows_per_group * groups;
 }
 

@@ -82,14 +82,15 @@ Layout layout(const moe_dims& d) {
     off += align_up(bytes);
     return o;
   };
-  L.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
-  L.wsplit = take(router_wsplit_bytes(d));
+  // the routing and the permutation first, in the order the header documents
   L.idx = take(slots * 4);
   L.w = take(slots * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
   L.perm = take(slots * 4);
   L.inv = take(slots * 4);
+  L.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
+  L.wsplit = take(router_wsplit_bytes(d));
   L.hist = take(nb * E * 4);
   L.base = take(nb * E * 4);
   L.tiles = take(max_tiles * sizeof(Tile));
@@ -212,14 +213,15 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
     off += align_up(bytes);
     return o;
   };
-  P.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
-  P.wsplit = take(router_wsplit_bytes(d));
+  // the routing and the permutation first, in the order the header documents
   P.idx = take(slots * 4);
   P.w = take(slots * 4);
   P.counts = take(E * 4);
   P.offsets = take((E + 1) * 4);
   P.perm = take(slots * 4);
   P.inv = take(slots * 4);
+  P.zpart = take((size_t)moe::router_zpart_floats(d.tokens, d.n_experts, d.d_model) * 4);
+  P.wsplit = take(router_wsplit_bytes(d));
   P.hist = take(nb * E * 4);
   P.base = take(nb * E * 4);
   P.tiles = take(max_tiles * sizeof(Tile));

@@ -251,15 +251,37 @@ def permute(topk_idx, n_experts):
 
 
 # ------------------------------------------------------------------------------- FFN
-def swiglu(x_rows, w1, w3, w2):
+def swiglu(x_rows, w1, w3, w2, bf16_points=()):
     """One SwiGLU expert on a set of rows: g = x W1, u = x W3, a = g sigma(g), h = a u,
     E = h W2 ("Kimi K2 · Transformer blocks", expert and shared-expert equations).
-    Weights [out, in]; float64 throughout."""
+    Weights [out, in]; float64 throughout, except that "h" in bf16_points rounds h to
+    bf16 (the diagnostic mode below)."""
     x_rows = _f64(x_rows)
     g = x_rows @ _f64(w1).T
     u = x_rows @ _f64(w3).T
     h = silu(g) * u
+    if "h" in bf16_points:
+        h = round_bf16(h)
     return h @ _f64(w2).T
+
+
+# ------------------------------------------------------- diagnostic: bf16 points
+# DIAGNOSTIC ONLY, never a pass/fail reference: moe_sparse(..., bf16_points=...) rounds
+# chosen intermediates to bf16 (round_bf16: to fp32, then to bf16, nearest-even) so that
+# a difference between the HIP path and the exact oracle can be attributed to a precision
+# schedule rather than to a mistake.  The points:
+#   "h"           the SwiGLU hidden row, before the down projection
+#   "expert_out"  each expert's output row E_i
+#   "y_routed"    the gate-weighted sum over the k slots
+#   "y_shared"    the shared expert's output
+#   "out"         the layer output
+# PAGE_BF16_POINTS: where a bf16 copy of the module rounds ("Kimi K3 · Latent
+# up-projection", moe_infer: expert outputs in the module dtype, weighted sum taken in
+# fp32 and cast back; the shared output added in the module dtype).
+# KERNEL_BF16_POINTS: the HIP path's schedule (h is the down GEMM's bf16 operand; expert
+# outputs, the weighted sum and the shared output stay fp32; one final rounding).
+PAGE_BF16_POINTS = ("h", "expert_out", "y_routed", "y_shared", "out")
+KERNEL_BF16_POINTS = ("h", "out")
 
 
 def _expert_getter(w1, w3, w2):
@@ -281,7 +303,7 @@ def moe_dense(x, w_r, b, w1, w3, w2, ws1, ws3, ws2, top_k, alpha=ALPHA_K2):
 
 
 def moe_sparse(x, w_r, b, top_k, alpha=ALPHA_K2, *, get_expert=None, w1=None, w3=None,
-               w2=None, shared=None, tokens=None, routing=None):
+               w2=None, shared=None, tokens=None, routing=None, bf16_points=()):
     """Delta_ffn computed only through the k selected experts of each token.
 
     Follows the grouping of the K3 page's moe_infer (rows grouped by expert, each
@@ -291,6 +313,7 @@ def moe_sparse(x, w_r, b, top_k, alpha=ALPHA_K2, *, get_expert=None, w1=None, w3
     get_expert(e) -> (w1_e, w3_e, w2_e) lets a caller hand over one expert at a time
     (large shapes); shared = (ws1, ws3, ws2) or None.  tokens: optional list of token
     rows to evaluate (sampled check); routing: a precomputed route() result.
+    bf16_points: the diagnostic rounding points above (empty: exact, the reference).
     """
     if get_expert is None:
         get_expert = _expert_getter(w1, w3, w2)
@@ -309,7 +332,9 @@ def moe_sparse(x, w_r, b, top_k, alpha=ALPHA_K2, *, get_expert=None, w1=None, w3
     for e in sorted(by_expert):
         pairs = by_expert[e]
         w1e, w3e, w2e = get_expert(e)
-        out_e = swiglu(x[rows[[i for i, _ in pairs]]], w1e, w3e, w2e)
+        out_e = swiglu(x[rows[[i for i, _ in pairs]]], w1e, w3e, w2e, bf16_points)
+        if "expert_out" in bf16_points:
+            out_e = round_bf16(out_e)
         for n, pr in enumerate(pairs):
             per_slot[pr] = out_e[n]
     d = next(iter(per_slot.values())).shape[0] if per_slot else _f64(w_r).shape[1]
@@ -318,10 +343,17 @@ def moe_sparse(x, w_r, b, top_k, alpha=ALPHA_K2, *, get_expert=None, w1=None, w3
         for j in np.argsort(sel[i], kind="stable"):          # ascending expert index
             y_r[i] = y_r[i] + gates[i, j] * per_slot[(i, int(j))]
     if shared is not None:
-        y_s = swiglu(x[rows], *shared)
+        y_s = swiglu(x[rows], *shared, bf16_points)
     else:
         y_s = np.zeros_like(y_r)
-    return dict(r, rows=rows, y_routed=y_r, y_shared=y_s, out=y_r + y_s)
+    if "y_routed" in bf16_points:
+        y_r = round_bf16(y_r)
+    if "y_shared" in bf16_points:
+        y_s = round_bf16(y_s)
+    out = y_r + y_s
+    if "out" in bf16_points:
+        out = round_bf16(out)
+    return dict(r, rows=rows, y_routed=y_r, y_shared=y_s, out=out)
 
 
 # ------------------------------------------------------------------ latent variant

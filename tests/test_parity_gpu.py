@@ -68,14 +68,14 @@ def run_split(cfg, inp, dims=None):
                 y_r=y_r, y_s=y_s, out=out, dims=dims)
 
 
-def run_forward(cfg, inp, dims=None):
+def run_forward(cfg, inp, dims=None, keep_ws=False):
     dims = dims or M.dims_for(cfg)
     ws = M.workspace(dims)
     out = torch.full((dims.tokens, dims.d_model), float("nan"), dtype=torch.bfloat16, device=DEV)
     M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
                   inp.get("ws1"), inp.get("ws3"), inp.get("ws2"), out, ws)
     torch.cuda.synchronize()
-    return out
+    return (out, ws) if keep_ws else out
 
 
 def oracle_route(inp, dims):
@@ -108,6 +108,38 @@ def check_routing(g, ref, dims, ztol=1e-5):
     return int((~keep).sum())
 
 
+def check_near_ties(idx, ref, dims):
+    """Tokens excluded from the bit-exact comparison (k-th/(k+1)-th fp32 score gap below
+    1e-6) must still get a valid top-k: every chosen expert's score is within 1e-6 of the
+    best score left out, and the k experts are distinct.  Returns the excluded tokens."""
+    excl = np.nonzero(ref["gap"] < GAP)[0]
+    E, k = dims.n_experts, dims.top_k
+    sc = ref["score32"].astype(np.float64)
+    for t in excl:
+        chosen = np.asarray(idx[t], dtype=np.int64)
+        assert np.unique(chosen).size == k, (t, chosen)
+        if k < E:
+            left = np.ones(E, dtype=bool)
+            left[chosen] = False
+            assert sc[t, chosen].min() >= sc[t, left].max() - GAP, (t, chosen)
+    return excl
+
+
+def routing_of_gpu_selection(ref, idx, excl, alpha):
+    """The oracle's routing with the GPU's own expert sets on the excluded tokens (gates
+    alpha * s / sum s over that set, from the oracle's float64 sigmoids), so that the output
+    of near-tie tokens is still compared element by element."""
+    r = dict(ref)
+    r["topk_idx"] = ref["topk_idx"].copy()
+    r["topk_w"] = ref["topk_w"].copy()
+    for t in excl:
+        sel = np.asarray(idx[t], dtype=np.int64)
+        s = ref["s"][t, sel]
+        r["topk_idx"][t] = sel
+        r["topk_w"][t] = alpha * s / s.sum()
+    return r
+
+
 def check_permute(g, dims):
     """Bit-exact against the oracle's permutation of the GPU's own topk_idx."""
     counts, offsets, perm, inv = O.permute(g["idx"].cpu().numpy(), dims.n_experts)
@@ -124,6 +156,23 @@ def check_out(got, want, what="out"):
     rms = np.sqrt(np.mean(want ** 2))
     say(f"  {what}: max|err| {err.max():.3e}  tol {TOL * rms:.3e}  (rms {rms:.3e})")
     assert err.max() <= TOL * rms, (err.max(), TOL * rms, np.unravel_index(err.argmax(), err.shape))
+
+
+def attribute(got, want, inp, dims, toks, routing):
+    """On a failed output check: replay the kernels' precision schedule (the oracle's
+    bf16-points diagnostic, h and the output rounded to bf16) and report how far the GPU
+    sits from it.  A GPU within a bf16 step of the replay while the replay itself is over
+    the bar points at the schedule, not at a mistake; this never turns a failure into a
+    pass."""
+    rep = O.moe_sparse(f64(inp["x"]), None, None, dims.top_k, dims.routed_scale,
+                       get_expert=expert_getter(inp), shared=shared_of(inp), tokens=toks,
+                       routing=routing, bf16_points=O.KERNEL_BF16_POINTS)["out"]
+    rms = np.sqrt(np.mean(want ** 2))
+    over = np.abs(got - want) > TOL * rms
+    step = np.ldexp(1.0, np.frexp(np.abs(rep))[1] - 8)
+    say(f"  attribution: {int(over.sum())} elements over the bar; replay of the schedule "
+        f"max|err|/RMS {np.abs(rep - want).max() / rms:.4f}; GPU within one bf16 step of the "
+        f"replay on {int((np.abs(got - rep) <= step)[over].sum())} of them")
 
 
 def bf16r(a):
@@ -217,21 +266,36 @@ def full_check(cfg, inp, dims=None, sample=None, intermediates=False, seed=0):
     check_permute(g, dims)
     say("  permutation bit-exact")
     T = dims.tokens
-    keep = ref["gap"] >= GAP
+    idx = g["idx"].cpu().numpy()
+    excl = check_near_ties(idx, ref, dims)
+    if excl.size:
+        say(f"  near-tie tokens {excl.tolist()[:8]}: valid top-k sets, compared on the GPU's sets")
     if sample is None:
         toks = np.arange(T)
     else:
         rng = np.random.default_rng(seed)
-        toks = np.sort(rng.choice(T, size=min(sample, T), replace=False))
-    toks = toks[keep[toks]]
+        toks = np.unique(np.concatenate([rng.choice(T, size=min(sample, T), replace=False), excl]))
+    rsel = routing_of_gpu_selection(ref, idx, excl, dims.routed_scale)
     o = O.moe_sparse(f64(inp["x"]), None, None, dims.top_k, dims.routed_scale,
                      get_expert=expert_getter(inp), shared=shared_of(inp), tokens=toks,
-                     routing=ref)
-    check_out(f64(g["out"])[toks], o["out"])
+                     routing=rsel)
+    try:
+        check_out(f64(g["out"])[toks], o["out"], f"out ({toks.size} of {T} tokens)")
+    except AssertionError:
+        attribute(f64(g["out"])[toks], o["out"], inp, dims, toks, rsel)
+        raise
     if intermediates:
-        check_intermediates(g, inp, dims, toks[: 16 if dims.d_model <= 1024 else 2])
-    fw = run_forward(cfg, inp, dims)
+        n_int = intermediates if isinstance(intermediates, int) and intermediates > 1 else (
+            16 if dims.d_model <= 1024 else 2)
+        check_intermediates(g, inp, dims, toks[:n_int])
+    fw, ws = run_forward(cfg, inp, dims, keep_ws=True)
     assert torch.equal(fw.view(torch.int16), g["out"].view(torch.int16)), "forward != split path"
+    # the fused call's own routing and permutation, left at the front of its workspace
+    rw = M.routing_in_workspace(dims, ws)
+    for mine, theirs in (("idx", "topk_idx"), ("w", "topk_w"), ("counts", "counts"),
+                         ("offsets", "offsets"), ("perm", "perm_rows"), ("inv", "inv_perm")):
+        assert torch.equal(g[mine].reshape(-1).view(torch.int32),
+                           rw[theirs].reshape(-1).view(torch.int32)), f"forward's {theirs}"
     return g, ref
 
 
@@ -359,6 +423,33 @@ def test_expert_count_not_a_multiple_of_four(E, T):
     full_check(cfg, to_dev(S.make_inputs(cfg, "cpu", seed=20 + E)), intermediates=True)
 
 
+def test_near_ties_get_a_valid_topk():
+    """Experts 3 and 5 share a router row and a bias, so every token scores them equally:
+    whenever they straddle the k-th place the gap is 0 and the token leaves the bit-exact
+    comparison.  Its expert set must still be a valid top-k, and its output must match the
+    oracle's on that set."""
+    cfg = S.with_overrides("tiny", tokens=200, top_k=3)
+    inp = S.make_inputs(cfg, "cpu", seed=12)
+    inp["w_r"][5] = inp["w_r"][3]
+    inp["b"][5] = inp["b"][3]
+    inp = to_dev(inp)
+    g, ref = full_check(cfg, inp)
+    assert int((ref["gap"] < GAP).sum()) > 0, "the plant produced no near-tie token"
+
+
+def test_wide_kernel_main_loop_every_token():
+    """K = 1024 (gate/up) and 512 (down) give 16 and 8 chunks of 64: the 256-row kernel's
+    six-chunk main loop runs in both GEMMs, with ragged last tiles (256 rows per expert on
+    average, 16 experts), and every token is compared."""
+    cfg = dict(tokens=1024, d_model=1024, n_experts=16, top_k=4, d_expert=512, d_shared=512,
+               routed_scale=2.827, bias="uniform")
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=30))
+    g, _ = full_check(cfg, inp, intermediates=32)
+    c = g["counts"].cpu().numpy()
+    say(f"  rows per expert {c.min()}..{c.max()}")
+    assert c.max() > 256          # some experts span two row tiles
+
+
 def test_tie_break_lower_index():
     cfg = S.with_overrides("tiny", top_k=1)
     inp = S.make_inputs(cfg, "cpu", seed=11)
@@ -457,22 +548,30 @@ def test_workspace_too_small_rejected_on_device():
 
 
 # ------------------------------------------------------------------ K2 shape
-def _k2_case(name, k2_weights, sample):
-    cfg = S.CONFIGS[name]
+def _k2_case(name, k2_weights, sample, intermediates=True, tokens=None):
+    cfg = S.CONFIGS[name] if tokens is None else S.with_overrides(name, tokens=tokens)
     inp = dict(k2_weights)
     inp.update(S.make_activations(cfg, DEV))
-    g, ref = full_check(cfg, inp, sample=sample, intermediates=True)
+    g, ref = full_check(cfg, inp, sample=sample, intermediates=intermediates)
     active = int((g["counts"] > 0).sum())
     say(f"  {name}: active experts {active}, max rows/expert {int(g['counts'].max())}")
     return g
 
 
 def test_k2_decode_128(k2_weights):
-    _k2_case("k2_decode", k2_weights, sample=16)
+    _k2_case("k2_decode", k2_weights, sample=None, intermediates=8)
+
+
+@pytest.mark.parametrize("T", [256, 300])
+def test_k2_around_the_permutation_split(k2_weights, T):
+    """K2 shape at 256 tokens (the one-workgroup permutation that also builds the tile
+    list) and 300 (the three-launch permutation), both on the 256-row expert GEMMs with
+    1-7 rows per tile: every token, routing, permutation, written elements, intermediates."""
+    _k2_case("k2_decode", k2_weights, sample=None, intermediates=4, tokens=T)
 
 
 def test_k2_prefill_8192(k2_weights):
-    _k2_case("k2_prefill", k2_weights, sample=8)
+    _k2_case("k2_prefill", k2_weights, sample=1024)
 
 
 def test_k2_skewed_4096(k2_weights):

@@ -12,6 +12,7 @@ import torch
 import mixture_experts_transformer_sigmoid_amd as M
 import synth_inputs as S
 from oracle import moe_oracle as O
+from test_parity_gpu import check_permute, check_routing
 
 pytestmark = pytest.mark.gpu
 
@@ -37,17 +38,25 @@ def run_latent(cfg, inp):
                          inp["w3"], inp["w2"], inp["w_up"], inp.get("ws1"), inp.get("ws3"),
                          inp.get("ws2"), out, ws)
     torch.cuda.synchronize()
-    return out
+    return out, ws
 
 
 def check(cfg, inp, sample=None, seed=0):
     T = cfg["tokens"]
     say(f"latent case T={T} d={cfg['d_model']} L={cfg['d_latent']} E={cfg['n_experts']} k={cfg['top_k']}")
-    out = run_latent(cfg, inp)
-    again = run_latent(cfg, inp)
+    out, ws = run_latent(cfg, inp)
+    dims = M.dims_for(cfg)
+    rw = M.routing_in_workspace(dims, ws)
+    g = {"idx": rw["topk_idx"], "w": rw["topk_w"], "counts": rw["counts"],
+         "offsets": rw["offsets"], "perm": rw["perm_rows"], "inv": rw["inv_perm"]}
+    again, _ = run_latent(cfg, inp)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "not deterministic"
     r = O.route(f64(inp["x"]), f64(inp["w_r"]), inp["b"].cpu().numpy(), cfg["top_k"],
                 cfg["routed_scale"])
+    # the latent call's own routing (on the full-width x) and permutation
+    n_ex = check_routing(g, r, dims)
+    check_permute(g, dims)
+    say(f"  routing and permutation exact ({n_ex} near-tie tokens excluded)")
     keep = r["gap"] >= GAP
     toks = np.arange(T) if sample is None else np.sort(
         np.random.default_rng(seed).choice(T, size=min(sample, T), replace=False))
@@ -77,11 +86,20 @@ def test_latent_ragged(T):
     check(cfg, {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu", seed=T).items()})
 
 
+@pytest.mark.parametrize("T", [12, 600])
+def test_latent_shared_expert_kernel_choice(T):
+    """The shared expert runs as a launch of its own (one group of T rows): the skinny
+    kernel up to 512 rows, the 256-row kernel above."""
+    cfg = S.with_overrides("tiny_latent", tokens=T, d_model=512, d_latent=256, d_expert=256,
+                           d_shared=256)
+    check(cfg, {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu", seed=50 + T).items()})
+
+
 def test_latent_k2_shape_4096():
     cfg = S.CONFIGS["latent"]
     say("generating latent-MoE weights on the GPU (384 experts on a 3584-wide latent)")
     inp = S.make_inputs(cfg, DEV)
     torch.cuda.synchronize()
-    check(cfg, inp, sample=8)
+    check(cfg, inp, sample=64)
     del inp
     torch.cuda.empty_cache()
