@@ -112,18 +112,25 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* c
 
 /* Expert gate/up projections with the SwiGLU product fused in the epilogue
  * ("Kimi K2 · Transformer blocks", g = x W1, u = x W3, a = g sigma(g), h = a (.) u).
- *   h [(T*k + Ts), I] bf16: rows 0..T*k-1 in grouped order (row p reads token
+ *   h [(T*k + Ts), H] bf16: rows 0..T*k-1 in grouped order (row p reads token
  *     perm_rows[p] / k of x through expert e with offsets[e] <= p < offsets[e+1]), then,
  *     if the shared expert is present (d_shared > 0, ws1/ws3 non-NULL), Ts = T rows of
  *     the shared expert for tokens 0..T-1.  Rows p >= offsets[E] of the routed block are
- *     left untouched.  g, u are fp32 accumulations of bf16 products; h is rounded to bf16. */
+ *     left untouched.  g, u are fp32 accumulations of bf16 products.
+ *   H = I: h rounded to bf16.  H = 2I when top_k <= MOE_HSPLIT_MAX_TOP_K: h in two bf16
+ *     parts, columns [0, I) = bf16(h), [I, 2I) = bf16(h - bf16(h)) (16 significant bits;
+ *     with so few slots per token a single rounding of h would take most of the output's
+ *     error budget).  moe_expert_down reads h in the same form.  The FP8 entry points
+ *     always use H = I. */
+#define MOE_HSPLIT_MAX_TOP_K 2
 moe_status moe_expert_gate_up(const moe_dims* dims, const uint16_t* x, const int32_t* perm_rows,
                               const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                               const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, void* ws,
                               size_t ws_bytes, void* stream);
 
 /* Expert down projections ("Kimi K2 · Transformer blocks", E_i = h W2; y_shared = h W2).
- *   h as produced by moe_expert_gate_up;
+ *   h as produced by moe_expert_gate_up ([rows, H]; with H = 2I both parts are multiplied
+ *   by W2 and summed in the fp32 accumulation);
  *   y_routed [T*k, d] fp32 grouped order (rows >= offsets[E] untouched);
  *   y_shared [T, d]   fp32 (NULL iff no shared expert).  fp32 accumulation; the expert
  *   outputs stay fp32 so that the layer output is rounded to bf16 only once. */

@@ -94,11 +94,14 @@ __global__ __launch_bounds__(kGatherThreads) void combine_kernel(
   *reinterpret_cast<u32x4_t*>(out + t * d + c) = o;
 }
 
-// Latent variant: u_hat[t] = bf16(RMSNorm(sum_slot G * Y[inv[t, slot]])) with unit gain,
-// eps as given ("Kimi K3 · Latent up-projection": the routed sum on the latent width is
+// Latent variant: u_hat[t] = RMSNorm(sum_slot G * Y[inv[t, slot]]) with unit gain, eps as
+// given ("Kimi K3 · Latent up-projection": the routed sum on the latent width is
 // normalised before the up-projection).  One workgroup per token; each thread keeps up
 // to CPT 4-wide fp32 chunks of the sum, the sum of squares is reduced in a fixed tree
-// order (deterministic), and the row is scaled by 1/sqrt(mean + eps).
+// order (deterministic), and the row is scaled by 1/sqrt(mean + eps).  u_hat is the
+// up-projection's MFMA operand, written in two bf16 parts, [bf16(u_hat) | bf16(rest)]:
+// a single bf16 rounding of it would join the roundings of the latent input and of h and
+// take the output to the edge of its error bar.
 template <int KMAX, int CPT>
 __global__ __launch_bounds__(kCombineThreads) void combine_rmsnorm_kernel(
     const float* __restrict__ y_routed, const int32_t* __restrict__ inv,
@@ -166,10 +169,20 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rmsnorm_kernel(
   for (int j = 0; j < CPT; ++j) {
     const int c = tid + kCombineThreads * j;
     if (c >= nch) continue;
-    u32x2_t o;
-    o[0] = f32_to_bf16(acc[j][0] * scale) | (f32_to_bf16(acc[j][1] * scale) << 16);
-    o[1] = f32_to_bf16(acc[j][2] * scale) | (f32_to_bf16(acc[j][3] * scale) << 16);
-    *reinterpret_cast<u32x2_t*>(out + t * L + 4 * c) = o;
+    f32x4_t u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = acc[j][i] * scale;
+    u32x2_t hi, lo;
+    hi[0] = f32_to_bf16(u[0]) | (f32_to_bf16(u[1]) << 16);
+    hi[1] = f32_to_bf16(u[2]) | (f32_to_bf16(u[3]) << 16);
+    // the remainders are exact in fp32
+    lo[0] = f32_to_bf16(u[0] - bf16_to_f32(hi[0] & 0xffffu)) |
+            (f32_to_bf16(u[1] - bf16_to_f32(hi[0] >> 16)) << 16);
+    lo[1] = f32_to_bf16(u[2] - bf16_to_f32(hi[1] & 0xffffu)) |
+            (f32_to_bf16(u[3] - bf16_to_f32(hi[1] >> 16)) << 16);
+    uint16_t* row = out + t * 2 * L;
+    *reinterpret_cast<u32x2_t*>(row + 4 * c) = hi;
+    *reinterpret_cast<u32x2_t*>(row + L + 4 * c) = lo;
   }
 }
 

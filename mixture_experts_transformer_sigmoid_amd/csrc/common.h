@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/moe.h"
+
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -183,7 +185,15 @@ struct FfnShape {
   int k;        // slots per token
   int I;        // expert intermediate width
   bool shared;  // shared expert present (Is == I)
+  // h in two bf16 parts (hi = bf16(h), lo = bf16(h - hi)), rows [hi | lo] of 2I: the down
+  // GEMM then runs over K = 2I with each weight used twice (bf16 kernels only)
+  bool hsplit = false;
 };
+
+// The two-part form of h is used when a token has at most this many slots: with so few
+// gate-weighted expert rows in a token's sum, the bf16 rounding of h alone takes most of
+// the output's error budget.
+constexpr int kHsplitMaxTopK = MOE_HSPLIT_MAX_TOP_K;
 
 int64_t ffn_max_tiles(const FfnShape& sh);
 // The tiles of the bf16 and of the FP8 gate/up and down launches at this shape (both
@@ -197,9 +207,11 @@ TileSpec ffn_tile_spec_fp8(const FfnShape& sh);
 // 64-k chunks, and slice j writes its partial product to columns j N .. j N + N - 1 of
 // Cf [rows, ksplit N].
 enum class DenseOut { kF32, kBF16, kAddBF16 };
+// wk > 0: A is in two bf16 parts, rows [hi | lo] of K = 2 wk, and W is [N, wk] (no K
+// slices then).
 hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
                         DenseOut mode, float* Cf, uint16_t* Cb, const float* R, Tile* tiles,
-                        int32_t* ntiles, hipStream_t s, int ksplit = 1);
+                        int32_t* ntiles, hipStream_t s, int ksplit = 1, int wk = 0);
 
 hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* perm,
                           const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
@@ -249,7 +261,8 @@ hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float
 hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, uint16_t* out, int64_t T, int d,
                           float eps, hipStream_t s);
 
-// out[t] = bf16(RMSNorm(sum_slot topk_w * y_routed[inv])) over L features (L <= 8192).
+// u = RMSNorm(sum_slot topk_w * y_routed[inv]) over L features (L <= 8192), written in two
+// bf16 parts: out[t] = [bf16(u) | bf16(u - bf16(u))], rows of 2L.
 hipError_t launch_combine_rmsnorm(const float* y_routed, const int32_t* inv, const float* topk_w,
                                   uint16_t* out, int64_t T, int L, int k, float eps,
                                   hipStream_t s);

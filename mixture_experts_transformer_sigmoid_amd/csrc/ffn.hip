@@ -39,7 +39,10 @@ namespace {
 // activations as the B operand (16 rows), so a lane ends up with four consecutive
 // output features of one row and stores them with one 8-byte (bf16) or 16-byte (fp32)
 // write.
-template <int NF, int KU, int EPI>
+//
+// TWO: the activation rows are in two bf16 parts [hi | lo] (K = 2 WK) and the weight rows
+// have WK elements; reduction index k reads weight column k mod WK.
+template <int NF, int KU, int EPI, bool TWO = false>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int BN = 4 * 16 * NF;
@@ -50,6 +53,8 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const int K = a.K, N = a.N;
+  const int WK = TWO ? a.wk : K;
+  auto wcol = [&](int k) { return TWO && k >= WK ? k - WK : k; };
 
   int64_t p = tile.row_begin + r;
   const bool row_ok = p < tile.row_end;
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
   const uint16_t* arow = act_row(a, GATEUP, p) + q * 8;
 
   const bool is_shared = tile.group >= a.E;
-  const int64_t wofs = (int64_t)tile.group * N * K;
+  const int64_t wofs = (int64_t)tile.group * N * WK;
   const uint16_t* W1 = is_shared ? a.S1 : a.B1 + wofs;
   const uint16_t* W3 = GATEUP ? (is_shared ? a.S3 : a.B3 + wofs) : nullptr;
 
@@ -68,8 +73,8 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
   for (int f = 0; f < NF; ++f) {
     int n = n0 + 16 * f + r;
     if (n > N - 1) n = N - 1;
-    w1p[f] = W1 + (int64_t)n * K + q * 8;
-    w3p[f] = GATEUP ? W3 + (int64_t)n * K + q * 8 : nullptr;
+    w1p[f] = W1 + (int64_t)n * WK + q * 8;
+    w3p[f] = GATEUP ? W3 + (int64_t)n * WK + q * 8 : nullptr;
   }
 
   f32x4_t acc1[NF], acc3[NF];
@@ -86,8 +91,8 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
     for (int u = 0; u < KU; ++u)
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        b1v[f][u] = load16(w1p[f] + k0 + 32 * u);
-        if (GATEUP) b3v[f][u] = load16(w3p[f] + k0 + 32 * u);
+        b1v[f][u] = load16(w1p[f] + wcol(k0 + 32 * u));
+        if (GATEUP) b3v[f][u] = load16(w3p[f] + wcol(k0 + 32 * u));
       }
 #pragma unroll
     for (int u = 0; u < KU; ++u) av[u] = load16(arow + k0 + 32 * u);
@@ -104,8 +109,8 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
     const u32x4_t av = load16(arow + k0);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      acc1[f] = mfma16x16x32(load16(w1p[f] + k0), av, acc1[f]);
-      if (GATEUP) acc3[f] = mfma16x16x32(load16(w3p[f] + k0), av, acc3[f]);
+      acc1[f] = mfma16x16x32(load16(w1p[f] + wcol(k0)), av, acc1[f]);
+      if (GATEUP) acc3[f] = mfma16x16x32(load16(w3p[f] + wcol(k0)), av, acc3[f]);
     }
   }
 
@@ -156,12 +161,15 @@ struct LdsCtx {
   int wrd[4];                  // per-lane slot (16 B units) of sub-step kk's piece in the
   int ard[4];                  // wave's first weight / activation row fragment
   int nc;                      // chunks
+  int ncw;                     // chunks of a weight row: chunk c reads weight chunk c mod ncw
+                               // (ncw < nc only for two-part activations)
 };
 
 // Whole-chunk weight move, for the prologue: the wave's 8 weight transfers of chunk c
 // (units 8 wave .. 8 wave + 7).
 __device__ __forceinline__ void lds_fetch_w(const LdsCtx& x, u32x4_t* wgt, int wave, int c) {
-  const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.woob;
+  const uint32_t soff = c < x.nc ? (uint32_t)(c >= x.ncw ? c - x.ncw : c) * (kLdsChunkK * 2)
+                                  : x.woob;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     dma16(x.wgt, wgt + (wave * 8 + j) * 64, x.woff[j & 1], soff + (uint32_t)j * x.wstride);
@@ -198,7 +206,8 @@ __device__ __forceinline__ void lds_fetch_a(const LdsCtx& x, u32x4_t* act, int w
 
 __device__ __forceinline__ void lds_fetch_w4(const LdsCtx& x, u32x4_t* wgt, int wave, int c,
                                              int j0) {
-  const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.woob;
+  const uint32_t soff = c < x.nc ? (uint32_t)(c >= x.ncw ? c - x.ncw : c) * (kLdsChunkK * 2)
+                                  : x.woob;
 #pragma unroll
   for (int j = j0; j < j0 + 4; ++j)
     dma16(x.wgt, wgt + (wave * 8 + j) * 64, x.woff[j & 1], soff + (uint32_t)j * x.wstride);
@@ -317,8 +326,11 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   const int nrows = tile.row_end - tile.row_begin;
   const int f0 = nb * FEAT;
 
+  // weight row length: K, or half of it for two-part activations ([hi | lo], K = 2 WK; no K
+  // slices then)
+  const int WK = a.wk > 0 ? a.wk : K;
   const bool is_shared = tile.group >= a.E;
-  const int64_t wofs = (int64_t)tile.group * N * K;
+  const int64_t wofs = (int64_t)tile.group * N * WK;
   const uint16_t* Wa = is_shared ? a.S1 : a.B1 + wofs;
   const uint16_t* Wb = GATEUP ? (is_shared ? a.S3 : a.B3 + wofs) : Wa;
 
@@ -330,7 +342,7 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
 
   LdsCtx x;
   // one weight matrix is N*K*2 < 2^32 bytes, and so is x (checked on the host)
-  const uint32_t wbytes = (uint32_t)N * (uint32_t)K * 2u;
+  const uint32_t wbytes = (uint32_t)N * (uint32_t)WK * 2u;
   x.wgt = buffer_rsrc(GATEUP && wave >= 2 ? Wb : Wa, wbytes);
   const uint16_t* abase = GATEUP ? a.A : a.A + (int64_t)tile.row_begin * K;
   const uint32_t abytes = GATEUP ? (uint32_t)(a.a_rows * K * 2) : (uint32_t)nrows * K * 2u;
@@ -356,8 +368,8 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
     const int n0 = f0 + 64 * (GATEUP ? (wave & 1) : wave) + (lane >> 3);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      x.woff[e] = (uint32_t)n0 * (uint32_t)K * 2u + ((lane & 7) ^ (lane >> 3) ^ e) * 16 + kofs;
-    x.wstride = 8u * (uint32_t)K * 2u;
+      x.woff[e] = (uint32_t)n0 * (uint32_t)WK * 2u + ((lane & 7) ^ (lane >> 3) ^ e) * 16 + kofs;
+    x.wstride = 8u * (uint32_t)WK * 2u;
   }
   // the two row halves interleave 32-row fragments (wave wm: tile rows 64 t + 32 wm ..),
   // so a partly filled tile keeps both halves equally busy
@@ -375,6 +387,7 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
     }
   }
   x.nc = c1 - c0;
+  x.ncw = WK < K ? WK / kLdsChunkK : x.nc;
   // both buffers are under 2 GiB (checked on the host), so offset + this stays in 32 bits
   x.aoob = abytes;
   x.woob = wbytes;
@@ -417,9 +430,11 @@ void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a) {
 
 hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
                         DenseOut mode, float* Cf, uint16_t* Cb, const float* R, Tile* tiles,
-                        int32_t* ntiles, hipStream_t s, int ksplit) {
+                        int32_t* ntiles, hipStream_t s, int ksplit, int wk) {
   // the epilogues store whole 4-output groups: an output row must be a multiple of 4
   if ((N & 3) != 0) return hipErrorInvalidValue;
+  // two-part activations: K = 2 wk, no K slices
+  if (wk > 0 && (K != 2 * wk || ksplit > 1)) return hipErrorInvalidValue;
   // one group (the "shared" slot of the tile list) whose rows are all the rows of A
   const FfnShape sh{rows, K, 0, 0, N, true};
   const bool wide = rows > kSingleGroupWideRows;
@@ -439,6 +454,7 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
   a.k = 1;
   a.N = N;
   a.K = K;
+  a.wk = wk;
   a.E = 0;
   // K slices only on the 256-row kernel's fp32 output, each at least one 64-k chunk
   const int nks = (mode == DenseOut::kF32 && wide && ksplit > 1)
@@ -448,17 +464,21 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
   a.ldc = nks * N;
   const dim3 gs = grid_for(sh, BM, kWideBNDown, N), gk = grid_for(sh, BM, 64, N),
              gk2 = grid_for(sh, BM, 128, N);
+  const bool two = wk > 0;
   switch (mode) {
     case DenseOut::kF32:
       if (wide) launch_wide<kF32>(dim3(gs.x * nks), s, a);
+      else if (two) hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, kF32, true>), gk, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, kF32>), gk, dim3(256), 0, s, a);
       break;
     case DenseOut::kBF16:
       if (wide) launch_wide<kBF16>(gs, s, a);
+      else if (two) hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kBF16, true>), gk2, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kBF16>), gk2, dim3(256), 0, s, a);
       break;
     case DenseOut::kAddBF16:
       if (wide) launch_wide<kAddBF16>(gs, s, a);
+      else if (two) hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kAddBF16, true>), gk2, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kAddBF16>), gk2, dim3(256), 0, s, a);
       break;
   }
@@ -491,6 +511,7 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   a.N = sh.I;
   a.K = sh.d;
   a.E = sh.E;
+  a.hsplit = sh.hsplit ? 1 : 0;
   if (wide)
     launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a);
   else
@@ -524,10 +545,15 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.ntiles = ntiles;
   a.k = sh.k;
   a.N = sh.d;
-  a.K = sh.I;
+  // h in two bf16 parts: rows [hi | lo] of 2I, each weight used for both
+  a.K = sh.hsplit ? 2 * sh.I : sh.I;
+  a.wk = sh.hsplit ? sh.I : 0;
   a.E = sh.E;
   if (wide)
     launch_wide<kF32>(grid_for(sh, BM, kWideBNDown, a.N), s, a);
+  else if (sh.hsplit)
+    hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32, true>),
+                       grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);

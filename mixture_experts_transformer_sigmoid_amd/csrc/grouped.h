@@ -35,6 +35,9 @@ struct FfnArgs {
   int32_t N, K, E;
   int32_t ksplit;         // 256-row kernel, fp32 output: K slices (0 or 1: none)
   int32_t ldc;            // row stride of Ys (0: N); slice j writes from column j N
+  int32_t wk;             // > 0: A in two bf16 parts ([hi | lo], K = 2 wk) and weight rows
+                          // of wk; reduction index k reads weight column k mod wk
+  int32_t hsplit;         // gate/up: write h in two bf16 parts, rows [hi | lo] of 2N
   int64_t a_rows;         // rows of A (gate/up: tokens of x)
   const float* R;         // kAddBF16: fp32 rows added before the bf16 store
   // FP8 kernels only: E4M3 codes with the layouts of B1, B3, S1, S3, and their fp32
@@ -80,14 +83,37 @@ __device__ __forceinline__ const uint16_t* act_row(const FfnArgs& a, bool gateup
   return a.A + tok * a.K;
 }
 
-__device__ __forceinline__ void store_gateup(uint16_t* dst, f32x4_t g, f32x4_t u) {
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = swiglu_f32(g[i], u[i]);
+// Four consecutive h values as bf16 at dst; with lo non-null also their remainders
+// bf16(h - bf16(h)) at lo (the remainder is exact in fp32, its rounding leaves h with 16
+// significant bits in the two parts).
+__device__ __forceinline__ void store_h4(uint16_t* dst, uint16_t* lo, f32x4_t v) {
   u32x2_t packed;
   packed[0] = pack_bf16x2(v[0], v[1]);
   packed[1] = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<u32x2_t*>(dst) = packed;
+  if (lo != nullptr) {
+    u32x2_t rest;
+    rest[0] = pack_bf16x2(v[0] - __uint_as_float(packed[0] << 16),
+                          v[1] - __uint_as_float(packed[0] & 0xffff0000u));
+    rest[1] = pack_bf16x2(v[2] - __uint_as_float(packed[1] << 16),
+                          v[3] - __uint_as_float(packed[1] & 0xffff0000u));
+    *reinterpret_cast<u32x2_t*>(lo) = rest;
+  }
+}
+
+// h = silu(g) u for four outputs (features nn .. nn + 3) of grouped row p, in one or two
+// bf16 parts.
+__device__ __forceinline__ void store_gateup(const FfnArgs& a, int64_t p, int nn, f32x4_t g,
+                                             f32x4_t u) {
+  f32x4_t v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = swiglu_f32(g[i], u[i]);
+  if (a.hsplit) {
+    uint16_t* row = a.C + p * 2 * a.N;
+    store_h4(row + nn, row + a.N + nn, v);
+  } else {
+    store_h4(a.C + p * a.N + nn, nullptr, v);
+  }
 }
 
 // Store four consecutive outputs (features nn .. nn+3) of grouped row p.  Every output
@@ -100,7 +126,7 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
                                        f32x4_t u, int col0 = 0) {
   const int N = a.N;
   if (EPI == kSwiGLU) {
-    store_gateup(a.C + p * N + nn, v, u);
+    store_gateup(a, p, nn, v, u);
   } else if (EPI == kF32) {
     float* yrow = p < a.routed_rows ? a.Y + p * N
                                     : a.Ys + (p - a.routed_rows) * (a.ldc ? a.ldc : N) + col0;
@@ -181,8 +207,19 @@ __device__ __forceinline__ void lds_epilogue(const FfnArgs& a, u32x4_t* stage,
       const f32x4_t v = __builtin_bit_cast(f32x4_t, stage[r * PPR + (pr ^ (r & 7))]);
       const int m = arow + tstride * t + r;
       const int nn = nbase + 4 * pr;
-      if (m < nrows && nn < a.N)
-        store_row4<GATEUP ? kBF16 : EPI>(a, tile.row_begin + m, nn, v, col0);
+      if (m < nrows && nn < a.N) {
+        if constexpr (GATEUP) {
+          const int64_t p = tile.row_begin + m;
+          if (a.hsplit) {
+            uint16_t* row = a.C + p * 2 * a.N;
+            store_h4(row + nn, row + a.N + nn, v);
+          } else {
+            store_h4(a.C + p * a.N + nn, nullptr, v);
+          }
+        } else {
+          store_row4<EPI>(a, tile.row_begin + m, nn, v, col0);
+        }
+      }
     }
   }
 }

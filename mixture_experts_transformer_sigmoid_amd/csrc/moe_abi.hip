@@ -63,6 +63,12 @@ size_t router_wsplit_bytes(const moe_dims& d) {
   return 3 * (size_t)moe::router_part_rows(d.n_experts) * d.d_model * 2;
 }
 
+bool hsplit(const moe_dims& d) { return d.top_k <= moe::kHsplitMaxTopK; }
+
+// Columns of h per row: I, or 2I when h is kept in two bf16 parts (bf16 weights, few slots
+// per token).
+size_t h_width(const moe_dims& d) { return (hsplit(d) ? 2 : 1) * (size_t)d.d_expert; }
+
 struct Layout {
   size_t zpart, wsplit, idx, w, counts, offsets, perm, inv, hist, base, tiles, ntiles, h, y,
       total;
@@ -95,7 +101,7 @@ Layout layout(const moe_dims& d) {
   L.base = take(nb * E * 4);
   L.tiles = take(max_tiles * sizeof(Tile));
   L.ntiles = take(4);
-  L.h = take(rows * (size_t)d.d_expert * 2);
+  L.h = take(rows * h_width(d) * 2);
   L.y = take(rows * (size_t)d.d_model * 4);
   L.total = off;
   return L;
@@ -115,7 +121,13 @@ moe_status check_ws(const moe_dims& d, const void* ws, size_t ws_bytes) {
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 FfnShape ffn_shape(const moe_dims& d) {
-  return FfnShape{d.tokens, d.d_model, d.n_experts, d.top_k, d.d_expert, has_shared(d)};
+  return FfnShape{d.tokens, d.d_model, d.n_experts, d.top_k, d.d_expert, has_shared(d),
+                  hsplit(d)};
+}
+
+// The FP8 kernels keep h in one bf16 part.
+FfnShape ffn_shape_fp8(const moe_dims& d) {
+  return FfnShape{d.tokens, d.d_model, d.n_experts, d.top_k, d.d_expert, has_shared(d), false};
 }
 
 #define MOE_TRY(expr)                 \
@@ -227,10 +239,10 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
   P.tiles = take(max_tiles * sizeof(Tile));
   P.ntiles = take(4);
   P.lat = take(T * (size_t)L * 2);
-  P.h = take(slots * (size_t)d.d_expert * 2);
-  P.hs = take(has_shared(d) ? T * (size_t)d.d_shared * 2 : 0);
+  P.h = take(slots * h_width(d) * 2);
+  P.hs = take(has_shared(d) ? T * h_width(d) * 2 : 0);
   P.y = take(slots * (size_t)L * 4);
-  P.uhat = take(T * (size_t)L * 2);
+  P.uhat = take(T * (size_t)L * 2 * 2);  // two bf16 parts
   P.ys = take(has_shared(d) ? T * (size_t)d.d_model * 4 : 0);
   P.total = off;
   return P;
@@ -368,7 +380,7 @@ moe_status moe_expert_gate_up_fp8(const moe_dims* dims, const uint16_t* x,
   MOE_TRY(check_ws(d, ws, ws_bytes));
   (void)hipGetLastError();
   const Layout L = layout(d);
-  return hip_status(moe::launch_gate_up_fp8(ffn_shape(d), x, perm_rows, offsets, fp8_of(*w), h,
+  return hip_status(moe::launch_gate_up_fp8(ffn_shape_fp8(d), x, perm_rows, offsets, fp8_of(*w), h,
                                             at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
                                             (hipStream_t)stream));
 }
@@ -385,7 +397,7 @@ moe_status moe_expert_down_fp8(const moe_dims* dims, const uint16_t* h, const in
   MOE_TRY(check_ws(d, ws, ws_bytes));
   (void)hipGetLastError();
   const Layout L = layout(d);
-  return hip_status(moe::launch_down_fp8(ffn_shape(d), h, offsets, fp8_of(*w), y_routed,
+  return hip_status(moe::launch_down_fp8(ffn_shape_fp8(d), h, offsets, fp8_of(*w), y_routed,
                                          has_shared(d) ? y_shared : nullptr,
                                          at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
                                          (hipStream_t)stream));
@@ -413,13 +425,13 @@ moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float*
   float* y_routed = at<float>(ws, L.y);
   float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
   const moe::Fp8Weights fw = fp8_of(*w);
-  const moe::TileSpec ts = moe::ffn_tile_spec_fp8(ffn_shape(d));
+  const moe::TileSpec ts = moe::ffn_tile_spec_fp8(ffn_shape_fp8(d));
   MOE_TRY(route_impl(d, x, w_router, bias, idx, gw, nullptr, ws, s));
   MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s, &ts));
-  MOE_TRY(hip_status(moe::launch_gate_up_fp8(ffn_shape(d), x, perm, offsets, fw, h,
+  MOE_TRY(hip_status(moe::launch_gate_up_fp8(ffn_shape_fp8(d), x, perm, offsets, fw, h,
                                              at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
                                              s, true)));
-  MOE_TRY(hip_status(moe::launch_down_fp8(ffn_shape(d), h, offsets, fw, y_routed, y_shared,
+  MOE_TRY(hip_status(moe::launch_down_fp8(ffn_shape_fp8(d), h, offsets, fw, y_routed, y_shared,
                                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
                                           s, true)));
   return combine_impl(d, y_routed, inv, gw, y_shared, out, s);
@@ -613,7 +625,7 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
   MOE_TRY(hip_status(moe::launch_dense(x, T, d.d_model, w_down, L, moe::DenseOut::kBF16, nullptr,
                                        lat, nullptr, tiles, ntiles, s)));
   // routed experts on the latent
-  const FfnShape rsh{T, L, d.n_experts, d.top_k, d.d_expert, false};
+  const FfnShape rsh{T, L, d.n_experts, d.top_k, d.d_expert, false, hsplit(d)};
   MOE_TRY(hip_status(moe::launch_gate_up(rsh, lat, perm, offsets, w1, w3, nullptr, nullptr, h,
                                          tiles, ntiles, s)));
   MOE_TRY(hip_status(
@@ -622,19 +634,21 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
   MOE_TRY(hip_status(moe::launch_combine_rmsnorm(y, inv, w, uhat, T, L, d.top_k, 1e-6f, s)));
   if (has_shared(d)) {
     // shared expert on the full-width input: a T-row group with no routed experts
-    const FfnShape ssh{T, d.d_model, 0, 0, d.d_shared, true};
+    const FfnShape ssh{T, d.d_model, 0, 0, d.d_shared, true, hsplit(d)};
     uint16_t* hs = at<uint16_t>(ws, P.hs);
     float* ys = at<float>(ws, P.ys);
     MOE_TRY(hip_status(moe::launch_gate_up(ssh, x, nullptr, nullptr, nullptr, nullptr, ws1, ws3,
                                            hs, tiles, ntiles, s)));
     MOE_TRY(hip_status(moe::launch_down(ssh, hs, nullptr, nullptr, ws2, nullptr, ys, tiles, ntiles,
                                         s, true)));
-    // up-projection with the shared output added before the one bf16 rounding
-    return hip_status(moe::launch_dense(uhat, T, L, w_up, d.d_model, moe::DenseOut::kAddBF16,
-                                        nullptr, out, ys, tiles, ntiles, s));
+    // up-projection (u_hat in two bf16 parts) with the shared output added before the one
+    // bf16 rounding
+    return hip_status(moe::launch_dense(uhat, T, 2 * L, w_up, d.d_model,
+                                        moe::DenseOut::kAddBF16, nullptr, out, ys, tiles, ntiles,
+                                        s, 1, L));
   }
-  return hip_status(moe::launch_dense(uhat, T, L, w_up, d.d_model, moe::DenseOut::kBF16, nullptr,
-                                      out, nullptr, tiles, ntiles, s));
+  return hip_status(moe::launch_dense(uhat, T, 2 * L, w_up, d.d_model, moe::DenseOut::kBF16,
+                                      nullptr, out, nullptr, tiles, ntiles, s, 1, L));
 }
 
 }  // extern "C"

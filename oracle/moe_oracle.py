@@ -262,6 +262,9 @@ def swiglu(x_rows, w1, w3, w2, bf16_points=()):
     h = silu(g) * u
     if "h" in bf16_points:
         h = round_bf16(h)
+    elif "h2" in bf16_points:
+        hi = round_bf16(h)
+        h = hi + round_bf16(h - hi)
     return h @ _f64(w2).T
 
 
@@ -271,6 +274,7 @@ def swiglu(x_rows, w1, w3, w2, bf16_points=()):
 # a difference between the HIP path and the exact oracle can be attributed to a precision
 # schedule rather than to a mistake.  The points:
 #   "h"           the SwiGLU hidden row, before the down projection
+#   "h2"          the same row kept as two bf16 parts, bf16(h) + bf16(h - bf16(h))
 #   "expert_out"  each expert's output row E_i
 #   "y_routed"    the gate-weighted sum over the k slots
 #   "y_shared"    the shared expert's output
@@ -279,9 +283,11 @@ def swiglu(x_rows, w1, w3, w2, bf16_points=()):
 # up-projection", moe_infer: expert outputs in the module dtype, weighted sum taken in
 # fp32 and cast back; the shared output added in the module dtype).
 # KERNEL_BF16_POINTS: the HIP path's schedule (h is the down GEMM's bf16 operand; expert
-# outputs, the weighted sum and the shared output stay fp32; one final rounding).
+# outputs, the weighted sum and the shared output stay fp32; one final rounding), and
+# KERNEL_BF16_POINTS_TWO_PART the same with h in two bf16 parts (top_k <= 2).
 PAGE_BF16_POINTS = ("h", "expert_out", "y_routed", "y_shared", "out")
 KERNEL_BF16_POINTS = ("h", "out")
+KERNEL_BF16_POINTS_TWO_PART = ("h2", "out")
 
 
 def _expert_getter(w1, w3, w2):

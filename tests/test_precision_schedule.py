@@ -107,9 +107,9 @@ def test_bf16_points_change_values_by_rounding_only():
         assert 0 < d.max() < 2.0 ** -6 * np.abs(exact).max()
 
 
-def _replay_ratio(cfg, seed, bias=None):
-    """max |kernel-schedule replay - exact| / RMS(exact) over the tokens outside the
-    near-tie window, on the GPU tests' seeded inputs."""
+def _replay_ratio(cfg, seed, bias=None, points=mo.KERNEL_BF16_POINTS):
+    """max |schedule replay - exact| / RMS(exact) over the tokens outside the near-tie
+    window, on the GPU tests' seeded inputs."""
     inp = S.make_inputs(cfg, "cpu", seed=seed)
     if bias is not None:
         inp["b"] = bias
@@ -119,7 +119,7 @@ def _replay_ratio(cfg, seed, bias=None):
               routing=r)
     exact = mo.moe_sparse(f["x"], None, None, cfg["top_k"], cfg["routed_scale"], **kw)["out"]
     replay = mo.moe_sparse(f["x"], None, None, cfg["top_k"], cfg["routed_scale"],
-                           bf16_points=mo.KERNEL_BF16_POINTS, **kw)["out"]
+                           bf16_points=points, **kw)["out"]
     keep = r["gap"] >= 1e-6
     return np.abs(replay - exact)[keep].max() / np.sqrt(np.mean(exact[keep] ** 2))
 
@@ -131,7 +131,7 @@ def _same_experts_bias(n, top):
 
 
 SHAPES = {
-    # name: (config, seed, bias, ratio range of the replay)
+    # name: (config, seed, bias, ratio range of the replay with h rounded once to bf16)
     "tiny (64 tokens, k 2)": (S.CONFIGS["tiny"], 0, None, (0.010, 0.020)),
     "tiny, 300 tokens all on experts 0-1 (k 2)": (
         S.with_overrides("tiny", tokens=300), 6, _same_experts_bias(16, 2), (0.020, 0.030)),
@@ -143,6 +143,12 @@ SHAPES = {
     "d 128, E 7, I 64, 600 tokens, k 3": (
         dict(tokens=600, d_model=128, n_experts=7, top_k=3, d_expert=64, d_shared=64,
              routed_scale=2.827, bias="uniform"), 27, None, (0.010, 0.020)),
+    "d 128, E 7, I 64, 600 tokens, k 1": (
+        dict(tokens=600, d_model=128, n_experts=7, top_k=1, d_expert=64, d_shared=64,
+             routed_scale=2.827, bias="uniform"), 27, None, (0.020, 0.030)),
+    "d 128, E 1024, I 64, 4096 tokens, k 8": (
+        dict(tokens=4096, d_model=128, n_experts=1024, top_k=8, d_expert=64, d_shared=64,
+             routed_scale=2.827, bias="uniform"), 0, None, (0.020, 0.030)),
 }
 
 
@@ -154,3 +160,31 @@ def test_kernel_schedule_limits(name):
     ratio = _replay_ratio(cfg, seed, bias)
     print(f"{name}: schedule replay max|err| / RMS = {ratio:.4f}")
     assert lo <= ratio < hi, ratio
+
+
+@pytest.mark.parametrize("name", [n for n in SHAPES if SHAPES[n][0]["top_k"] <= 2])
+def test_two_part_h_holds_the_bar_at_few_slots(name):
+    """With at most two slots per token the kernels keep h in two bf16 parts (16
+    significant bits); the replay of that schedule is inside the bar with margin on every
+    shape where the single rounding is not."""
+    cfg, seed, bias, _ = SHAPES[name]
+    ratio = _replay_ratio(cfg, seed, bias, mo.KERNEL_BF16_POINTS_TWO_PART)
+    print(f"{name}: two-part-h replay max|err| / RMS = {ratio:.4f}")
+    assert ratio < 0.018, ratio
+
+
+def test_two_part_h_replay_against_torch():
+    """The "h2" point: torch's bf16 cast of h plus the cast of its remainder."""
+    L = _layer(43)
+    r = mo.route(L["x"], L["w_r"], L["b"], L["k"])
+    x = _t(L["x"])
+    got = mo.moe_sparse(L["x"], L["w_r"], L["b"], L["k"], w1=L["w1"], w3=L["w3"], w2=L["w2"],
+                        shared=None, routing=r, bf16_points=("h2",))["y_routed"]
+    want = torch.zeros(x.shape[0], x.shape[1], dtype=torch.float64)
+    for t in range(x.shape[0]):
+        for j in range(L["k"]):
+            e = int(r["topk_idx"][t, j])
+            h = F.silu(F.linear(x[t], _t(L["w1"][e]))) * F.linear(x[t], _t(L["w3"][e]))
+            hi = _bf(h)
+            want[t] += float(r["topk_w"][t, j]) * F.linear(hi + _bf(h - hi), _t(L["w2"][e]))
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-9, atol=1e-12)
