@@ -171,7 +171,7 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
  * the module's load until the process ends).  The call itself allocates nothing.
  *   - Limit: moe_workspace_bytes(dims) <= MOE_NOALLOC_SCRATCH_BYTES, else MOE_ESCRATCH
  *     before anything is launched.  At the K2 shape (d 7168, 384 experts, top-8, I 2048,
- *     shared expert) that admits up to 404 tokens.
+ *     shared expert) that admits up to 450 tokens.
  *   - The array of the CURRENT device is used: `stream` must belong to it.
  *   - Every call on one GPU shares that GPU's array.  Calls that overlap on one GPU (on
  *     different streams, or from different host threads without ordering) race on it and

@@ -127,15 +127,14 @@ struct TileSpec {
   int64_t capacity;     // entries the list has room for
 };
 
-// Router: w_split [3 router_part_rows(E), d] bf16 and z_part (router_zpart_floats) fp32
-// are workspace;
-// logits may be null.  Up to kRouterSmallT tokens take the K-sliced small kernel, whose
-// partial logits need kRouterKSplit times the room.
+// Router.  Up to kRouterSmallT tokens, one kernel computes each (16 tokens x 16 experts)
+// tile of z over the whole K with the sigmoid and the bias in its epilogue, and writes the
+// biased scores and the sigmoids, [T, E] fp32 each (router_zpart_floats holds both); the
+// top-k and the gates are then taken per token by one wave of the selection launch.
+// Above it, the bf16 (hi, mid, lo) copy
+// of W_r (w_split, [3 router_part_rows(E), d]) feeds the 256-row GEMM kernel, whose
+// partial logits (z_part) the selection kernel adds in fp64.  logits may be null.
 constexpr int64_t kRouterSmallT = 512;
-#ifndef MOE_ROUTER_KSPLIT
-#define MOE_ROUTER_KSPLIT 8
-#endif
-constexpr int kRouterKSplit = MOE_ROUTER_KSPLIT;
 // Rows per part (hi, mid, lo) of the split router weights and of the partial logits the
 // 256-row kernel writes: E rounded up to a multiple of 4 (the padding rows are zero).
 inline int router_part_rows(int E) { return (E + 3) / 4 * 4; }
@@ -162,20 +161,55 @@ inline int router_ksplit(int64_t T, int E, int d) {
   return best;
 }
 inline int64_t router_zpart_floats(int64_t T, int E, int d) {
-  return T <= kRouterSmallT ? T * 3 * E * kRouterKSplit
+  return T <= kRouterSmallT ? 2 * T * E
                             : T * 3 * router_part_rows(E) * router_ksplit(T, E, d);
 }
+
+// The pre-MoE RMSNorm done inside the small-batch router's pass over the residual stream:
+// x_ffn[t] = bf16(x'[t] / sqrt(mean(x'[t]^2) + eps) * gain), written to x_ffn.
+struct RouterNorm {
+  const float* gain;
+  float eps;
+  uint16_t* x_ffn;
+};
+
+// Up to kRouterSmallT tokens: the scores (score = fl32(sigmoid(z) + b), NaN -> -inf) and
+// sigmoids [T, E] fp32; with norm non-null, x is the residual stream and the router reads
+// its normalised rows (and writes them to norm->x_ffn).
+hipError_t launch_router_scores(const uint16_t* x, const RouterNorm* norm, const float* w_r,
+                                const float* bias, int64_t T, int d, int E, float* score,
+                                float* sig, float* logits, hipStream_t s);
+
+// The whole routing: scores and selection (two launches up to kRouterSmallT tokens), or the
+// split, GEMM and selection launches above.
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
                          int E, int k, float alpha, uint16_t* w_split, float* z_part,
                          Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,
                          float* topk_w, hipStream_t s);
 
+// The per-token top-k of launch_router_scores' output, written to idx / w.
+hipError_t launch_router_select(const float* score, const float* sig, int64_t T, int E, int k,
+                                float alpha, int32_t* idx, float* w, hipStream_t s);
+
+// The selection handed to the permutation: launch_router_scores' output, the routing
+// constants, and where the chosen experts and gates go.
+struct SelectIn {
+  const float* score;
+  const float* sig;
+  float alpha;
+  int32_t* idx;
+  float* w;
+};
+
 // ts (or null): also build the tile list of a grouped launch for the new offsets into
 // tiles / ntiles, so that the launch can skip building it.
+// sel (or null): the top-k is first taken from sel's scores by the selection launch
+// (topk_idx is then ignored and sel->idx, sel->w are written).
 hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* hist,
                           int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm,
                           int32_t* inv, hipStream_t s, const TileSpec* ts = nullptr,
-                          Tile* tiles = nullptr, int32_t* ntiles = nullptr);
+                          Tile* tiles = nullptr, int32_t* ntiles = nullptr,
+                          const SelectIn* sel = nullptr);
 int64_t permute_blocks(int64_t T);
 
 struct FfnShape {

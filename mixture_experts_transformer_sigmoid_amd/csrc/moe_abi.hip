@@ -248,17 +248,72 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
   return P;
 }
 
-// The layer on an already-normalised bf16 input x; residual (or null) is added to the
-// output before its rounding.  Arguments checked by the callers.
-moe_status forward_impl(const moe_dims& d, const uint16_t* x, const float* w_router,
-                        const float* bias, const uint16_t* w1, const uint16_t* w3,
-                        const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
-                        const uint16_t* ws2, const uint16_t* residual, uint16_t* out, void* ws,
-                        hipStream_t s) {
+// Routing and permutation of a layer entry point, into the workspace arrays at the given
+// offsets (and the tile list of ts when ts is non-null).  Up to kRouterSmallT tokens: the
+// router kernel writes scores and sigmoids and the permutation takes the top-k itself (in
+// its prologue up to 256 tokens, else as a launch of its own).  With norm non-null, x is
+// the residual stream x' and the experts' input x_ffn = RMSNorm(x') goes to norm->x_ffn:
+// written by the router kernel up to kRouterSmallT tokens, else by the norm kernel before
+// the router.  The experts' input (x, or norm->x_ffn) is returned through x_in.
+struct RouteBufs {
+  size_t zpart, wsplit, idx, w, counts, offsets, perm, inv, hist, base, tiles, ntiles;
+};
+
+template <typename LayoutT>
+RouteBufs route_bufs(const LayoutT& L) {
+  return RouteBufs{L.zpart, L.wsplit, L.idx, L.w, L.counts, L.offsets,
+                   L.perm,  L.inv,    L.hist, L.base, L.tiles, L.ntiles};
+}
+
+moe_status route_permute(const moe_dims& d, const uint16_t* x, const moe::RouterNorm* norm,
+                         const float* w_router, const float* bias, void* ws, const RouteBufs& B,
+                         const moe::TileSpec* ts, hipStream_t s, const uint16_t** x_in) {
+  const int64_t T = d.tokens;
+  const int E = d.n_experts;
+  int32_t* idx = at<int32_t>(ws, B.idx);
+  float* w = at<float>(ws, B.w);
+  moe::Tile* tiles = at<Tile>(ws, B.tiles);
+  int32_t* ntiles = at<int32_t>(ws, B.ntiles);
+  int32_t* hist = at<int32_t>(ws, B.hist);
+  int32_t* base = at<int32_t>(ws, B.base);
+  int32_t* counts = at<int32_t>(ws, B.counts);
+  int32_t* offsets = at<int32_t>(ws, B.offsets);
+  int32_t* perm = at<int32_t>(ws, B.perm);
+  int32_t* inv = at<int32_t>(ws, B.inv);
+  if (T <= moe::kRouterSmallT) {
+    float* score = at<float>(ws, B.zpart);
+    float* sig = score + T * E;
+    MOE_TRY(hip_status(moe::launch_router_scores(x, norm, w_router, bias, T, d.d_model, E, score,
+                                                 sig, nullptr, s)));
+    *x_in = norm != nullptr ? norm->x_ffn : x;
+    const moe::SelectIn sel{score, sig, d.routed_scale, idx, w};
+    return hip_status(moe::launch_permute(nullptr, T, E, d.top_k, hist, base, counts, offsets,
+                                          perm, inv, s, ts, tiles, ntiles, &sel));
+  }
+  if (norm != nullptr) {
+    MOE_TRY(hip_status(
+        moe::launch_rmsnorm(x, norm->gain, norm->x_ffn, T, d.d_model, norm->eps, s)));
+    x = norm->x_ffn;
+  }
+  *x_in = x;
+  MOE_TRY(hip_status(moe::launch_router(x, w_router, bias, T, d.d_model, E, d.top_k,
+                                        d.routed_scale, at<uint16_t>(ws, B.wsplit),
+                                        at<float>(ws, B.zpart), tiles, ntiles, nullptr, idx, w,
+                                        s)));
+  return hip_status(moe::launch_permute(idx, T, E, d.top_k, hist, base, counts, offsets, perm,
+                                        inv, s, ts, tiles, ntiles));
+}
+
+// The layer; with norm non-null, x is the residual stream and the layer runs on its
+// RMSNorm (moe_forward_block).  residual (or null) is added to the output before its
+// rounding.  Arguments checked by the callers.
+moe_status forward_impl(const moe_dims& d, const uint16_t* x, const moe::RouterNorm* norm,
+                        const float* w_router, const float* bias, const uint16_t* w1,
+                        const uint16_t* w3, const uint16_t* w2, const uint16_t* ws1,
+                        const uint16_t* ws3, const uint16_t* ws2, const uint16_t* residual,
+                        uint16_t* out, void* ws, hipStream_t s) {
   const Layout L = layout(d);
-  int32_t* idx = at<int32_t>(ws, L.idx);
   float* w = at<float>(ws, L.w);
-  int32_t* counts = at<int32_t>(ws, L.counts);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm = at<int32_t>(ws, L.perm);
   int32_t* inv = at<int32_t>(ws, L.inv);
@@ -266,9 +321,9 @@ moe_status forward_impl(const moe_dims& d, const uint16_t* x, const float* w_rou
   float* y_routed = at<float>(ws, L.y);
   float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
   const moe::TileSpec ts = moe::ffn_tile_spec(ffn_shape(d));
-  MOE_TRY(route_impl(d, x, w_router, bias, idx, w, nullptr, ws, s));
-  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s, &ts));
-  MOE_TRY(gate_up_impl(d, x, perm, offsets, w1, w3, ws1, ws3, h, ws, s, true));
+  const uint16_t* x_in = nullptr;
+  MOE_TRY(route_permute(d, x, norm, w_router, bias, ws, route_bufs(L), &ts, s, &x_in));
+  MOE_TRY(gate_up_impl(d, x_in, perm, offsets, w1, w3, ws1, ws3, h, ws, s, true));
   MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s, true));
   return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, residual, out, d.tokens,
                                         d.d_model, d.top_k, s));
@@ -346,7 +401,7 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
   MOE_NEED(aligned(x, 16));
   MOE_TRY(check_forward_args(d, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, ws, ws_bytes));
   (void)hipGetLastError();
-  return forward_impl(d, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, nullptr, out, ws,
+  return forward_impl(d, x, nullptr, w_router, bias, w1, w3, w2, ws1, ws3, ws2, nullptr, out, ws,
                       (hipStream_t)stream);
 }
 
@@ -364,7 +419,7 @@ moe_status moe_forward_noalloc(const moe_dims* dims, const uint16_t* x, const fl
   void* ws = nullptr;
   MOE_TRY(noalloc_scratch(&ws));
   (void)hipGetLastError();
-  return forward_impl(d, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, nullptr, out, ws,
+  return forward_impl(d, x, nullptr, w_router, bias, w1, w3, w2, ws1, ws3, ws2, nullptr, out, ws,
                       (hipStream_t)stream);
 }
 
@@ -415,9 +470,7 @@ moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float*
   (void)hipGetLastError();
   const hipStream_t s = (hipStream_t)stream;
   const Layout L = layout(d);
-  int32_t* idx = at<int32_t>(ws, L.idx);
   float* gw = at<float>(ws, L.w);
-  int32_t* counts = at<int32_t>(ws, L.counts);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm = at<int32_t>(ws, L.perm);
   int32_t* inv = at<int32_t>(ws, L.inv);
@@ -426,8 +479,8 @@ moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float*
   float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
   const moe::Fp8Weights fw = fp8_of(*w);
   const moe::TileSpec ts = moe::ffn_tile_spec_fp8(ffn_shape_fp8(d));
-  MOE_TRY(route_impl(d, x, w_router, bias, idx, gw, nullptr, ws, s));
-  MOE_TRY(permute_impl(d, idx, counts, offsets, perm, inv, ws, s, &ts));
+  const uint16_t* x_in = nullptr;
+  MOE_TRY(route_permute(d, x, nullptr, w_router, bias, ws, route_bufs(L), &ts, s, &x_in));
   MOE_TRY(hip_status(moe::launch_gate_up_fp8(ffn_shape_fp8(d), x, perm, offsets, fw, h,
                                              at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
                                              s, true)));
@@ -459,9 +512,11 @@ moe_status moe_forward_block(const moe_dims* dims, const uint16_t* x_res, const 
   if (ws_bytes < base + align_up((size_t)d.tokens * d.d_model * 2)) return MOE_EWORKSPACE;
   (void)hipGetLastError();
   const hipStream_t s = (hipStream_t)stream;
-  uint16_t* x_ffn = at<uint16_t>(ws, base);
-  MOE_TRY(hip_status(moe::launch_rmsnorm(x_res, norm_w, x_ffn, d.tokens, d.d_model, norm_eps, s)));
-  return forward_impl(d, x_ffn, w_router, bias, w1, w3, w2, ws1, ws3, ws2, x_res, out, ws, s);
+  // x_ffn = RMSNorm(x_res) goes to the end of the workspace, made by the router kernel's
+  // own pass over x_res up to kRouterSmallT tokens (else by the norm kernel)
+  const moe::RouterNorm norm{norm_w, norm_eps, at<uint16_t>(ws, base)};
+  return forward_impl(d, x_res, &norm, w_router, bias, w1, w3, w2, ws1, ws3, ws2, x_res, out, ws,
+                      s);
 }
 
 const char* moe_status_str(int status) {
@@ -601,7 +656,6 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
   (void)hipGetLastError();
   const hipStream_t s = (hipStream_t)stream;
   const int64_t T = d.tokens;
-  int32_t* idx = at<int32_t>(ws, P.idx);
   float* w = at<float>(ws, P.w);
   int32_t* offsets = at<int32_t>(ws, P.offsets);
   int32_t* perm = at<int32_t>(ws, P.perm);
@@ -613,14 +667,10 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
   float* y = at<float>(ws, P.y);
   uint16_t* uhat = at<uint16_t>(ws, P.uhat);
   // router on the full-width input ("Kimi K3 · Latent up-projection": the gate scores
-  // hidden_states before the down-projection)
-  MOE_TRY(hip_status(moe::launch_router(x, w_router, bias, T, d.d_model, d.n_experts, d.top_k,
-                                        d.routed_scale, at<uint16_t>(ws, P.wsplit),
-                                        at<float>(ws, P.zpart), tiles, ntiles, nullptr, idx, w,
-                                        s)));
-  MOE_TRY(hip_status(moe::launch_permute(idx, T, d.n_experts, d.top_k, at<int32_t>(ws, P.hist),
-                                         at<int32_t>(ws, P.base), at<int32_t>(ws, P.counts),
-                                         offsets, perm, inv, s)));
+  // hidden_states before the down-projection), and the permutation
+  const uint16_t* x_in = nullptr;
+  MOE_TRY(route_permute(d, x, nullptr, w_router, bias, ws, route_bufs(P), nullptr, s, &x_in));
+  (void)x_in;
   // down-projection to the latent width (bf16: the experts' MFMA operand)
   MOE_TRY(hip_status(moe::launch_dense(x, T, d.d_model, w_down, L, moe::DenseOut::kBF16, nullptr,
                                        lat, nullptr, tiles, ntiles, s)));

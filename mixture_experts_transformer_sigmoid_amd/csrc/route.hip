@@ -6,15 +6,16 @@
 // router weight is split exactly into three bf16 numbers, w = hi + mid + lo (hi is w
 // rounded to bf16, mid the rounded remainder, lo the rest, which fits in bf16's 8
 // significant bits), so x W_r^T = x hi^T + x mid^T + x lo^T.  x is bf16, so every
-// product is exact in fp32; the three partial logits are accumulated in fp32 by the
-// grouped-GEMM kernels (one group, 3E outputs) and added in fp64 by the selection kernel.
-// For a few tokens (decode) one kernel does the split in registers and cuts K into
-// slices instead (router_small_kernel below).
+// product is exact in fp32.  Above kRouterSmallT tokens the three partial logits are
+// accumulated in fp32 by the grouped-GEMM kernels (one group, 3E outputs) and added in
+// fp64 by the selection kernel.  For fewer tokens (decode) router_scores_kernel does the
+// split in registers, owns whole logits, and applies the sigmoid and the bias itself.
 // (The split follows the bf16x3 scheme of Henry, Tang and Heinecke, "Leveraging the
 // bfloat16 artificial intelligence datatype for higher-precision computations", 2019.)
 #include <math.h>
 
 #include "common.h"
+#include "select.h"
 
 namespace moe {
 namespace {
@@ -38,21 +39,32 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
   }
 }
 
-// ---------------------------------------------------------------- logits, few tokens
-// For a decode-sized batch the logits GEMM is small (T x E outputs) and its cost is
-// reading W_r.  This kernel reads the fp32 router weights once, splits each value into
-// its hi, mid and lo bf16 parts in registers (no split pass, no bf16 copy of W_r) and
-// accumulates the three partial logits in three fp32 accumulators.  K is cut into
-// kRouterKSplit slices (grid z) so that the launch fills the chip; every (slice, part)
-// pair writes its own partial, and the selection kernel adds the 3 * kRouterKSplit
-// partials of a logit in fp64, in a fixed order (slice by slice, hi, mid, lo).
-// Block: 4 waves; wave w owns experts n0 + 16 w .. + 15 (one MFMA fragment), the block
-// 16 rows (tokens).  Lane (r, q): expert n0 + 16 w + r, token t0 + r, k 8q .. 8q + 7 of
-// each 32-wide step; weights are the MFMA's A operand, tokens its B operand.
+// ---------------------------------------------------------------- scores, few tokens
+// Up to kRouterSmallT tokens the router is a small GEMM (T x E outputs) whose cost is
+// reading the fp32 W_r.  One workgroup owns a 16-token x 16-expert tile of z over the whole
+// K, so every logit is complete inside it and the sigmoid and the bias follow in its
+// epilogue (no partial logits leave the chip).  Its 16 waves take a sixteenth of K each,
+// so that a workgroup keeps many loads in flight; each fp32 router weight is split into
+// its hi, mid and lo bf16 parts in registers (no split pass, no bf16 copy of W_r), and the
+// three partial products accumulate in three fp32 accumulators.  The 48 per-wave partials
+// of a logit are then added in fp64 in a fixed order (wave by wave, hi, mid, lo) and
+// rounded to fp32.
+// Lane (r, q) of a wave: expert e0 + r and token t0 + r, k 8q .. 8q + 7 of each 32-wide
+// step; the weights are the MFMA's A operand, the tokens its B operand, so the lane's
+// accumulator holds experts e0 + 4q .. + 3 of token t0 + r.
+// With a norm (the block entry point), x is the residual stream x': wave i first takes
+// the sum of squares of row t0 + i (all of the row's loads in flight at once, fp64, a fixed
+// order), and every operand element is then bf16(fp32(x' * (1 / sqrt(mean + eps)) * gain)),
+// the value the norm kernel stores; the workgroups of expert tile 0 store those rows as
+// x_ffn for the experts.
+constexpr int kRouterWaves = 16;
 #ifndef MOE_ROUTER_KU
 #define MOE_ROUTER_KU 4
 #endif
 constexpr int kRouterKU = MOE_ROUTER_KU;   // k-steps of loads issued before their MFMAs
+// row pieces (8 elements) per lane that the norm prologue requests at once: rows of up to
+// 64 x 16 x 8 = 8192 elements in one batch
+constexpr int kRouterNormPieces = 16;
 
 // The split of two weights at once, each part a packed bf16 pair (first weight in bits
 // 0..15), on the hardware round-to-nearest-even conversion (two values per instruction;
@@ -65,25 +77,78 @@ __device__ __forceinline__ void split3x2(float a, float b, uint32_t& H, uint32_t
   L = pack_bf16x2(ra - __uint_as_float(M << 16), rb - __uint_as_float(M & 0xffff0000u));
 }
 
-__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
-                                                           const float* __restrict__ w_r,
-                                                           int64_t T, int d, int E,
-                                                           float* __restrict__ z_part) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+__device__ __forceinline__ double sumsq8(const u32x4_t& w, double acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double a = bf16_to_f32(w[i] & 0xffffu), b = bf16_to_f32(w[i] >> 16);
+    acc = fma(a, a, acc);
+    acc = fma(b, b, acc);
+  }
+  return acc;
+}
+
+// Eight elements of x' normalised with the row's 1/rms and the gain: fp64 products rounded
+// to fp32, then to bf16 (nearest-even both times).
+__device__ __forceinline__ u32x4_t norm8(const u32x4_t& v, double rinv, const u32x4_t (&g)[2]) {
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float ga = __uint_as_float(g[i >> 1][2 * (i & 1)]);
+    const float gb = __uint_as_float(g[i >> 1][2 * (i & 1) + 1]);
+    const float a = (float)((double)bf16_to_f32(v[i] & 0xffffu) * rinv * (double)ga);
+    const float b = (float)((double)bf16_to_f32(v[i] >> 16) * rinv * (double)gb);
+    o[i] = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+  }
+  return o;
+}
+
+template <bool NORM>
+__global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
+    uint16_t* __restrict__ x_ffn, const float* __restrict__ w_r, const float* __restrict__ bias,
+    int64_t T, int d, int E, float* __restrict__ score, float* __restrict__ sig,
+    float* __restrict__ logits) {
+  __shared__ f32x4_t part[kRouterWaves][3][64];
+  __shared__ double rinv_s[16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * 16;
-  const int n0 = blockIdx.y * 64 + wave * 16;
-  const int kz = blockIdx.z, nks = d / 32;
-  const int ks0 = (int)((int64_t)nks * kz / kRouterKSplit);
-  const int ks1 = (int)((int64_t)nks * (kz + 1) / kRouterKSplit);
-  int64_t t = t0 + r;
-  if (t > T - 1) t = T - 1;
-  int e = n0 + r;
-  if (e > E - 1) e = E - 1;
+  const int e0 = blockIdx.y * 16;
+  if constexpr (NORM) {
+    // wave i: row t0 + i; lane l sums pieces l, l + 64, ... (8 elements each), then the 64
+    // partial sums meet in a fixed butterfly order
+    const uint16_t* row = x + min<int64_t>(t0 + wave, T - 1) * d;
+    const int npc = d / 8;
+    double ss = 0.0;
+    for (int c0 = 0; c0 < npc; c0 += 64 * kRouterNormPieces) {
+      u32x4_t v[kRouterNormPieces];
+#pragma unroll
+      for (int u = 0; u < kRouterNormPieces; ++u)
+        v[u] = load16(row + 8 * min(c0 + lane + 64 * u, npc - 1));
+#pragma unroll
+      for (int u = 0; u < kRouterNormPieces; ++u)
+        if (c0 + lane + 64 * u < npc) ss = sumsq8(v[u], ss);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) rinv_s[wave] = 1.0 / sqrt(ss / (double)d + (double)eps);
+    __syncthreads();
+  }
+  const int64_t t = min<int64_t>(t0 + r, T - 1);
+  const int e = min(e0 + r, E - 1);
   const float* wrow = w_r + (int64_t)e * d + q * 8;
   const uint16_t* xrow = x + t * d + q * 8;
+  const float* grow = NORM ? gain + q * 8 : nullptr;
+  const double rinv = NORM ? rinv_s[r] : 1.0;
+  uint16_t* xo = (NORM && blockIdx.y == 0 && t0 + r < T) ? x_ffn + t * d + q * 8 : nullptr;
+  const int nst = d / 32;
+  const int s0 = nst * wave / kRouterWaves, s1 = nst * (wave + 1) / kRouterWaves;
   f32x4_t acc[3] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f},
                     f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  auto step = [&](const u32x4_t (&wv)[2], u32x4_t xv) {
+  auto step = [&](const u32x4_t (&wv)[2], u32x4_t xv, const u32x4_t (&gv)[2], int k) {
+    if constexpr (NORM) {
+      xv = norm8(xv, rinv, gv);
+      if (xo != nullptr) *reinterpret_cast<u32x4_t*>(xo + k) = xv;
+    }
     uint32_t h[4], m[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -97,44 +162,71 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
     acc[1] = mfma16x16x32(Mv, xv, acc[1]);
     acc[2] = mfma16x16x32(Lv, xv, acc[2]);
   };
-  int ks = ks0;
-  for (; ks + kRouterKU <= ks1; ks += kRouterKU) {
-    u32x4_t wv[kRouterKU][2], xv[kRouterKU];
-#pragma unroll
-    for (int u = 0; u < kRouterKU; ++u) {
-      const float* wp = wrow + (ks + u) * 32;
-      wv[u][0] = *reinterpret_cast<const u32x4_t*>(wp);
-      wv[u][1] = *reinterpret_cast<const u32x4_t*>(wp + 4);
-      xv[u] = load16(xrow + (ks + u) * 32);
+  auto load_step = [&](int st, u32x4_t (&wv)[2], u32x4_t& xv, u32x4_t (&gv)[2]) {
+    const float* wp = wrow + st * 32;
+    wv[0] = *reinterpret_cast<const u32x4_t*>(wp);
+    wv[1] = *reinterpret_cast<const u32x4_t*>(wp + 4);
+    xv = load16(xrow + st * 32);
+    if constexpr (NORM) {
+      gv[0] = *reinterpret_cast<const u32x4_t*>(grow + st * 32);
+      gv[1] = *reinterpret_cast<const u32x4_t*>(grow + st * 32 + 4);
     }
+  };
+  int st = s0;
+  for (; st + kRouterKU <= s1; st += kRouterKU) {
+    u32x4_t wv[kRouterKU][2], xv[kRouterKU], gv[kRouterKU][2];
+#pragma unroll
+    for (int u = 0; u < kRouterKU; ++u) load_step(st + u, wv[u], xv[u], gv[u]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kRouterKU; ++u) step(wv[u], xv[u]);
+    for (int u = 0; u < kRouterKU; ++u) step(wv[u], xv[u], gv[u], (st + u) * 32);
   }
-  for (; ks < ks1; ++ks) {
-    const float* wp = wrow + ks * 32;
-    const u32x4_t wv[2] = {*reinterpret_cast<const u32x4_t*>(wp),
-                           *reinterpret_cast<const u32x4_t*>(wp + 4)};
-    step(wv, load16(xrow + ks * 32));
+  for (; st < s1; ++st) {
+    u32x4_t wv[2], xv, gv[2];
+    load_step(st, wv, xv, gv);
+    step(wv, xv, gv, st * 32);
   }
-  // lane holds experts n0 + 4q .. + 3 of token t0 + r; partial (slice kz, part p) of a
-  // token's logits sits at z_part[t][(3 kz + p) E + e]
-  if (t0 + r >= T) return;
-  float* zrow = z_part + (t0 + r) * (int64_t)(3 * kRouterKSplit) * E;
+  // the 48 partials of each logit meet in LDS and are added in fp64, wave by wave, hi,
+  // mid, lo
 #pragma unroll
-  for (int p = 0; p < 3; ++p)
+  for (int p = 0; p < 3; ++p) part[wave][p][lane] = acc[p];
+  __syncthreads();
+  if (tid >= 256) return;
+  const int i = tid >> 4, jj = tid & 15;   // token t0 + i, expert e0 + jj
+  const int src = (jj >> 2) * 16 + i, reg = jj & 3;
+  double zd = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ee = n0 + 4 * q + i;
-      if (ee < E) zrow[(3 * kz + p) * (int64_t)E + ee] = acc[p][i];
-    }
+  for (int w = 0; w < kRouterWaves; ++w)
+#pragma unroll
+    for (int p = 0; p < 3; ++p) zd += (double)part[w][p][src][reg];
+  const int64_t tt = t0 + i;
+  const int ee = e0 + jj;
+  if (tt >= T || ee >= E) return;
+  const float z = (float)zd;
+  if (logits != nullptr) logits[tt * E + ee] = z;
+  const float s = 1.0f / (1.0f + expf(-z));
+  float v = s + bias[ee];
+  if (v != v) v = -INFINITY;
+  score[tt * E + ee] = v;
+  sig[tt * E + ee] = s;
 }
 
 // ---------------------------------------------------------------- top-k + gates
-// One wave per token.  z = hi + mid + lo partial logits summed in fp64, rounded to fp32.
-// Lane l holds experts l, l + 64, ...; k rounds of a wave-wide argmax over (score,
-// -index) pick the experts (ties to the lower index, NaN scores treated as -inf); the
-// gates use the sigmoid without the bias.
+// Up to kRouterSmallT tokens: one wave per token over the scores the kernel above wrote.
+template <int EPL>
+__global__ __launch_bounds__(256) void router_select_scores_kernel(
+    const float* __restrict__ score, const float* __restrict__ sig, int64_t T, int E, int k,
+    float alpha, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float sc[EPL], sg[EPL];
+  load_scores<EPL>(score + t * E, sig + t * E, E, lane, sc, sg);
+  select_topk<EPL>(sc, sg, E, k, alpha, lane, topk_idx + t * k, topk_w + t * k, nullptr);
+}
+
+// Above kRouterSmallT tokens: z = the np partial logits (hi, mid, lo of each K slice)
+// summed in fp64, rounded to fp32; then as above.
 template <int EPL, int PB>
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ z_part,
                                                             int np, int row_parts, int pstride,
@@ -189,63 +281,11 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
       sig[i] = 0.0f;
     }
   }
-  uint32_t taken = 0;
-  int sel_idx[kMaxTopK];
-  float sel_s[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    sel_idx[j] = 0;
-    sel_s[j] = 0.0f;
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j < k) {
-      float bv = -INFINITY, bs = 0.0f;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u)) {
-          if (score[i] > bv || (score[i] == bv && e < bi)) {
-            bv = score[i];
-            bi = e;
-            bs = sig[i];
-          }
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        const float os = __shfl_xor(bs, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-          bs = os;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + 64 * i == bi) taken |= 1u << i;
-      sel_idx[j] = bi;
-      sel_s[j] = bs;
-    }
-  }
-  float den = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j)
-    if (j < k) den += sel_s[j];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j < k && lane == j) {
-      topk_idx[t * k + j] = sel_idx[j];
-      topk_w[t * k + j] = den > 0.0f ? alpha * sel_s[j] / den : 0.0f;
-    }
-  }
+  select_topk<EPL>(score, sig, E, k, alpha, lane, topk_idx + t * k, topk_w + t * k, nullptr);
 }
 
-// Parts per batch of loads: every part in one batch (np is at most 24: 3 per K slice, at
-// most 8 slices) while the loaded values fit in 144 registers, else batches of 8.
+// Parts per batch of loads: up to 12 parts in one batch while the loaded values fit in
+// registers, else batches of 8.
 template <int EPL>
 void select_launch(const float* z_part, int np, int row_parts, int pstride, const float* bias,
                    int64_t T, int E, int k, float alpha, float* logits, int32_t* idx, float* w,
@@ -254,9 +294,6 @@ void select_launch(const float* z_part, int np, int row_parts, int pstride, cons
   if (EPL <= 6 && np <= 12)
     hipLaunchKernelGGL((router_select_kernel<EPL, 12>), dim3(grid), dim3(256), 0, s, z_part, np,
                        row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
-  else if (EPL <= 6)
-    hipLaunchKernelGGL((router_select_kernel<EPL, 24>), dim3(grid), dim3(256), 0, s, z_part, np,
-                       row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
   else
     hipLaunchKernelGGL((router_select_kernel<EPL, 8>), dim3(grid), dim3(256), 0, s, z_part, np,
                        row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
@@ -264,54 +301,75 @@ void select_launch(const float* z_part, int np, int row_parts, int pstride, cons
 
 }  // namespace
 
+hipError_t launch_router_scores(const uint16_t* x, const RouterNorm* norm, const float* w_r,
+                                const float* bias, int64_t T, int d, int E, float* score,
+                                float* sig, float* logits, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16));
+  if (norm != nullptr)
+    hipLaunchKernelGGL(router_scores_kernel<true>, grid, dim3(64 * kRouterWaves), 0, s, x, norm->gain,
+                       norm->eps, norm->x_ffn, w_r, bias, T, d, E, score, sig, logits);
+  else
+    hipLaunchKernelGGL(router_scores_kernel<false>, grid, dim3(64 * kRouterWaves), 0, s, x, nullptr, 0.0f,
+                       nullptr, w_r, bias, T, d, E, score, sig, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_select(const float* score, const float* sig, int64_t T, int E, int k,
+                                float alpha, int32_t* idx, float* w, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((T + 3) / 4));
+#define MOE_SELECT_SCORES(N)                                                                  \
+  hipLaunchKernelGGL(router_select_scores_kernel<N>, grid, dim3(256), 0, s, score, sig, T, E, \
+                     k, alpha, idx, w)
+  switch (select_epl(E)) {
+    case 1: MOE_SELECT_SCORES(1); break;
+    case 2: MOE_SELECT_SCORES(2); break;
+    case 4: MOE_SELECT_SCORES(4); break;
+    case 6: MOE_SELECT_SCORES(6); break;
+    case 8: MOE_SELECT_SCORES(8); break;
+    default: MOE_SELECT_SCORES(16); break;
+  }
+#undef MOE_SELECT_SCORES
+  return hipGetLastError();
+}
+
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
                          int E, int k, float alpha, uint16_t* w_split, float* z_part,
                          Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,
                          float* topk_w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   hipError_t err;
-  int np, row_parts, pstride;
   if (T <= kRouterSmallT) {
-    const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 63) / 64), kRouterKSplit);
-    hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, x, w_r, T, d, E, z_part);
-    err = hipGetLastError();
+    // scores [T, E] and sigmoids [T, E] in z_part
+    float* score = z_part;
+    float* sig = z_part + T * E;
+    err = launch_router_scores(x, nullptr, w_r, bias, T, d, E, score, sig, logits, s);
     if (err != hipSuccess) return err;
-    // the selection adds the 3 * kRouterKSplit partials of each logit in fp64, slice by
-    // slice
-    np = 3 * kRouterKSplit;
-    row_parts = 3 * kRouterKSplit;
-    pstride = E;
-  } else {
-    const int Ep = router_part_rows(E);
-    const int64_t n = (int64_t)E * d, np_ = (int64_t)Ep * d;
-    const int64_t blocks = (np_ + 255) / 256 < 4096 ? (np_ + 255) / 256 : 4096;
-    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w_r, n, np_,
-                       w_split);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    // K cut into S slices (router_ksplit): every token's row holds S x (hi, mid, lo)
-    // partial logits, Ep apart, which the selection adds in fp64 in that order
-    const int S = router_ksplit(T, E, d);
-    err = launch_dense(x, T, d, w_split, 3 * Ep, DenseOut::kF32, z_part, nullptr, nullptr, tiles,
-                       ntiles, s, S);
-    if (err != hipSuccess) return err;
-    np = 3 * S;
-    row_parts = 3 * S;
-    pstride = Ep;
+    return launch_router_select(score, sig, T, E, k, alpha, topk_idx, topk_w, s);
   }
-  const int epl = (E + 63) / 64;
-  if (epl <= 1)
-    select_launch<1>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
-  else if (epl <= 2)
-    select_launch<2>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
-  else if (epl <= 4)
-    select_launch<4>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
-  else if (epl <= 6)
-    select_launch<6>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
-  else if (epl <= 8)
-    select_launch<8>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
-  else
-    select_launch<16>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s);
+  const int Ep = router_part_rows(E);
+  const int64_t n = (int64_t)E * d, np_ = (int64_t)Ep * d;
+  const int64_t blocks = (np_ + 255) / 256 < 4096 ? (np_ + 255) / 256 : 4096;
+  hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w_r, n, np_,
+                     w_split);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // K cut into S slices (router_ksplit): every token's row holds S x (hi, mid, lo)
+  // partial logits, Ep apart, which the selection adds in fp64 in that order
+  const int S = router_ksplit(T, E, d);
+  err = launch_dense(x, T, d, w_split, 3 * Ep, DenseOut::kF32, z_part, nullptr, nullptr, tiles,
+                     ntiles, s, S);
+  if (err != hipSuccess) return err;
+  const int np = 3 * S, row_parts = 3 * S, pstride = Ep;
+  switch (select_epl(E)) {
+    case 1: select_launch<1>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s); break;
+    case 2: select_launch<2>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s); break;
+    case 4: select_launch<4>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s); break;
+    case 6: select_launch<6>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s); break;
+    case 8: select_launch<8>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s); break;
+    default: select_launch<16>(z_part, np, row_parts, pstride, bias, T, E, k, alpha, logits, topk_idx, topk_w, s); break;
+  }
   return hipGetLastError();
 }
 
