@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "K2 MoE-layer tokens/s (128 & 8192 tok, bf16); % of HBM / MFMA peak"
 # the gate/up kernel each workload runs (decode: a few rows per expert; prefill: many)
-GATEUP_KERNEL = {"k2_decode": "ffn_skinny_kernel<1, 16, 0>", "k2_prefill": "ffn_lds_kernel<0>"}
+GATEUP_KERNEL = {"k2_decode": "ffn_skinny_kernel<1, 16, 0, false>", "k2_prefill": "ffn_lds_kernel<0>"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
@@ -165,7 +165,8 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight figures")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the fused norm + residual block figure")
-    ap.add_argument("--cpu-sample", type=int, default=32, help="tokens in the oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=128,
+                    help="tokens in the oracle sample (default: all 128 of the decode batch)")
     ap.add_argument("--no-power", action="store_true",
                     help="skip sampling socket power / clock during the prefill loop")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -496,7 +497,9 @@ def sample_power(M, torch, dims, inp, out, ws, seconds=6.0):
 
 def cpu_baseline(torch, S, cfg, inp, n_tok):
     """The oracle as it stands on a bounded sample: route + sparse FFN for n_tok tokens of
-    the batch, weights pre-staged on the host (bf16), timed on the host cores."""
+    the batch (all of them by default), timed on the host cores.  The weights are staged on
+    the host as bf16 beforehand; their conversion to float64, which the oracle's expert
+    getter does one expert at a time, is timed separately and left out of the figure."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -509,19 +512,76 @@ def cpu_baseline(torch, S, cfg, inp, n_tok):
     r = O.route(x, w_r, b, cfg["top_k"], cfg["routed_scale"])
     need = sorted(set(int(e) for e in r["topk_idx"].reshape(-1)))
     host = {e: (inp["w1"][e].cpu(), inp["w3"][e].cpu(), inp["w2"][e].cpu()) for e in need}
-    shared_h = (inp["ws1"].cpu(), inp["ws3"].cpu(), inp["ws2"].cpu())
+    shared = tuple(t.cpu().to(torch.float64).numpy() for t in (inp["ws1"], inp["ws3"], inp["ws2"]))
+    conv = [0.0]
 
     def get(e):
-        return tuple(t.to(torch.float64).numpy() for t in host[e])
+        c = time.perf_counter()
+        out = tuple(t.to(torch.float64).numpy() for t in host[e])
+        conv[0] += time.perf_counter() - c
+        return out
     t = time.perf_counter()
     r = O.route(x, w_r, b, cfg["top_k"], cfg["routed_scale"])
-    O.moe_sparse(x, w_r, b, cfg["top_k"], cfg["routed_scale"], get_expert=get,
-                 shared=tuple(s.to(torch.float64).numpy() for s in shared_h), routing=r)
-    el = time.perf_counter() - t
+    O.moe_sparse(x, w_r, b, cfg["top_k"], cfg["routed_scale"], get_expert=get, shared=shared,
+                 routing=r)
+    el = time.perf_counter() - t - conv[0]
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [torch.get_num_threads()])
     return {"value": len(toks) / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(toks)} of the {T} tokens (route + {len(need)} experts + shared, "
-                      f"float64 numpy, {el:.1f} s)"}
+                      f"float64 numpy, {el:.1f} s; the bf16 -> float64 weight conversion, "
+                      f"{conv[0]:.1f} s, left out)"}
+
+
+def near_ties(M, torch, dims, x, w_r, b, ws):
+    """Tokens whose k-th and (k+1)-th biased scores are within 1e-6: the ones a parity check
+    leaves out of the bit-exact routing comparison.  Scores from the layer's own logits
+    (moe_route), fl32(sigmoid(z)) + b in fp32."""
+    T, E, k = int(dims.tokens), int(dims.n_experts), int(dims.top_k)
+    dev = x.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    z = torch.empty((T, E), dtype=torch.float32, device=dev)
+    M.moe_route(dims, x, w_r, b, idx, w, z, ws)
+    sc = torch.sigmoid(z) + b.float()
+    top = torch.topk(sc, min(k + 1, E), dim=1).values
+    if k >= E:
+        return 0
+    return int(((top[:, k - 1] - top[:, k]) < 1e-6).sum())
+
+
+def time_tiny(M, torch, S, dev, calls=200):
+    """The tiny config (64 tokens, d 256, 16 experts, top-2): a latency-bound call.  Reports
+    the mean per call over back-to-back calls (HIP events) and the median wall time of one
+    call followed by a synchronisation."""
+    cfg = S.CONFIGS["tiny"]
+    inp = {k: v.to(dev) for k, v in S.make_inputs(cfg, "cpu").items()}
+    dims = M.dims_for(cfg)
+    ws = M.workspace(dims, dev)
+    out = torch.empty(cfg["tokens"], cfg["d_model"], dtype=torch.bfloat16, device=dev)
+
+    def call():
+        M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
+                      inp["ws1"], inp["ws3"], inp["ws2"], out, ws)
+    for _ in range(10):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    walls = []
+    for _ in range(50):
+        t = time.perf_counter()
+        call()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t)
+    walls.sort()
+    per = e0.elapsed_time(e1) / calls
+    return {"workload": "tiny: T=64, d=256, 16 experts top-2 (x2.827), I=Is=128, bf16 kernels",
+            "us_per_call_pipelined": per * 1e3, "us_per_call_synchronised": walls[len(walls) // 2] * 1e6,
+            "tokens_per_s": cfg["tokens"] / (per * 1e-3)}
 
 
 def main():
@@ -597,8 +657,10 @@ def main():
                   "mfma_tflops": layer_tfs, "mfma_frac": layer_tfs / MFMA_BF16_PEAK_TFLOPS,
                   "algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"]},
     }
+    res["config"]["near_tie_tokens"] = near_ties(M, torch, dims, inp["x"], inp["w_r"], inp["b"], ws)
     log(f"{args.workload}: {ms:.3f} ms/step, {res['value']:.0f} tok/s, layer {layer_gbs:.0f} GB/s, "
-        f"gate/up {gu_ms:.3f} ms = {gu_gbs:.0f} GB/s")
+        f"gate/up {gu_ms:.3f} ms = {gu_gbs:.0f} GB/s, "
+        f"{res['config']['near_tie_tokens']} near-tie tokens")
     if not args.no_block:
         del ws
         bms = time_block(M, torch, S, cfg, weights, args.steps, args.warmup)
@@ -626,16 +688,18 @@ def main():
         ptf = palg["layer_flops"] / (pms * 1e-3) / 1e12
         pgb = palg["layer_bytes"] / (pms * 1e-3) / 1e9
         power = None if args.no_power else sample_power(M, torch, pdims, pin, pout, pws)
-        if not args.no_block:
-            del pws
-            pbms = time_block(M, torch, S, pcfg, weights, psteps, 1)
-            pws = None
+        pties = near_ties(M, torch, pdims, pin["x"], pin["w_r"], pin["b"], pws)
         res["prefill"] = {"workload": "k2_prefill: T=8192 (4 x 2048), same layer", "steps": psteps,
+                          "near_tie_tokens": pties,
                           "ms_per_step": pms, "tokens_per_s": pcfg["tokens"] / (pms * 1e-3),
                           "step_ms": {"median": sorted(psteps_ms)[len(psteps_ms) // 2],
                                       "min": min(psteps_ms), "max": max(psteps_ms)},
                           "mfma_tflops": ptf, "mfma_frac": ptf / MFMA_BF16_PEAK_TFLOPS,
                           "hbm_gbs": pgb, "hbm_frac": pgb / HBM_PEAK_GBS, "active_experts": pact}
+        if not args.no_block:
+            del pws
+            pbms = time_block(M, torch, S, pcfg, weights, psteps, 1)
+            pws = None
         # MFMA counters of the prefill GEMMs (committed rocprofv3 --pmc summary, taken on
         # the current kernel sources): busy fraction of the active cycles, implied clock
         ctr = {role: mfma_for("ffn_lds_kernel<%d>" % epi, grid) for role, epi, grid in
@@ -675,6 +739,7 @@ def main():
                        "steps": ssteps, "ms_per_step": sms, "tokens_per_s": scfg["tokens"] / (sms * 1e-3),
                        "mfma_tflops": stf, "mfma_frac": stf / MFMA_BF16_PEAK_TFLOPS,
                        "active_experts": sact, "max_rows_per_expert": int(cnt.max()),
+                       "near_tie_tokens": near_ties(M, torch, sdims, sin["x"], sin["w_r"], sin["b"], sws),
                        "hbm_gbs": salg["layer_bytes"] / (sms * 1e-3) / 1e9}
         log(f"skew: {sms:.3f} ms/step, {res['skew']['tokens_per_s']:.0f} tok/s, {stf:.0f} TFLOP/s, "
             f"{sact} active experts, up to {int(cnt.max())} rows")
@@ -690,6 +755,10 @@ def main():
             f" = {fres['gate_up']['achieved_gbs']:.0f} GB/s"
             + (f"; prefill {fres['prefill_ms_per_step']:.3f} ms" if "prefill_ms_per_step" in fres else ""))
         torch.cuda.empty_cache()
+    tiny = time_tiny(M, torch, S, dev)
+    res["tiny"] = tiny
+    log(f"tiny: {tiny['us_per_call_pipelined']:.1f} us per call back to back, "
+        f"{tiny['us_per_call_synchronised']:.1f} us with a synchronisation")
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_sample} tokens")
         res["cpu_baseline"] = cpu_baseline(torch, S, cfg, inp, args.cpu_sample)
