@@ -29,9 +29,10 @@ Readings where the pages are silent:
 * Weights are stored [out, in] (the K3 page states this for its projection); so
   ``w_r`` is [E, d], ``w1``/``w3`` are [E, I, d], ``w2`` is [E, d, I].
 * Top-k tie-break: the lower expert index wins.
-* The selection is a floating-point decision, so it is taken in the precision the
-  kernel takes it in (fp32): z rounded to fp32, s = sigma(z) rounded to fp32, the
-  score s + b rounded to fp32.  All values (gates, FFN, sums) are float64.
+* The selection compares the stored fp32 activations: z rounded to fp32, s = sigma(z)
+  rounded to fp32, then the biased score s + b taken exactly (float64) and compared.
+  Tokens whose k-th and (k+1)-th scores lie within 1e-6 are near ties that any fp32
+  implementation may order either way.  All values (gates, FFN, sums) are float64.
 * The bias enters only the selection, added to sigma(z), never to z and never to G.
 * No epsilon in the renormalising denominator (the denominator is > 0).
 * RMSNorm: u / sqrt(mean(u^2) + eps) times the gain (the pre-MoE norm; the latent
@@ -177,10 +178,11 @@ def route(x, w_r, b, top_k, alpha=ALPHA_K2):
     Returns a dict:
       z        [T, E] float64 logits
       s        [T, E] float64 sigmoid scores
-      score32  [T, E] float32 decision scores fl32(fl32(sigma(fl32(z))) + b)
+      score    [T, E] float64 decision scores fl32(sigma(fl32(z))) + b, exact
+      score32  [T, E] float32 the same rounded to fp32 (the slot order a fp32 kernel sees)
       topk_idx [T, k] int32   selected experts, descending score, ties to lower index
       topk_w   [T, k] float64 gates G (same order)
-      gap      [T]    float64 score32 of the k-th pick minus that of the (k+1)-th
+      gap      [T]    float64 score of the k-th pick minus that of the (k+1)-th
                       (+inf when k == E): tokens with a tiny gap can flip under rounding
     """
     x = _f64(x)
@@ -192,25 +194,27 @@ def route(x, w_r, b, top_k, alpha=ALPHA_K2):
         raise ValueError("top_k must be in [1, E]")
     z = x @ w_r.T                                  # library matmul as the GEMM step
     s = sigmoid(z)
-    # decision precision: fp32, as the kernel takes it
+    # the stored activations are fp32: z and s = sigma(z) rounded to fp32; the biased
+    # score is then compared exactly
     z32 = z.astype(np.float32)
     s32 = sigmoid(z32.astype(np.float64)).astype(np.float32)
-    score32 = (s32.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
+    score = s32.astype(np.float64) + b.astype(np.float64)
     # order experts by (score descending, index ascending)
     idx = np.broadcast_to(np.arange(E), (T, E))
-    order = np.lexsort((idx, -score32.astype(np.float64)), axis=-1)
+    order = np.lexsort((idx, -score), axis=-1)
     sel = order[:, :top_k].astype(np.int32)
     if top_k < E:
-        kth = np.take_along_axis(score32, order[:, top_k - 1:top_k], axis=1)[:, 0]
-        nxt = np.take_along_axis(score32, order[:, top_k:top_k + 1], axis=1)[:, 0]
-        gap = kth.astype(np.float64) - nxt.astype(np.float64)
+        kth = np.take_along_axis(score, order[:, top_k - 1:top_k], axis=1)[:, 0]
+        nxt = np.take_along_axis(score, order[:, top_k:top_k + 1], axis=1)[:, 0]
+        gap = kth - nxt
     else:
         gap = np.full(T, np.inf)
     s_sel = np.take_along_axis(s, sel, axis=1)
     den = s_sel.sum(axis=1, keepdims=True)
     assert np.all(den > 0.0), "renormalising denominator must be positive"
     gates = alpha * s_sel / den
-    return {"z": z, "s": s, "score32": score32, "topk_idx": sel, "topk_w": gates, "gap": gap}
+    return {"z": z, "s": s, "score": score, "score32": score.astype(np.float32), "topk_idx": sel,
+            "topk_w": gates, "gap": gap}
 
 
 def gate_matrix(topk_idx, topk_w, n_experts):

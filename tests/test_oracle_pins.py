@@ -124,7 +124,7 @@ def test_topk_brute_force_e16_k2():
     rng = np.random.default_rng(4)
     L = _layer(rng, T=64, d=256, E=16, k=2, bias_scale=0.05)
     r = oracle.route(L["x"], L["w_r"], L["b"], 2)
-    sc = r["score32"].astype(np.float64)
+    sc = r["score"]
     for t in range(64):
         best = max(itertools.combinations(range(16), 2), key=lambda p: (sc[t, p[0]] + sc[t, p[1]], [-p[0], -p[1]]))
         assert set(r["topk_idx"][t].tolist()) == set(best)
@@ -137,7 +137,7 @@ def test_topk_brute_force_e10_k3():
     rng = np.random.default_rng(5)
     L = _layer(rng, T=40, d=16, E=10, k=3, bias_scale=0.1)
     r = oracle.route(L["x"], L["w_r"], L["b"], 3)
-    sc = r["score32"].astype(np.float64)
+    sc = r["score"]
     for t in range(40):
         best = max(itertools.combinations(range(10), 3), key=lambda p: sum(sc[t, list(p)]))
         assert set(r["topk_idx"][t].tolist()) == set(best)

@@ -190,7 +190,7 @@ def test_fp8_zero_and_extreme_scales():
 
 
 def test_fp8_zero_and_extreme_scales_wide():
-    # the same scale edits on the 256-row kernel (600 tokens, top-8 of 16: ~300 rows per
+    # the same scale edits on the 128-row stream kernel (600 tokens, top-8 of 16: ~300 rows per
     # expert): its per-128-k-block partial sums must keep the zero block and the extreme
     # scales exact too
     cfg = S.with_overrides("tiny", tokens=600, n_experts=16, top_k=8)

@@ -114,7 +114,7 @@ def check_near_ties(idx, ref, dims):
     best score left out, and the k experts are distinct.  Returns the excluded tokens."""
     excl = np.nonzero(ref["gap"] < GAP)[0]
     E, k = dims.n_experts, dims.top_k
-    sc = ref["score32"].astype(np.float64)
+    sc = ref["score"]
     for t in excl:
         chosen = np.asarray(idx[t], dtype=np.int64)
         assert np.unique(chosen).size == k, (t, chosen)
