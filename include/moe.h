@@ -250,7 +250,8 @@ moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float*
  *   z, s, sel, G as in moe_route, computed on the full-width x;
  *   l = x W_down^T  [T, L] (bf16);
  *   u = sum_i G_i E_i(l)  (SwiGLU experts of input and output width L);
- *   u_hat = u / sqrt(mean(u^2) + 1e-6)  (unit gain; the norm precedes W_up);
+ *   u_hat = u / sqrt(mean(u^2) + 1e-6)  (unit gain; the norm precedes W_up; u_hat enters
+ *   the up-projection rounded to bf16, or as two bf16 parts when L <= 1024);
  *   out = bf16(u_hat W_up^T + y_shared(x))  (shared expert on the full width).
  *   w_down [L, d] bf16; w1, w3 [E, I, L]; w2 [E, L, I]; w_up [d, L] bf16; shared expert
  *   [Is, d] / [d, Is] on the full width; out [T, d] bf16.  d_latent: multiple of 64,

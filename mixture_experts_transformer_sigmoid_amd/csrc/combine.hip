@@ -99,10 +99,9 @@ __global__ __launch_bounds__(kGatherThreads) void combine_kernel(
 // normalised before the up-projection).  One workgroup per token; each thread keeps up
 // to CPT 4-wide fp32 chunks of the sum, the sum of squares is reduced in a fixed tree
 // order (deterministic), and the row is scaled by 1/sqrt(mean + eps).  u_hat is the
-// up-projection's MFMA operand, written in two bf16 parts, [bf16(u_hat) | bf16(rest)]:
-// a single bf16 rounding of it would join the roundings of the latent input and of h and
-// take the output to the edge of its error bar.
-template <int KMAX, int CPT>
+// up-projection's MFMA operand: rounded to bf16 once (rows of L), or with TWO in two bf16
+// parts, [bf16(u_hat) | bf16(rest)] (rows of 2L).
+template <int KMAX, int CPT, bool TWO>
 __global__ __launch_bounds__(kCombineThreads) void combine_rmsnorm_kernel(
     const float* __restrict__ y_routed, const int32_t* __restrict__ inv,
     const float* __restrict__ topk_w, uint16_t* __restrict__ out, int64_t T, int L, int k,
@@ -180,9 +179,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rmsnorm_kernel(
             (f32_to_bf16(u[1] - bf16_to_f32(hi[0] >> 16)) << 16);
     lo[1] = f32_to_bf16(u[2] - bf16_to_f32(hi[1] & 0xffffu)) |
             (f32_to_bf16(u[3] - bf16_to_f32(hi[1] >> 16)) << 16);
-    uint16_t* row = out + t * 2 * L;
-    *reinterpret_cast<u32x2_t*>(row + 4 * c) = hi;
-    *reinterpret_cast<u32x2_t*>(row + L + 4 * c) = lo;
+    if constexpr (TWO) {
+      uint16_t* row = out + t * 2 * L;
+      *reinterpret_cast<u32x2_t*>(row + 4 * c) = hi;
+      *reinterpret_cast<u32x2_t*>(row + L + 4 * c) = lo;
+    } else {
+      *reinterpret_cast<u32x2_t*>(out + t * L + 4 * c) = hi;
+    }
   }
 }
 
@@ -190,14 +193,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rmsnorm_kernel(
 
 hipError_t launch_combine_rmsnorm(const float* y_routed, const int32_t* inv, const float* topk_w,
                                   uint16_t* out, int64_t T, int L, int k, float eps,
-                                  hipStream_t s) {
+                                  bool two_part, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (L <= 4 * kCombineThreads * 4)
-    hipLaunchKernelGGL((combine_rmsnorm_kernel<kMaxTopK, 4>), dim3((unsigned)T),
-                       dim3(kCombineThreads), 0, s, y_routed, inv, topk_w, out, T, L, k, eps);
-  else
-    hipLaunchKernelGGL((combine_rmsnorm_kernel<kMaxTopK, 8>), dim3((unsigned)T),
-                       dim3(kCombineThreads), 0, s, y_routed, inv, topk_w, out, T, L, k, eps);
+#define MOE_CRN(CPT, TWO)                                                                   \
+  hipLaunchKernelGGL((combine_rmsnorm_kernel<kMaxTopK, CPT, TWO>), dim3((unsigned)T),        \
+                     dim3(kCombineThreads), 0, s, y_routed, inv, topk_w, out, T, L, k, eps)
+  if (L <= 4 * kCombineThreads * 4) {
+    if (two_part) MOE_CRN(4, true);
+    else MOE_CRN(4, false);
+  } else {
+    if (two_part) MOE_CRN(8, true);
+    else MOE_CRN(8, false);
+  }
+#undef MOE_CRN
   return hipGetLastError();
 }
 

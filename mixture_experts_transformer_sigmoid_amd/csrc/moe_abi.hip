@@ -242,7 +242,7 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
   P.h = take(slots * h_width(d) * 2);
   P.hs = take(has_shared(d) ? T * h_width(d) * 2 : 0);
   P.y = take(slots * (size_t)L * 4);
-  P.uhat = take(T * (size_t)L * 2 * 2);  // two bf16 parts
+  P.uhat = take(T * (size_t)L * 2 * (L <= moe::kLatentTwoPartMaxL ? 2 : 1));  // one or two parts
   P.ys = take(has_shared(d) ? T * (size_t)d.d_model * 4 : 0);
   P.total = off;
   return P;
@@ -681,7 +681,10 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
   MOE_TRY(hip_status(
       moe::launch_down(rsh, h, offsets, w2, nullptr, y, nullptr, tiles, ntiles, s, true)));
   // gate-weighted sum over the slots, RMSNorm (eps from the config), bf16
-  MOE_TRY(hip_status(moe::launch_combine_rmsnorm(y, inv, w, uhat, T, L, d.top_k, 1e-6f, s)));
+  const bool uhat2 = L <= moe::kLatentTwoPartMaxL;
+  MOE_TRY(hip_status(
+      moe::launch_combine_rmsnorm(y, inv, w, uhat, T, L, d.top_k, 1e-6f, uhat2, s)));
+  const int KU = uhat2 ? 2 * L : L, WK = uhat2 ? L : 0;
   if (has_shared(d)) {
     // shared expert on the full-width input: a T-row group with no routed experts
     const FfnShape ssh{T, d.d_model, 0, 0, d.d_shared, true, hsplit(d)};
@@ -691,14 +694,13 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
                                            hs, tiles, ntiles, s)));
     MOE_TRY(hip_status(moe::launch_down(ssh, hs, nullptr, nullptr, ws2, nullptr, ys, tiles, ntiles,
                                         s, true)));
-    // up-projection (u_hat in two bf16 parts) with the shared output added before the one
-    // bf16 rounding
-    return hip_status(moe::launch_dense(uhat, T, 2 * L, w_up, d.d_model,
-                                        moe::DenseOut::kAddBF16, nullptr, out, ys, tiles, ntiles,
-                                        s, 1, L));
+    // up-projection (u_hat in one or two bf16 parts) with the shared output added before the
+    // one bf16 rounding
+    return hip_status(moe::launch_dense(uhat, T, KU, w_up, d.d_model, moe::DenseOut::kAddBF16,
+                                        nullptr, out, ys, tiles, ntiles, s, 1, WK));
   }
-  return hip_status(moe::launch_dense(uhat, T, 2 * L, w_up, d.d_model, moe::DenseOut::kBF16,
-                                      nullptr, out, nullptr, tiles, ntiles, s, 1, L));
+  return hip_status(moe::launch_dense(uhat, T, KU, w_up, d.d_model, moe::DenseOut::kBF16,
+                                      nullptr, out, nullptr, tiles, ntiles, s, 1, WK));
 }
 
 }  // extern "C"

@@ -3,7 +3,10 @@
 The no-allocation entry point runs moe_forward's kernels on the library's fixed device
 scratch instead of a caller's workspace, so its output must equal moe_forward's bit for
 bit.  Each case makes two calls in a row, the second with fewer tokens: the scratch keeps
-the first call's contents, and nothing of them may leak into the second result.
+the first call's contents, and nothing of them may leak into the second result.  The entry
+point is also captured in a HIP graph and replayed (it allocates nothing and launches no
+memset): every replay must reproduce the eager result, with an eager call on other inputs
+through the same scratch between replays.
 """
 import numpy as np
 import pytest
@@ -81,3 +84,38 @@ def test_noalloc_rejects_beyond_scratch():
     with pytest.raises(M.MoeError) as ei:
         M.moe_forward_noalloc(dims, x, x, x, x, x, x, x, x, x, x)
     assert ei.value.status == M.MOE_ESCRATCH
+
+
+def _call(dims, inp, out):
+    M.moe_forward_noalloc(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
+                          inp["ws1"], inp["ws3"], inp["ws2"], out)
+
+
+@pytest.mark.parametrize("name,tokens", [("tiny", 64), ("wide", 600)])
+def test_noalloc_graph_replays_match_eager(name, tokens):
+    cfg = S.CONFIGS["tiny"] if name == "tiny" else dict(
+        tokens=tokens, d_model=1024, n_experts=16, top_k=4, d_expert=512, d_shared=512,
+        routed_scale=2.827, bias="uniform")
+    inp = {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu", seed=61).items()}
+    other = {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu", seed=62).items()}
+    dims = M.dims_for(cfg)
+    want = torch.empty(cfg["tokens"], cfg["d_model"], dtype=torch.bfloat16, device=DEV)
+    M.moe_forward(dims, inp["x"], inp["w_r"], inp["b"], inp["w1"], inp["w3"], inp["w2"],
+                  inp["ws1"], inp["ws3"], inp["ws2"], want, M.workspace(dims))
+    out = torch.empty_like(want)
+    scratch_user = torch.empty_like(want)
+    _call(dims, inp, out)                  # first call on the device: scratch address lookup
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _call(dims, inp, out)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(float("nan"))
+        _call(dims, other, scratch_user)   # eager work through the same scratch
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"replay {i}: equal {torch.equal(out.view(torch.int16), want.view(torch.int16))}",
+              flush=True)
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {i}"
