@@ -16,6 +16,7 @@ import torch
 import mixture_experts_transformer_sigmoid_amd as M
 import synth_inputs as S
 from oracle import moe_oracle as O
+from test_parity_gpu import check_permute, check_routing
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +52,7 @@ def run_block(cfg, inp, eps=EPS):
     torch.cuda.synchronize()
     base = M.moe_workspace_bytes(dims)
     x_ffn = ws[base: base + T * d * 2].view(torch.bfloat16).view(T, d).clone()
+    run_block.ws = ws
     return out, x_ffn
 
 
@@ -65,6 +67,10 @@ def check_block(cfg, inp, eps=EPS, sample=None, seed=0):
     say(f"block case T={T} d={cfg['d_model']} E={cfg['n_experts']} k={cfg['top_k']} "
         f"I={cfg['d_expert']} Is={cfg['d_shared']} eps={eps}")
     out, x_ffn = run_block(cfg, inp, eps)
+    rw = M.routing_in_workspace(M.dims_for(cfg), run_block.ws)
+    g = {"idx": rw["topk_idx"].clone(), "w": rw["topk_w"].clone(), "counts": rw["counts"].clone(),
+         "offsets": rw["offsets"].clone(), "perm": rw["perm_rows"].clone(),
+         "inv": rw["inv_perm"].clone()}
     again, _ = run_block(cfg, inp, eps)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "not deterministic"
     x_res = f64(inp["x_res"])
@@ -76,6 +82,13 @@ def check_block(cfg, inp, eps=EPS, sample=None, seed=0):
         bad = np.argwhere(g_ffn[a:a + 1024] != want)
         assert bad.size == 0, f"x_ffn differs at {bad[:4] + [a, 0]}"
     say("  x_ffn bit-exact")
+    # the call's own routing (on its x_ffn) and permutation, left at the front of the workspace
+    dims = M.dims_for(cfg)
+    r_all = O.route(g_ffn, f64(inp["w_r"]), inp["b"].cpu().numpy(), cfg["top_k"],
+                    cfg["routed_scale"])
+    n_ex = check_routing(g, r_all, dims)
+    check_permute(g, dims)
+    say(f"  routing and permutation exact ({n_ex} near-tie tokens excluded)")
     toks = np.arange(T) if sample is None else np.sort(
         np.random.default_rng(seed).choice(T, size=min(sample, T), replace=False))
     get = lambda e: (f64(inp["w1"][e]), f64(inp["w3"][e]), f64(inp["w2"][e]))  # noqa: E731
@@ -101,8 +114,10 @@ def test_block_tiny():
     check_block(cfg, block_inputs(cfg))
 
 
-@pytest.mark.parametrize("T", [1, 37, 300])
+@pytest.mark.parametrize("T", [1, 37, 300, 600])
 def test_block_ragged(T):
+    # up to 512 tokens the router kernel normalises the residual stream itself; 600 takes
+    # the norm kernel and the GEMM router
     cfg = S.with_overrides("tiny", tokens=T, d_model=320, n_experts=24, top_k=3, d_expert=192,
                            d_shared=192)
     check_block(cfg, block_inputs(cfg, seed=T))
@@ -134,9 +149,9 @@ def test_block_w2_zero_returns_residual():
 
 def test_block_k2_decode_128(k2_weights):
     cfg = S.CONFIGS["k2_decode"]
-    check_block(cfg, block_inputs(cfg, weights=k2_weights), sample=16)
+    check_block(cfg, block_inputs(cfg, weights=k2_weights), sample=64)
 
 
 def test_block_k2_prefill_8192(k2_weights):
     cfg = S.CONFIGS["k2_prefill"]
-    check_block(cfg, block_inputs(cfg, weights=k2_weights), sample=8)
+    check_block(cfg, block_inputs(cfg, weights=k2_weights), sample=64)

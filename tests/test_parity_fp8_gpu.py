@@ -222,9 +222,9 @@ def k2_fp8_weights():
 
 def test_fp8_k2_decode_128(k2_fp8_weights):
     cfg = S.CONFIGS["k2_decode"]
-    full_check(cfg, fp8_inputs(cfg, weights=k2_fp8_weights), sample=16)
+    full_check(cfg, fp8_inputs(cfg, weights=k2_fp8_weights), sample=32)
 
 
 def test_fp8_k2_prefill_8192(k2_fp8_weights):
     cfg = S.CONFIGS["k2_prefill"]
-    full_check(cfg, fp8_inputs(cfg, weights=k2_fp8_weights), sample=8)
+    full_check(cfg, fp8_inputs(cfg, weights=k2_fp8_weights), sample=32)
