@@ -52,12 +52,22 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // Lane (r, q) of a wave: expert e0 + r and token t0 + r, k 8q .. 8q + 7 of each 32-wide
 // step; the weights are the MFMA's A operand, the tokens its B operand, so the lane's
 // accumulator holds experts e0 + 4q .. + 3 of token t0 + r.
-// With a norm (the block entry point), x is the residual stream x': wave i first takes
-// the sum of squares of row t0 + i (all of the row's loads in flight at once, fp64, a fixed
+// With a norm (the block entry point), x is the residual stream x': the waves first take
+// the sums of squares of the 16 rows (a row's loads in flight at once, fp64, a fixed
 // order), and every operand element is then bf16(fp32(x' * (1 / sqrt(mean + eps)) * gain)),
 // the value the norm kernel stores; the workgroups of expert tile 0 store those rows as
 // x_ffn for the experts.
-constexpr int kRouterWaves = 16;
+// Waves per workgroup x k-steps of loads in flight per wave, swept at the K2 shape (d 7168,
+// 384 experts; one box; kernel us at T = 16 / 128 / 512, then with the norm at T = 128):
+// 16 x 4: 21.7 / 22.8 / 60.0, 37.6; 16 x 7: 21.3 / 22.3 / 62.5, 71.1 (the norm variant
+// spills); 8 x 7: 21.0 / 21.8 / 57.8, 43.2; 8 x 14: 21.7 / 22.4 / 63.4, 73.8 (spills);
+// 4 x 14: 22.3 / 23.7 / 61.6, 54.0.
+#ifndef MOE_ROUTER_WAVES
+#define MOE_ROUTER_WAVES 16
+#endif
+constexpr int kRouterWaves = MOE_ROUTER_WAVES;
+// the epilogue's 256 threads each add one (token, expert) logit; the norm takes 16 rows
+static_assert(kRouterWaves >= 4 && kRouterWaves <= 16, "router waves per workgroup");
 #ifndef MOE_ROUTER_KU
 #define MOE_ROUTER_KU 4
 #endif
@@ -114,23 +124,25 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
   const int64_t t0 = (int64_t)blockIdx.x * 16;
   const int e0 = blockIdx.y * 16;
   if constexpr (NORM) {
-    // wave i: row t0 + i; lane l sums pieces l, l + 64, ... (8 elements each), then the 64
-    // partial sums meet in a fixed butterfly order
-    const uint16_t* row = x + min<int64_t>(t0 + wave, T - 1) * d;
+    // wave w: rows t0 + w, t0 + w + kRouterWaves, ...; lane l sums pieces l, l + 64, ...
+    // (8 elements each), then the 64 partial sums of a row meet in a fixed butterfly order
     const int npc = d / 8;
-    double ss = 0.0;
-    for (int c0 = 0; c0 < npc; c0 += 64 * kRouterNormPieces) {
-      u32x4_t v[kRouterNormPieces];
+    for (int i = wave; i < 16; i += kRouterWaves) {
+      const uint16_t* row = x + min<int64_t>(t0 + i, T - 1) * d;
+      double ss = 0.0;
+      for (int c0 = 0; c0 < npc; c0 += 64 * kRouterNormPieces) {
+        u32x4_t v[kRouterNormPieces];
 #pragma unroll
-      for (int u = 0; u < kRouterNormPieces; ++u)
-        v[u] = load16(row + 8 * min(c0 + lane + 64 * u, npc - 1));
+        for (int u = 0; u < kRouterNormPieces; ++u)
+          v[u] = load16(row + 8 * min(c0 + lane + 64 * u, npc - 1));
 #pragma unroll
-      for (int u = 0; u < kRouterNormPieces; ++u)
-        if (c0 + lane + 64 * u < npc) ss = sumsq8(v[u], ss);
+        for (int u = 0; u < kRouterNormPieces; ++u)
+          if (c0 + lane + 64 * u < npc) ss = sumsq8(v[u], ss);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+      if (lane == 0) rinv_s[i] = 1.0 / sqrt(ss / (double)d + (double)eps);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    if (lane == 0) rinv_s[wave] = 1.0 / sqrt(ss / (double)d + (double)eps);
     __syncthreads();
   }
   const int64_t t = min<int64_t>(t0 + r, T - 1);
