@@ -19,7 +19,7 @@
 // Two kernels: "skinny" for row tiles of <= 16 rows (decode: a few tokens per expert),
 // weights streamed from HBM straight into MFMA registers and activations from L2; and an
 // LDS-tiled kernel for 256-row tiles (prefill, and the dense projections), both operands
-// staged in LDS and shared by the workgroup's four waves.
+// staged in LDS and shared by the workgroup's four or eight waves.
 #include "grouped.h"
 
 namespace moe {
@@ -129,6 +129,9 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
 // registers), so every operand fragment read from LDS feeds four MFMAs; the 32x32x16
 // MFMA also reads half the operand bytes per flop of the 16x16x32 one.  On this part
 // the prefill GEMMs run at the power limit, and both choices cut the energy per flop.
+// Or eight waves, two per SIMD, each owning 128 rows x 64 outputs (eight accumulator tiles
+// in VGPRs): more LDS reads per MFMA, but one wave's reads and waits overlap the other's
+// MFMAs, which pays where the tiles are mostly full.
 //
 // K goes in chunks of 64.  Per chunk a workgroup moves 32 KiB of weights and 32 KiB of
 // activations (gate/up: rows of x gathered through perm, each lane's offset naming its
@@ -147,6 +150,12 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
 // slot, so the global reads stay 128 contiguous bytes per row, and an MFMA operand read
 // (16 consecutive rows, one piece) touches 16 distinct 16-byte bank groups.
 constexpr int kLdsChunkK = 64;
+// W = 4 waves per workgroup (one per SIMD, 128 rows x 128 outputs each) or 8 (two per SIMD,
+// 128 rows x 64 outputs each).
+__host__ __device__ constexpr int lds_units(int W) { return 32 / W; }  // 1 KiB transfers
+                                                                     // per wave and operand
+__host__ __device__ constexpr int lds_no(int W) { return W == 4 ? 4 : 2; }  // 32-output
+                                                                          // fragments
 
 struct LdsCtx {
   __amdgpu_buffer_rsrc_t act;  // activation rows (x, or the tile's rows of h)
@@ -165,24 +174,30 @@ struct LdsCtx {
                                // (ncw < nc only for two-part activations)
 };
 
-// Whole-chunk weight move, for the prologue: the wave's 8 weight transfers of chunk c
-// (units 8 wave .. 8 wave + 7).
+// Whole-chunk weight move, for the prologue: the wave's weight transfers of chunk c
+// (units lds_units(W) wave ..).
+template <int W>
 __device__ __forceinline__ void lds_fetch_w(const LdsCtx& x, u32x4_t* wgt, int wave, int c) {
+  constexpr int kLdsUnits = lds_units(W);
   const uint32_t soff = c < x.nc ? (uint32_t)(c >= x.ncw ? c - x.ncw : c) * (kLdsChunkK * 2)
                                   : x.woob;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    dma16(x.wgt, wgt + (wave * 8 + j) * 64, x.woff[j & 1], soff + (uint32_t)j * x.wstride);
+  for (int j = 0; j < kLdsUnits; ++j)
+    dma16(x.wgt, wgt + (wave * kLdsUnits + j) * 64, x.woff[j & 1],
+          soff + (uint32_t)j * x.wstride);
 }
 
 // Sub-step kk reads weight fragment o at slot wrd[kk] + 8 wfrag_row(o) and row fragment t
 // (tile rows 64 t + 32 wm ..) at slot ard[kk] + 512 t (the wave-dependent parts are in
 // wrd/ard, so the fragment offsets are immediates).
-template <bool GATEUP>
+template <bool GATEUP, int W>
 __device__ __forceinline__ constexpr int wfrag_row(int o) {
-  // gate/up: o = 0, 1 are W1 rows 32 o of the wave's 64 features, o = 2, 3 the same
-  // features of W3 (128 rows further); otherwise 32 o
-  return GATEUP ? 128 * (o >> 1) + 32 * (o & 1) : 32 * o;
+  constexpr int kLdsNO = lds_no(W);
+  // four fragments: gate/up o = 0, 1 are W1 rows 32 o of the wave's 64 features, o = 2, 3
+  // the same features of W3 (128 rows further); otherwise 32 o.  Two fragments: gate/up
+  // o = 0 the wave's 32 W1 features, o = 1 the same of W3; otherwise 32 o.
+  return kLdsNO == 4 ? (GATEUP ? 128 * (o >> 1) + 32 * (o & 1) : 32 * o)
+                     : (GATEUP ? 128 * o : 32 * o);
 }
 
 // Chunk c reads activation buffer Acur and weight buffer Wcur; during it the activations
@@ -191,54 +206,69 @@ __device__ __forceinline__ constexpr int wfrag_row(int o) {
 // compiler can tell which pending transfer an LDS read depends on.  At the barrier before chunk c + 1 only the 8 weight transfers of
 // chunk c + 2 may still be in flight: the activation transfers of chunk c + 1 were issued
 // before them, and transfers complete in order.
+template <int W>
 __device__ __forceinline__ void lds_sync8() {
-  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+  constexpr int kLdsUnits = lds_units(W);
+  static_assert(kLdsUnits == 8 || kLdsUnits == 4, "weight transfers per wave");
+  if constexpr (kLdsUnits == 8)
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
+// Half of the wave's activation (weight) transfers of chunk c: units j0 .. j0 + H - 1 of the
+// wave's lds_units(W), H = lds_units(W) / 2.
+template <int W>
 __device__ __forceinline__ void lds_fetch_a(const LdsCtx& x, u32x4_t* act, int wave, int c,
                                             int j0) {
+  constexpr int kLdsUnits = lds_units(W);
   const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.aoob;
 #pragma unroll
-  for (int j = j0; j < j0 + 4; ++j) dma16(x.act, act + (wave * 8 + j) * 64, x.aoff[j], soff);
+  for (int j = j0; j < j0 + kLdsUnits / 2; ++j)
+    dma16(x.act, act + (wave * kLdsUnits + j) * 64, x.aoff[j], soff);
 }
 
+template <int W>
 __device__ __forceinline__ void lds_fetch_w4(const LdsCtx& x, u32x4_t* wgt, int wave, int c,
                                              int j0) {
+  constexpr int kLdsUnits = lds_units(W);
   const uint32_t soff = c < x.nc ? (uint32_t)(c >= x.ncw ? c - x.ncw : c) * (kLdsChunkK * 2)
                                   : x.woob;
 #pragma unroll
-  for (int j = j0; j < j0 + 4; ++j)
-    dma16(x.wgt, wgt + (wave * 8 + j) * 64, x.woff[j & 1], soff + (uint32_t)j * x.wstride);
+  for (int j = j0; j < j0 + kLdsUnits / 2; ++j)
+    dma16(x.wgt, wgt + (wave * kLdsUnits + j) * 64, x.woff[j & 1],
+          soff + (uint32_t)j * x.wstride);
 }
 
-template <bool GATEUP, int NF>
+template <bool GATEUP, int NF, int W>
 __device__ __forceinline__ void lds_chunk_dma(const LdsCtx& x, const u32x4_t* acur,
                                               u32x4_t* anext, const u32x4_t* wcur,
                                               u32x4_t* wnext2, int wave, int c,
-                                              f32x16_t (&acc)[NF > 0 ? NF : 1][4]) {
-  lds_sync8();
+                                              f32x16_t (&acc)[NF > 0 ? NF : 1][lds_no(W)]) {
+  constexpr int kLdsUnits = lds_units(W), kLdsNO = lds_no(W);
+  lds_sync8<W>();
   constexpr int NA = NF > 0 ? NF : 1;
-  u32x4_t wv[2][4], av[2][NA];
+  u32x4_t wv[2][kLdsNO], av[2][NA];
   auto read = [&](int kk, int b) {
 #pragma unroll
-    for (int o = 0; o < 4; ++o) wv[b][o] = wcur[x.wrd[kk] + 8 * wfrag_row<GATEUP>(o)];
+    for (int o = 0; o < kLdsNO; ++o) wv[b][o] = wcur[x.wrd[kk] + 8 * wfrag_row<GATEUP, W>(o)];
 #pragma unroll
     for (int t = 0; t < NF; ++t) av[b][t] = acur[x.ard[kk] + 512 * t];
   };
   if constexpr (NF > 0) read(0, 0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    if (kk < 2) lds_fetch_a(x, anext, wave, c + 1, 4 * kk);
-    else lds_fetch_w4(x, wnext2, wave, c + 2, 4 * (kk - 2));
+    if (kk < 2) lds_fetch_a<W>(x, anext, wave, c + 1, (kLdsUnits / 2) * kk);
+    else lds_fetch_w4<W>(x, wnext2, wave, c + 2, (kLdsUnits / 2) * (kk - 2));
     if constexpr (NF > 0) {
       if (kk < 3) read(kk + 1, (kk + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < NF; ++t)
 #pragma unroll
-        for (int o = 0; o < 4; ++o)
+        for (int o = 0; o < kLdsNO; ++o)
           acc[t][o] = mfma32x32x16(wv[kk & 1][o], av[kk & 1][t], acc[t][o]);
     }
   }
@@ -254,55 +284,61 @@ struct LdsBufs {
 
 // A tile for a wave with NF live row fragments (NF = 0: the wave only moves data): the K
 // loop, then the epilogue.  Every wave runs the same loads and barriers whatever its NF.
-template <int EPI, int NF>
+template <int EPI, int NF, int W>
 __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, const LdsBufs& b,
                                          int wave, int arow, const Tile& tile, int nbase,
                                          int col0) {
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int NA = NF > 0 ? NF : 1;
-  f32x16_t acc[NA][4];
+  constexpr int kLdsUnits = lds_units(W), kLdsNO = lds_no(W);
+  f32x16_t acc[NA][kLdsNO];
 #pragma unroll
   for (int t = 0; t < NA; ++t)
 #pragma unroll
-    for (int o = 0; o < 4; ++o)
+    for (int o = 0; o < kLdsNO; ++o)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[t][o][e] = 0.f;
 
   const int nc = x.nc;
   // prologue: activations of chunk 0, then the weights of chunks 0 and 1 (the first
   // barrier leaves only chunk 1's weights in flight)
-  lds_fetch_a(x, b.A, wave, 0, 0);
-  lds_fetch_a(x, b.A, wave, 0, 4);
-  lds_fetch_w(x, b.W0, wave, 0);
-  lds_fetch_w(x, b.W1, wave, 1);
+  lds_fetch_a<W>(x, b.A, wave, 0, 0);
+  lds_fetch_a<W>(x, b.A, wave, 0, kLdsUnits / 2);
+  lds_fetch_w<W>(x, b.W0, wave, 0);
+  lds_fetch_w<W>(x, b.W1, wave, 1);
   // chunk parity picks the activation buffer, chunk mod 3 the weight buffer: period 6
   int c = 0;
   for (; c + 6 <= nc; c += 6) {
-    lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
-    lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
-    lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
-    lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
-    lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
-    lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W2, b.W1, wave, c + 5, acc);
+    lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
+    lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
+    lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
+    lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
+    lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
+    lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W2, b.W1, wave, c + 5, acc);
   }
-  if (c < nc) lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
-  if (c + 1 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
-  if (c + 2 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
-  if (c + 3 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
-  if (c + 4 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
+  if (c < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
+  if (c + 1 < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
+  if (c + 2 < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
+  if (c + 3 < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
+  if (c + 4 < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
   if constexpr (NF > 0) {
-    // staging: waves 0-1 in the even buffer, 2-3 in the odd one, 16 KiB each
-    if (wave < 2)
-      lds_epilogue<EPI, NF>(a, b.A + (wave & 1) * 1024, acc, arow, 64, tile, nbase, col0);
+    // staging: the first half of the waves in the even buffer, the rest in the odd one
+    // (16 KiB each with four waves, 8 KiB with eight)
+    constexpr int HW = W / 2, SL = 2048 / HW;
+    if (wave < HW)
+      lds_epilogue<EPI, NF, kLdsNO>(a, b.A + (wave % HW) * SL, acc, arow, 64, tile, nbase,
+                                    col0);
     else
-      lds_epilogue<EPI, NF>(a, b.A1 + (wave & 1) * 1024, acc, arow, 64, tile, nbase, col0);
+      lds_epilogue<EPI, NF, kLdsNO>(a, b.A1 + (wave % HW) * SL, acc, arow, 64, tile, nbase,
+                                    col0);
   }
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
+template <int EPI, int W>
+__global__ __launch_bounds__(64 * W, 1) void ffn_lds_kernel(const FfnArgs a) {
+  constexpr int kLdsWaves = W, kLdsUnits = lds_units(W);
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int BM = 256;
   constexpr int FEAT = GATEUP ? 128 : 256;  // features of N per workgroup
@@ -321,7 +357,8 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  // wave (wm, wn): rows half wm, outputs part wn (of 2 with four waves, of 4 with eight)
+  const int wm = wave / (kLdsWaves / 2), wn = wave % (kLdsWaves / 2);
   const int K = a.K, N = a.N;
   const int nrows = tile.row_end - tile.row_begin;
   const int f0 = nb * FEAT;
@@ -343,7 +380,7 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   LdsCtx x;
   // one weight matrix is N*K*2 < 2^32 bytes, and so is x (checked on the host)
   const uint32_t wbytes = (uint32_t)N * (uint32_t)WK * 2u;
-  x.wgt = buffer_rsrc(GATEUP && wave >= 2 ? Wb : Wa, wbytes);
+  x.wgt = buffer_rsrc(GATEUP && wave >= kLdsWaves / 2 ? Wb : Wa, wbytes);
   const uint16_t* abase = GATEUP ? a.A : a.A + (int64_t)tile.row_begin * K;
   const uint32_t abytes = GATEUP ? (uint32_t)(a.a_rows * K * 2) : (uint32_t)nrows * K * 2u;
   x.act = buffer_rsrc(abase, abytes);
@@ -352,8 +389,8 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   // rows past the tile's end load nothing (an offset past the buffer reads zeros and
   // moves no data; their outputs are not stored)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int u = wave * 8 + j, m = 8 * u + (lane >> 3);
+  for (int j = 0; j < kLdsUnits; ++j) {
+    const int u = wave * kLdsUnits + j, m = 8 * u + (lane >> 3);
     const int piece = (lane & 7) ^ (m & 7) ^ (u & 1);
     const int64_t p = tile.row_begin + m;
     x.aoff[j] = p < tile.row_end
@@ -362,10 +399,11 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   }
   // weight row m of the workgroup: gate/up rows 0..127 are W1 features f0 + m, rows
   // 128..255 the same features of W3; otherwise features f0 + m.  Unit j of the wave:
-  // m = 64 wave + 8 j + (lane >> 3), piece (lane & 7) ^ (lane >> 3) ^ (j & 1).  Features
-  // past N read beyond the matrix and get zeros (their outputs are not stored).
+  // m = 8 (kLdsUnits wave + j) + (lane >> 3), piece (lane & 7) ^ (lane >> 3) ^ (j & 1).
+  // Features past N read beyond the matrix and get zeros (their outputs are not stored).
   {
-    const int n0 = f0 + 64 * (GATEUP ? (wave & 1) : wave) + (lane >> 3);
+    constexpr int RPW = 8 * kLdsUnits;  // weight rows per wave
+    const int n0 = f0 + RPW * (GATEUP ? (wave % (kLdsWaves / 2)) : wave) + (lane >> 3);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
       x.woff[e] = (uint32_t)n0 * (uint32_t)WK * 2u + ((lane & 7) ^ (lane >> 3) ^ e) * 16 + kofs;
@@ -374,9 +412,10 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   // the two row halves interleave 32-row fragments (wave wm: tile rows 64 t + 32 wm ..),
   // so a partly filled tile keeps both halves equally busy
   const int arow = 32 * wm;
-  // first weight row of this wave's fragments: gate/up W1 rows 64 wn (W3 rows 128 + 64 wn);
-  // otherwise 128 wn
-  const int wrow0 = (GATEUP ? 64 : 128) * wn;
+  // first weight row of this wave's fragments: gate/up W1 rows 64 wn (W3 rows 128 + 64 wn),
+  // with eight waves 32 wn; otherwise 128 wn, with eight waves 64 wn
+  constexpr int OPW = 256 / (kLdsWaves / 2);  // weight rows of the wave's fragments
+  const int wrow0 = (GATEUP ? OPW / 2 : OPW) * wn;
   {
     const int r32 = lane & 31, sig = (lane & 7) ^ ((r32 >> 3) & 1);
 #pragma unroll
@@ -392,18 +431,18 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(const FfnArgs a) {
   x.aoob = abytes;
   x.woob = wbytes;
   // first output feature of this wave's fragments (gate/up: of its W1 and W3 fragments)
-  const int nbase = f0 + (GATEUP ? 64 : 128) * wn;
+  const int nbase = f0 + (GATEUP ? OPW / 2 : OPW) * wn;
 
   // live 32-row fragments of this wave's half of the tile (wave-uniform)
   const int nf = min(4, max(0, (nrows - arow + 63) / 64));
   const LdsBufs bufs{Ab, Ab1, W0, W1, W2};
   const int col0 = ks * N;  // this slice's columns in a row of Ys
   switch (nf) {
-    case 0: lds_tile<EPI, 0>(a, x, bufs, wave, arow, tile, nbase, col0); break;
-    case 1: lds_tile<EPI, 1>(a, x, bufs, wave, arow, tile, nbase, col0); break;
-    case 2: lds_tile<EPI, 2>(a, x, bufs, wave, arow, tile, nbase, col0); break;
-    case 3: lds_tile<EPI, 3>(a, x, bufs, wave, arow, tile, nbase, col0); break;
-    default: lds_tile<EPI, 4>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 0: lds_tile<EPI, 0, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 1: lds_tile<EPI, 1, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 2: lds_tile<EPI, 2, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 3: lds_tile<EPI, 3, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    default: lds_tile<EPI, 4, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
   }
 }
 
@@ -422,10 +461,28 @@ TileSpec ffn_tile_spec(const FfnShape& sh) {
   return tile_spec_for(sh, use_wide(sh, kWideRowsBf16) ? kWideBM : kSkinnyBM);
 }
 
+// Waves of the 256-row kernel.  Eight (two per SIMD) when the launch's tiles are mostly
+// full: one group (dense projections, the router GEMM), or 512 rows per group and more
+// (skewed routing); four otherwise (prefill with every expert active: ~190 rows per
+// group).  Each forced over the K2-shape layer (ms, one box): prefill T = 8192 8.620 with
+// four / 8.675 with eight (gate/up 4.95 / 5.01, down 3.03 / 3.01); skewed routing T = 4096
+// 3.332 / 3.180 (gate/up 1.83 / 1.72, down 1.16 / 1.08); router GEMM at T = 8192 152 /
+// 144 us, at T = 4096 80 / 74 us.
+constexpr int64_t kWide8RowsPerGroup = 512;
+
+bool wide8(const FfnShape& sh) {
+  const int64_t rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
+  const int64_t groups = sh.E + (sh.shared ? 1 : 0);
+  return groups <= 1 || rows >= kWide8RowsPerGroup * groups;
+}
+
 // The 256-row-tile kernel covers 128 (gate/up) or 256 (otherwise) features of N per block.
 template <int EPI>
-void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a) {
-  hipLaunchKernelGGL(ffn_lds_kernel<EPI>, grid, dim3(256), 0, s, a);
+void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a, bool eight) {
+  if (eight)
+    hipLaunchKernelGGL((ffn_lds_kernel<EPI, 8>), grid, dim3(64 * 8), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_lds_kernel<EPI, 4>), grid, dim3(64 * 4), 0, s, a);
 }
 
 hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
@@ -467,17 +524,17 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
   const bool two = wk > 0;
   switch (mode) {
     case DenseOut::kF32:
-      if (wide) launch_wide<kF32>(dim3(gs.x * nks), s, a);
+      if (wide) launch_wide<kF32>(dim3(gs.x * nks), s, a, true);
       else if (two) hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, kF32, true>), gk, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, kF32>), gk, dim3(256), 0, s, a);
       break;
     case DenseOut::kBF16:
-      if (wide) launch_wide<kBF16>(gs, s, a);
+      if (wide) launch_wide<kBF16>(gs, s, a, true);
       else if (two) hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kBF16, true>), gk2, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kBF16>), gk2, dim3(256), 0, s, a);
       break;
     case DenseOut::kAddBF16:
-      if (wide) launch_wide<kAddBF16>(gs, s, a);
+      if (wide) launch_wide<kAddBF16>(gs, s, a, true);
       else if (two) hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kAddBF16, true>), gk2, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kAddBF16>), gk2, dim3(256), 0, s, a);
       break;
@@ -513,7 +570,7 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   a.E = sh.E;
   a.hsplit = sh.hsplit ? 1 : 0;
   if (wide)
-    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a);
+    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, wide8(sh));
   else
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyGuNF, kSkinnyGuKU, kSwiGLU>),
                        grid_for(sh, BM, 64 * kSkinnyGuNF, a.N), dim3(256), 0, s, a);
@@ -550,7 +607,7 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.wk = sh.hsplit ? sh.I : 0;
   a.E = sh.E;
   if (wide)
-    launch_wide<kF32>(grid_for(sh, BM, kWideBNDown, a.N), s, a);
+    launch_wide<kF32>(grid_for(sh, BM, kWideBNDown, a.N), s, a, wide8(sh));
   else if (sh.hsplit)
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32, true>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);

@@ -142,12 +142,13 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
 
 // Epilogue of the LDS-tiled kernels (256-row tiles).  Accumulator register j of fragment
 // (t, o), lane l, is tile row arow + tstride t + (l & 31) and output
-// 32 o + 8 (j >> 2) + 4 (l >> 5) + (j & 3) of the wave's block (first output nbase), so a direct store writes 16 bytes into each of 32 rows, and the memory
-// system handles such scattered pieces far slower than whole lines.  Instead each wave
-// stages one 32-row fragment at a time in its own 16 KiB of the (by then idle) activation
-// buffers — fp32, the SwiGLU already applied — and reads it back along the rows, so that
-// one store instruction covers whole rows: 2 x 512 B (fp32, 128 outputs) or 4 x 128 B
-// (bf16 h, 64 outputs).
+// 32 o + 8 (j >> 2) + 4 (l >> 5) + (j & 3) of the wave's block (first output nbase), so a
+// direct store writes 16 bytes into each of 32 rows, and the memory system handles such
+// scattered pieces far slower than whole lines.  Instead each wave stages one 32-row
+// fragment at a time in its own part of the (by then idle) activation buffers (32 rows of
+// its outputs in fp32, the SwiGLU already applied: 16 KiB at most) and reads it back along
+// the rows, so that one store instruction covers whole rows: with four fragments 2 x 512 B
+// (fp32, 128 outputs) or 4 x 128 B (bf16 h, 64 outputs), with two 4 x 256 B or 8 x 64 B.
 //
 // Staging layout: row r (0..31) holds FW / 4 pieces of 4 outputs; piece p sits in slot
 // r (FW / 4) + (p ^ (r & 7)), so the 8 lanes that the LDS serves together (8 rows, one
@@ -169,14 +170,16 @@ __device__ __forceinline__ void store_row4(const FfnArgs& a, int64_t p, int nn, 
   }
 }
 
-// col0: first column of this workgroup's K slice in a row of Ys (fp32 output only).
-template <int EPI, int NF>
+// NO: output fragments the wave holds per row fragment (gate/up: the first NO / 2 of W1,
+// the rest the same features of W3).  col0: first column of this workgroup's K slice in a
+// row of Ys (fp32 output only).
+template <int EPI, int NF, int NO = 4>
 __device__ __forceinline__ void lds_epilogue(const FfnArgs& a, u32x4_t* stage,
-                                             const f32x16_t (&acc)[NF][4], int arow,
+                                             const f32x16_t (&acc)[NF][NO], int arow,
                                              int tstride, const Tile& tile, int nbase,
                                              int col0 = 0) {
   constexpr bool GATEUP = EPI == kSwiGLU;
-  constexpr int FO = GATEUP ? 2 : 4;  // 32-output fragments per row
+  constexpr int FO = GATEUP ? NO / 2 : NO;  // 32-output fragments per row
   constexpr int PPR = 8 * FO;         // 16-byte pieces per staged row
   constexpr int RPI = 64 / PPR;       // rows per read-back instruction
   const int lane = threadIdx.x & 63, hl = lane >> 5;
@@ -192,7 +195,7 @@ __device__ __forceinline__ void lds_epilogue(const FfnArgs& a, u32x4_t* stage,
         const f32x16_t& g = acc[t][oo];
         f32x4_t v = {g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
         if constexpr (GATEUP) {
-          const f32x16_t& u = acc[t][oo + 2];
+          const f32x16_t& u = acc[t][oo + NO / 2];
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = swiglu_f32(v[i], u[4 * q + i]);
         }

@@ -153,13 +153,14 @@ def test_fp8_tiny_skinny():
 
 @pytest.mark.parametrize("T", [1, 37, 300])
 def test_fp8_ragged(T):
-    # T = 300 puts 1200 rows on 25 groups: the 128-row stream kernel
+    # T = 300 puts 1200 rows on 25 groups (48 per group): the 256-row kernel, with K = 384
+    # (six 64-k chunks: one pass of its six-chunk loop) and K = 256 (four chunks: the tail)
     cfg = S.with_overrides("tiny", tokens=T, d_model=384, n_experts=24, top_k=3, d_expert=256,
                            d_shared=256)
     full_check(cfg, fp8_inputs(cfg, seed=T))
 
 
-def test_fp8_stream_kernel_no_shared():
+def test_fp8_wide_kernel_no_shared():
     # top-8 of 16 as at K2: without the shared expert the output RMS is small and with
     # two or three large gates the bf16 rounding of h and of the output sit at the edge of
     # the 2e-2 * RMS bar (1.01 of it at k = 3, with h and Y exact); eight gates of ~0.35
@@ -190,9 +191,9 @@ def test_fp8_zero_and_extreme_scales():
 
 
 def test_fp8_zero_and_extreme_scales_wide():
-    # the same scale edits on the 128-row stream kernel (600 tokens, top-8 of 16: ~300 rows per
-    # expert): its per-128-k-block partial sums must keep the zero block and the extreme
-    # scales exact too
+    # the same scale edits on the 256-row kernel (600 tokens, top-8 of 16: ~300 rows per
+    # expert, one full row tile and one partial one): its per-128-k-block partial sums must
+    # keep the zero block and the extreme scales exact too
     cfg = S.with_overrides("tiny", tokens=600, n_experts=16, top_k=8)
     inp = fp8_inputs(cfg, seed=5)
     inp["w1_scale"][0, 0, 1] = 0.0
@@ -208,6 +209,16 @@ def test_fp8_zero_and_extreme_scales_wide():
     touch = [t for t in range(T) if np.isin(idx[t], [0, 1, 2]).any()][:24]
     assert touch
     full_check(cfg, inp, inter_tokens=touch, per_row_bar=True)
+
+
+def test_fp8_wide_kernel_main_loop_every_token():
+    # K = 1024 (gate/up) and 512 (down): 16 and 8 chunks of 64, so the 256-row kernel runs
+    # its six-chunk loop twice and once, then tails of four and two chunks; experts of
+    # ~240 rows fill one row tile, the shared expert's 1024 rows four.  Every token is
+    # compared, and 16 tokens' h and Y.
+    cfg = S.with_overrides("tiny", tokens=1024, d_model=1024, n_experts=16, top_k=4,
+                           d_expert=512, d_shared=512)
+    full_check(cfg, fp8_inputs(cfg, seed=6), inter_tokens=16)
 
 
 @pytest.fixture(scope="module")

@@ -472,6 +472,20 @@ def test_wide_kernel_main_loop_every_token():
     assert c.max() > 256          # some experts span two row tiles
 
 
+def test_wide_kernel_eight_waves_every_token():
+    """512 rows per group and more take the eight-wave 256-row kernel: 2048 tokens, top-2 of
+    8 experts plus the shared one (683 rows per group, experts of two to three row tiles),
+    with h in two bf16 parts (top_k <= 2) so the down GEMM reads K = 2I.  Every token is
+    compared, and 32 tokens' intermediates."""
+    cfg = dict(tokens=2048, d_model=512, n_experts=8, top_k=2, d_expert=256, d_shared=256,
+               routed_scale=2.827, bias="uniform")
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=31))
+    g, _ = full_check(cfg, inp, intermediates=32)
+    c = g["counts"].cpu().numpy()
+    say(f"  rows per expert {c.min()}..{c.max()}")
+    assert c.sum() + cfg["tokens"] >= 512 * (cfg["n_experts"] + 1)
+
+
 def test_tie_break_lower_index():
     cfg = S.with_overrides("tiny", top_k=1)
     inp = S.make_inputs(cfg, "cpu", seed=11)
