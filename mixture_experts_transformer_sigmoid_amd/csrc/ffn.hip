@@ -461,13 +461,14 @@ TileSpec ffn_tile_spec(const FfnShape& sh) {
   return tile_spec_for(sh, use_wide(sh, kWideRowsBf16) ? kWideBM : kSkinnyBM);
 }
 
-// Waves of the 256-row kernel.  Eight (two per SIMD) when the launch's tiles are mostly
-// full: one group (dense projections, the router GEMM), or 512 rows per group and more
-// (skewed routing); four otherwise (prefill with every expert active: ~190 rows per
-// group).  Each forced over the K2-shape layer (ms, one box): prefill T = 8192 8.620 with
-// four / 8.675 with eight (gate/up 4.95 / 5.01, down 3.03 / 3.01); skewed routing T = 4096
-// 3.332 / 3.180 (gate/up 1.83 / 1.72, down 1.16 / 1.08); router GEMM at T = 8192 152 /
-// 144 us, at T = 4096 80 / 74 us.
+// Waves of the 256-row kernel: eight (two per SIMD) or four.  Each forced over the
+// K2-shape layer (ms, one box): prefill T = 8192 8.620 with four / 8.675 with eight
+// (gate/up 4.95 / 5.01, down 3.03 / 3.01); skewed routing T = 4096 3.332 / 3.180 (gate/up
+// 1.83 / 1.72, down 1.16 / 1.08); router GEMM at T = 8192 152 / 144 us, at T = 4096 80 /
+// 74 us.  So the down GEMM and every launch of one group (dense projections, the router
+// GEMM) take eight; gate/up takes eight only where the host knows the tiles are mostly
+// full, 512 rows per group and more on average (the host cannot see a skewed routing:
+// that depends on the device's counts).
 constexpr int64_t kWide8RowsPerGroup = 512;
 
 bool wide8(const FfnShape& sh) {
@@ -607,7 +608,7 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.wk = sh.hsplit ? sh.I : 0;
   a.E = sh.E;
   if (wide)
-    launch_wide<kF32>(grid_for(sh, BM, kWideBNDown, a.N), s, a, wide8(sh));
+    launch_wide<kF32>(grid_for(sh, BM, kWideBNDown, a.N), s, a, true);
   else if (sh.hsplit)
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32, true>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
