@@ -43,9 +43,11 @@ Readings where the pages are silent:
 * FP8 expert weights: OCP E4M3 values with one fp32 scale per 128 x 128 block of each
   [out, in] matrix; the weight is value x scale, exactly (dequant_fp8_blocks).
 
-Parity pins: see tests/test_oracle_pins.py.  The output values themselves have no
-worked example on the pages ("parity unpinned" beyond the invariants and closed
-forms the pins check).
+Parity pins: tests/test_oracle_pins.py pins every function here against something other
+than itself: library routines (scipy, torch), brute force on tiny inputs, closed forms,
+invariants and discriminating special cases, the page's parameter count, and a planted
+mistake that a pin must catch.  The pages print no worked example of output values, so no
+pin is a page-printed output.
 """
 from __future__ import annotations
 
