@@ -339,6 +339,7 @@ __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, cons
 template <int EPI, int W>
 __global__ __launch_bounds__(64 * W, 1) void ffn_lds_kernel(const FfnArgs a) {
   constexpr int kLdsWaves = W, kLdsUnits = lds_units(W);
+  if (a.wsel != nullptr && *a.wsel != W) return;
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int BM = 256;
   constexpr int FEAT = GATEUP ? 128 : 256;  // features of N per workgroup
@@ -466,9 +467,10 @@ TileSpec ffn_tile_spec(const FfnShape& sh) {
 // (gate/up 4.95 / 5.01, down 3.03 / 3.01); skewed routing T = 4096 3.332 / 3.180 (gate/up
 // 1.83 / 1.72, down 1.16 / 1.08); router GEMM at T = 8192 152 / 144 us, at T = 4096 80 /
 // 74 us.  So the down GEMM and every launch of one group (dense projections, the router
-// GEMM) take eight; gate/up takes eight only where the host knows the tiles are mostly
-// full, 512 rows per group and more on average (the host cannot see a skewed routing:
-// that depends on the device's counts).
+// GEMM) take eight.  Gate/up takes eight where the host knows the tiles are mostly full
+// (512 rows per group and more on average); otherwise the tile builder decides from the
+// device's counts (a skewed routing fills whole tiles) and both counts are launched, the
+// one not chosen returning at once.
 constexpr int64_t kWide8RowsPerGroup = 512;
 
 bool wide8(const FfnShape& sh) {
@@ -570,11 +572,16 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   a.K = sh.d;
   a.E = sh.E;
   a.hsplit = sh.hsplit ? 1 : 0;
-  if (wide)
-    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, wide8(sh));
-  else
+  if (wide && wide8(sh)) {
+    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, true);
+  } else if (wide) {
+    a.wsel = ntiles + 1;
+    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, false);
+    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, true);
+  } else {
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyGuNF, kSkinnyGuKU, kSwiGLU>),
                        grid_for(sh, BM, 64 * kSkinnyGuNF, a.N), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -31,6 +31,8 @@ struct FfnArgs {
   float* Ys;              // down: y_shared [T, N] fp32
   const Tile* tiles;
   const int32_t* ntiles;
+  const int32_t* wsel;    // 256-row bf16 kernel: the wave count the tile builder chose (a
+                          // workgroup of another count returns at once); null: no check
   int32_t k;              // slots per token (gate/up gather: token = slot / k)
   int32_t N, K, E;
   int32_t ksplit;         // 256-row kernel, fp32 output: K slices (0 or 1: none)
@@ -248,7 +250,7 @@ constexpr int kSkinnyKU = MOE_SKINNY_KU;  // skinny: k-steps (of 32) per batch o
 // 3.54 ms with the down GEMM's 2 x 8)
 constexpr int kSkinnyGuNF = MOE_SKINNY_GU_NF;
 constexpr int kSkinnyGuKU = MOE_SKINNY_GU_KU;
-// 256-row kernels (bf16 LDS-tiled, FP8 stream): features of N per workgroup
+// bf16 256-row kernel: features of N per workgroup
 constexpr int kWideBNGateUp = 128;  // gate/up: 128 features of W1 and the same of W3
 constexpr int kWideBNDown = 256;
 
@@ -263,8 +265,7 @@ int64_t max_tiles_for(const FfnShape& sh, int BM) {
 constexpr int64_t kSingleGroupWideRows = 512;
 
 // Average rows per group (routed experts plus the shared expert) decides the kernel: up to
-// rows_per_group (decode) -> skinny kernel; more -> the 256-row (bf16) or 128-row (FP8)
-// kernel.  Each weight type passes its own crossover, measured with the routed experts
+// rows_per_group (decode) -> skinny kernel; more -> the 256-row kernel (bf16 or FP8).  Each weight type passes its own crossover, measured with the routed experts
 // present; a launch of one group uses kSingleGroupWideRows instead.
 bool use_wide(const FfnShape& sh, int rows_per_group) {
   const int64_t rows = sh.T * sh.k + (sh.shared ? sh.T : 0);

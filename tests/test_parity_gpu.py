@@ -486,6 +486,25 @@ def test_wide_kernel_eight_waves_every_token():
     assert c.sum() + cfg["tokens"] >= 512 * (cfg["n_experts"] + 1)
 
 
+def test_wide_kernel_waves_chosen_on_device_every_token():
+    """Groups averaging under 512 rows leave the gate/up wave count to the device.  A bias of
+    +1 on four of 64 experts sends both slots of every token to them (about 1,024 rows each,
+    whole 256-row tiles), so the tile builder picks eight waves while the host sees 95 rows
+    per group; h is in two bf16 parts (top-2).  Every token is compared, and 32 tokens'
+    intermediates."""
+    cfg = dict(tokens=2048, d_model=512, n_experts=64, top_k=2, d_expert=256, d_shared=256,
+               routed_scale=2.827, bias="uniform")
+    inp = S.make_inputs(cfg, "cpu", seed=32)
+    inp["b"][:4] += 1.0
+    inp = to_dev(inp)
+    g, _ = full_check(cfg, inp, intermediates=32)
+    c = g["counts"].cpu().numpy()
+    say(f"  rows per expert (first four) {c[:4]}")
+    assert c[4:].sum() == 0
+    full = int((c // 256 * 256).sum()) + cfg["tokens"] // 256 * 256
+    assert 2 * full >= int(c.sum()) + cfg["tokens"]
+
+
 def test_tie_break_lower_index():
     cfg = S.with_overrides("tiny", top_k=1)
     inp = S.make_inputs(cfg, "cpu", seed=11)
