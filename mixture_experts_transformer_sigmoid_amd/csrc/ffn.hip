@@ -203,11 +203,12 @@ __device__ __forceinline__ constexpr int wfrag_row(int o) {
 // Chunk c reads activation buffer Acur and weight buffer Wcur; during it the activations
 // of chunk c + 1 go to Anext (sub-steps 0 and 1, four units each) and the weights of chunk
 // c + 2 to Wnext2 (sub-steps 2 and 3).  All buffers are separate LDS arrays, so the
-// compiler can tell which pending transfer an LDS read depends on.  At the barrier before chunk c + 1 only the 8 weight transfers of
-// chunk c + 2 may still be in flight: the activation transfers of chunk c + 1 were issued
+// compiler can tell which pending transfer an LDS read depends on.  At the barrier before
+// chunk c + 1 only the wave's weight transfers of chunk c + 2 (8 with four waves, 4 with
+// eight) may still be in flight: the activation transfers of chunk c + 1 were issued
 // before them, and transfers complete in order.
 template <int W>
-__device__ __forceinline__ void lds_sync8() {
+__device__ __forceinline__ void lds_sync_chunk() {
   constexpr int kLdsUnits = lds_units(W);
   static_assert(kLdsUnits == 8 || kLdsUnits == 4, "weight transfers per wave");
   if constexpr (kLdsUnits == 8)
@@ -231,8 +232,8 @@ __device__ __forceinline__ void lds_fetch_a(const LdsCtx& x, u32x4_t* act, int w
 }
 
 template <int W>
-__device__ __forceinline__ void lds_fetch_w4(const LdsCtx& x, u32x4_t* wgt, int wave, int c,
-                                             int j0) {
+__device__ __forceinline__ void lds_fetch_w_half(const LdsCtx& x, u32x4_t* wgt, int wave,
+                                                 int c, int j0) {
   constexpr int kLdsUnits = lds_units(W);
   const uint32_t soff = c < x.nc ? (uint32_t)(c >= x.ncw ? c - x.ncw : c) * (kLdsChunkK * 2)
                                   : x.woob;
@@ -248,7 +249,7 @@ __device__ __forceinline__ void lds_chunk_dma(const LdsCtx& x, const u32x4_t* ac
                                               u32x4_t* wnext2, int wave, int c,
                                               f32x16_t (&acc)[NF > 0 ? NF : 1][lds_no(W)]) {
   constexpr int kLdsUnits = lds_units(W), kLdsNO = lds_no(W);
-  lds_sync8<W>();
+  lds_sync_chunk<W>();
   constexpr int NA = NF > 0 ? NF : 1;
   u32x4_t wv[2][kLdsNO], av[2][NA];
   auto read = [&](int kk, int b) {
@@ -261,7 +262,7 @@ __device__ __forceinline__ void lds_chunk_dma(const LdsCtx& x, const u32x4_t* ac
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kk < 2) lds_fetch_a<W>(x, anext, wave, c + 1, (kLdsUnits / 2) * kk);
-    else lds_fetch_w4<W>(x, wnext2, wave, c + 2, (kLdsUnits / 2) * (kk - 2));
+    else lds_fetch_w_half<W>(x, wnext2, wave, c + 2, (kLdsUnits / 2) * (kk - 2));
     if constexpr (NF > 0) {
       if (kk < 3) read(kk + 1, (kk + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -572,12 +573,16 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   a.K = sh.d;
   a.E = sh.E;
   a.hsplit = sh.hsplit ? 1 : 0;
+  // fewer rows than one whole tile: the tile builder cannot choose eight waves
+  const bool may_fill = sh.T * sh.k + (sh.shared ? sh.T : 0) >= kWideBM;
   if (wide && wide8(sh)) {
     launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, true);
-  } else if (wide) {
+  } else if (wide && may_fill) {
     a.wsel = ntiles + 1;
     launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, false);
     launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, true);
+  } else if (wide) {
+    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, false);
   } else {
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyGuNF, kSkinnyGuKU, kSwiGLU>),
                        grid_for(sh, BM, 64 * kSkinnyGuNF, a.N), dim3(256), 0, s, a);
