@@ -19,7 +19,7 @@
 // Two kernels: "skinny" for row tiles of <= 16 rows (decode: a few tokens per expert),
 // weights streamed from HBM straight into MFMA registers and activations from L2; and an
 // LDS-tiled kernel for 256-row tiles (prefill, and the dense projections), both operands
-// staged in LDS and shared by the workgroup's four or eight waves.
+// staged in LDS and shared by the workgroup's eight waves.
 #include "grouped.h"
 
 namespace moe {
@@ -124,14 +124,13 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
 
 // ------------------------------------------------------------- LDS-tiled GEMM
 // 256-row tiles x 256 outputs per workgroup (gate/up: 128 features of W1 and the same 128
-// of W3; otherwise 256 features).  Four waves, one per SIMD, each owning a 128-row x
-// 128-output quarter as sixteen 32 x 32 fp32 accumulator tiles (256 accumulator
-// registers), so every operand fragment read from LDS feeds four MFMAs; the 32x32x16
-// MFMA also reads half the operand bytes per flop of the 16x16x32 one.  On this part
-// the prefill GEMMs run at the power limit, and both choices cut the energy per flop.
-// Or eight waves, two per SIMD, each owning 128 rows x 64 outputs (eight accumulator tiles
-// in VGPRs): more LDS reads per MFMA, but one wave's reads and waits overlap the other's
-// MFMAs, which pays where the tiles are mostly full.
+// of W3; otherwise 256 features).  Eight waves, two per SIMD, each owning 128 rows x 64
+// outputs as eight 32 x 32 fp32 accumulator tiles in VGPRs, so every activation fragment
+// read from LDS feeds two MFMAs and every weight fragment four; the 32x32x16 MFMA also
+// reads half the operand bytes per flop of the 16x16x32 one.  With two waves per SIMD one
+// wave's LDS reads and waits overlap the other's MFMAs.  (Four waves, one per SIMD, each
+// with a 128 x 128 quarter in 256 accumulator registers, read less LDS per MFMA but hide
+// nothing; they measured slower.)
 //
 // K goes in chunks of 64.  Per chunk a workgroup moves 32 KiB of weights and 32 KiB of
 // activations (gate/up: rows of x gathered through perm, each lane's offset naming its
@@ -150,12 +149,12 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
 // slot, so the global reads stay 128 contiguous bytes per row, and an MFMA operand read
 // (16 consecutive rows, one piece) touches 16 distinct 16-byte bank groups.
 constexpr int kLdsChunkK = 64;
-// W = 4 waves per workgroup (one per SIMD, 128 rows x 128 outputs each) or 8 (two per SIMD,
-// 128 rows x 64 outputs each).
-__host__ __device__ constexpr int lds_units(int W) { return 32 / W; }  // 1 KiB transfers
-                                                                     // per wave and operand
-__host__ __device__ constexpr int lds_no(int W) { return W == 4 ? 4 : 2; }  // 32-output
-                                                                          // fragments
+// Waves per workgroup: 8.  The kernel is also written for 4 (one per SIMD, 128 rows x 128
+// outputs each); eight measured faster at the K2 shape (see the launch below).
+constexpr int kLdsWaves = 8;
+static_assert(kLdsWaves == 4 || kLdsWaves == 8, "waves per 256-row workgroup");
+constexpr int kLdsUnits = 32 / kLdsWaves;       // 1 KiB transfers per wave and operand
+constexpr int kLdsNO = kLdsWaves == 4 ? 4 : 2;  // 32-output fragments per wave
 
 struct LdsCtx {
   __amdgpu_buffer_rsrc_t act;  // activation rows (x, or the tile's rows of h)
@@ -175,10 +174,8 @@ struct LdsCtx {
 };
 
 // Whole-chunk weight move, for the prologue: the wave's weight transfers of chunk c
-// (units lds_units(W) wave ..).
-template <int W>
+// (units kLdsUnits wave ..).
 __device__ __forceinline__ void lds_fetch_w(const LdsCtx& x, u32x4_t* wgt, int wave, int c) {
-  constexpr int kLdsUnits = lds_units(W);
   const uint32_t soff = c < x.nc ? (uint32_t)(c >= x.ncw ? c - x.ncw : c) * (kLdsChunkK * 2)
                                   : x.woob;
 #pragma unroll
@@ -190,9 +187,8 @@ __device__ __forceinline__ void lds_fetch_w(const LdsCtx& x, u32x4_t* wgt, int w
 // Sub-step kk reads weight fragment o at slot wrd[kk] + 8 wfrag_row(o) and row fragment t
 // (tile rows 64 t + 32 wm ..) at slot ard[kk] + 512 t (the wave-dependent parts are in
 // wrd/ard, so the fragment offsets are immediates).
-template <bool GATEUP, int W>
+template <bool GATEUP>
 __device__ __forceinline__ constexpr int wfrag_row(int o) {
-  constexpr int kLdsNO = lds_no(W);
   // four fragments: gate/up o = 0, 1 are W1 rows 32 o of the wave's 64 features, o = 2, 3
   // the same features of W3 (128 rows further); otherwise 32 o.  Two fragments: gate/up
   // o = 0 the wave's 32 W1 features, o = 1 the same of W3; otherwise 32 o.
@@ -201,15 +197,13 @@ __device__ __forceinline__ constexpr int wfrag_row(int o) {
 }
 
 // Chunk c reads activation buffer Acur and weight buffer Wcur; during it the activations
-// of chunk c + 1 go to Anext (sub-steps 0 and 1, four units each) and the weights of chunk
-// c + 2 to Wnext2 (sub-steps 2 and 3).  All buffers are separate LDS arrays, so the
+// of chunk c + 1 go to Anext (sub-steps 0 and 1, half of the wave's units each) and the
+// weights of chunk c + 2 to Wnext2 (sub-steps 2 and 3).  All buffers are separate LDS arrays, so the
 // compiler can tell which pending transfer an LDS read depends on.  At the barrier before
 // chunk c + 1 only the wave's weight transfers of chunk c + 2 (8 with four waves, 4 with
 // eight) may still be in flight: the activation transfers of chunk c + 1 were issued
 // before them, and transfers complete in order.
-template <int W>
 __device__ __forceinline__ void lds_sync_chunk() {
-  constexpr int kLdsUnits = lds_units(W);
   static_assert(kLdsUnits == 8 || kLdsUnits == 4, "weight transfers per wave");
   if constexpr (kLdsUnits == 8)
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
@@ -220,21 +214,17 @@ __device__ __forceinline__ void lds_sync_chunk() {
 }
 
 // Half of the wave's activation (weight) transfers of chunk c: units j0 .. j0 + H - 1 of the
-// wave's lds_units(W), H = lds_units(W) / 2.
-template <int W>
+// wave's kLdsUnits, H = kLdsUnits / 2.
 __device__ __forceinline__ void lds_fetch_a(const LdsCtx& x, u32x4_t* act, int wave, int c,
                                             int j0) {
-  constexpr int kLdsUnits = lds_units(W);
   const uint32_t soff = c < x.nc ? (uint32_t)c * (kLdsChunkK * 2) : x.aoob;
 #pragma unroll
   for (int j = j0; j < j0 + kLdsUnits / 2; ++j)
     dma16(x.act, act + (wave * kLdsUnits + j) * 64, x.aoff[j], soff);
 }
 
-template <int W>
 __device__ __forceinline__ void lds_fetch_w_half(const LdsCtx& x, u32x4_t* wgt, int wave,
                                                  int c, int j0) {
-  constexpr int kLdsUnits = lds_units(W);
   const uint32_t soff = c < x.nc ? (uint32_t)(c >= x.ncw ? c - x.ncw : c) * (kLdsChunkK * 2)
                                   : x.woob;
 #pragma unroll
@@ -243,26 +233,25 @@ __device__ __forceinline__ void lds_fetch_w_half(const LdsCtx& x, u32x4_t* wgt, 
           soff + (uint32_t)j * x.wstride);
 }
 
-template <bool GATEUP, int NF, int W>
+template <bool GATEUP, int NF>
 __device__ __forceinline__ void lds_chunk_dma(const LdsCtx& x, const u32x4_t* acur,
                                               u32x4_t* anext, const u32x4_t* wcur,
                                               u32x4_t* wnext2, int wave, int c,
-                                              f32x16_t (&acc)[NF > 0 ? NF : 1][lds_no(W)]) {
-  constexpr int kLdsUnits = lds_units(W), kLdsNO = lds_no(W);
-  lds_sync_chunk<W>();
+                                              f32x16_t (&acc)[NF > 0 ? NF : 1][kLdsNO]) {
+  lds_sync_chunk();
   constexpr int NA = NF > 0 ? NF : 1;
   u32x4_t wv[2][kLdsNO], av[2][NA];
   auto read = [&](int kk, int b) {
 #pragma unroll
-    for (int o = 0; o < kLdsNO; ++o) wv[b][o] = wcur[x.wrd[kk] + 8 * wfrag_row<GATEUP, W>(o)];
+    for (int o = 0; o < kLdsNO; ++o) wv[b][o] = wcur[x.wrd[kk] + 8 * wfrag_row<GATEUP>(o)];
 #pragma unroll
     for (int t = 0; t < NF; ++t) av[b][t] = acur[x.ard[kk] + 512 * t];
   };
   if constexpr (NF > 0) read(0, 0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    if (kk < 2) lds_fetch_a<W>(x, anext, wave, c + 1, (kLdsUnits / 2) * kk);
-    else lds_fetch_w_half<W>(x, wnext2, wave, c + 2, (kLdsUnits / 2) * (kk - 2));
+    if (kk < 2) lds_fetch_a(x, anext, wave, c + 1, (kLdsUnits / 2) * kk);
+    else lds_fetch_w_half(x, wnext2, wave, c + 2, (kLdsUnits / 2) * (kk - 2));
     if constexpr (NF > 0) {
       if (kk < 3) read(kk + 1, (kk + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -285,13 +274,12 @@ struct LdsBufs {
 
 // A tile for a wave with NF live row fragments (NF = 0: the wave only moves data): the K
 // loop, then the epilogue.  Every wave runs the same loads and barriers whatever its NF.
-template <int EPI, int NF, int W>
+template <int EPI, int NF>
 __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, const LdsBufs& b,
                                          int wave, int arow, const Tile& tile, int nbase,
                                          int col0) {
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int NA = NF > 0 ? NF : 1;
-  constexpr int kLdsUnits = lds_units(W), kLdsNO = lds_no(W);
   f32x16_t acc[NA][kLdsNO];
 #pragma unroll
   for (int t = 0; t < NA; ++t)
@@ -303,31 +291,31 @@ __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, cons
   const int nc = x.nc;
   // prologue: activations of chunk 0, then the weights of chunks 0 and 1 (the first
   // barrier leaves only chunk 1's weights in flight)
-  lds_fetch_a<W>(x, b.A, wave, 0, 0);
-  lds_fetch_a<W>(x, b.A, wave, 0, kLdsUnits / 2);
-  lds_fetch_w<W>(x, b.W0, wave, 0);
-  lds_fetch_w<W>(x, b.W1, wave, 1);
+  lds_fetch_a(x, b.A, wave, 0, 0);
+  lds_fetch_a(x, b.A, wave, 0, kLdsUnits / 2);
+  lds_fetch_w(x, b.W0, wave, 0);
+  lds_fetch_w(x, b.W1, wave, 1);
   // chunk parity picks the activation buffer, chunk mod 3 the weight buffer: period 6
   int c = 0;
   for (; c + 6 <= nc; c += 6) {
-    lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
-    lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
-    lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
-    lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
-    lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
-    lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W2, b.W1, wave, c + 5, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
+    lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W2, b.W1, wave, c + 5, acc);
   }
-  if (c < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
-  if (c + 1 < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
-  if (c + 2 < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
-  if (c + 3 < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
-  if (c + 4 < nc) lds_chunk_dma<GATEUP, NF, W>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
+  if (c < nc) lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W0, b.W2, wave, c, acc);
+  if (c + 1 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W1, b.W0, wave, c + 1, acc);
+  if (c + 2 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W2, b.W1, wave, c + 2, acc);
+  if (c + 3 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A1, b.A, b.W0, b.W2, wave, c + 3, acc);
+  if (c + 4 < nc) lds_chunk_dma<GATEUP, NF>(x, b.A, b.A1, b.W1, b.W0, wave, c + 4, acc);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
   if constexpr (NF > 0) {
     // staging: the first half of the waves in the even buffer, the rest in the odd one
     // (16 KiB each with four waves, 8 KiB with eight)
-    constexpr int HW = W / 2, SL = 2048 / HW;
+    constexpr int HW = kLdsWaves / 2, SL = 2048 / HW;
     if (wave < HW)
       lds_epilogue<EPI, NF, kLdsNO>(a, b.A + (wave % HW) * SL, acc, arow, 64, tile, nbase,
                                     col0);
@@ -337,10 +325,8 @@ __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, cons
   }
 }
 
-template <int EPI, int W>
-__global__ __launch_bounds__(64 * W, 1) void ffn_lds_kernel(const FfnArgs a) {
-  constexpr int kLdsWaves = W, kLdsUnits = lds_units(W);
-  if (a.wsel != nullptr && *a.wsel != W) return;
+template <int EPI>
+__global__ __launch_bounds__(64 * kLdsWaves, 1) void ffn_lds_kernel(const FfnArgs a) {
   constexpr bool GATEUP = EPI == kSwiGLU;
   constexpr int BM = 256;
   constexpr int FEAT = GATEUP ? 128 : 256;  // features of N per workgroup
@@ -440,11 +426,11 @@ __global__ __launch_bounds__(64 * W, 1) void ffn_lds_kernel(const FfnArgs a) {
   const LdsBufs bufs{Ab, Ab1, W0, W1, W2};
   const int col0 = ks * N;  // this slice's columns in a row of Ys
   switch (nf) {
-    case 0: lds_tile<EPI, 0, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
-    case 1: lds_tile<EPI, 1, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
-    case 2: lds_tile<EPI, 2, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
-    case 3: lds_tile<EPI, 3, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
-    default: lds_tile<EPI, 4, W>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 0: lds_tile<EPI, 0>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 1: lds_tile<EPI, 1>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 2: lds_tile<EPI, 2>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    case 3: lds_tile<EPI, 3>(a, x, bufs, wave, arow, tile, nbase, col0); break;
+    default: lds_tile<EPI, 4>(a, x, bufs, wave, arow, tile, nbase, col0); break;
   }
 }
 
@@ -463,30 +449,14 @@ TileSpec ffn_tile_spec(const FfnShape& sh) {
   return tile_spec_for(sh, use_wide(sh, kWideRowsBf16) ? kWideBM : kSkinnyBM);
 }
 
-// Waves of the 256-row kernel: eight (two per SIMD) or four.  Each forced over the
-// K2-shape layer (ms, one box): prefill T = 8192 8.620 with four / 8.675 with eight
-// (gate/up 4.95 / 5.01, down 3.03 / 3.01); skewed routing T = 4096 3.332 / 3.180 (gate/up
-// 1.83 / 1.72, down 1.16 / 1.08); router GEMM at T = 8192 152 / 144 us, at T = 4096 80 /
-// 74 us.  So the down GEMM and every launch of one group (dense projections, the router
-// GEMM) take eight.  Gate/up takes eight where the host knows the tiles are mostly full
-// (512 rows per group and more on average); otherwise the tile builder decides from the
-// device's counts (a skewed routing fills whole tiles) and both counts are launched, the
-// one not chosen returning at once.
-constexpr int64_t kWide8RowsPerGroup = 512;
-
-bool wide8(const FfnShape& sh) {
-  const int64_t rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
-  const int64_t groups = sh.E + (sh.shared ? 1 : 0);
-  return groups <= 1 || rows >= kWide8RowsPerGroup * groups;
-}
-
+// Eight waves against four, each forced over the K2-shape layer: prefill gate/up 5.07-5.13
+// against 5.22-5.28 ms (alternating runs on one box, three each), down 3.01 against 3.03;
+// skewed routing 3.18-3.19 against 3.30-3.33 ms; the latent variant 4.26 against 4.27;
+// the router GEMM 144 against 152 us (T = 8192) and 74 against 80 us (T = 4096).
 // The 256-row-tile kernel covers 128 (gate/up) or 256 (otherwise) features of N per block.
 template <int EPI>
-void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a, bool eight) {
-  if (eight)
-    hipLaunchKernelGGL((ffn_lds_kernel<EPI, 8>), grid, dim3(64 * 8), 0, s, a);
-  else
-    hipLaunchKernelGGL((ffn_lds_kernel<EPI, 4>), grid, dim3(64 * 4), 0, s, a);
+void launch_wide(dim3 grid, hipStream_t s, const FfnArgs& a) {
+  hipLaunchKernelGGL(ffn_lds_kernel<EPI>, grid, dim3(64 * kLdsWaves), 0, s, a);
 }
 
 hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* W, int N,
@@ -528,17 +498,17 @@ hipError_t launch_dense(const uint16_t* A, int64_t rows, int K, const uint16_t* 
   const bool two = wk > 0;
   switch (mode) {
     case DenseOut::kF32:
-      if (wide) launch_wide<kF32>(dim3(gs.x * nks), s, a, true);
+      if (wide) launch_wide<kF32>(dim3(gs.x * nks), s, a);
       else if (two) hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, kF32, true>), gk, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<1, kSkinnyKU, kF32>), gk, dim3(256), 0, s, a);
       break;
     case DenseOut::kBF16:
-      if (wide) launch_wide<kBF16>(gs, s, a, true);
+      if (wide) launch_wide<kBF16>(gs, s, a);
       else if (two) hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kBF16, true>), gk2, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kBF16>), gk2, dim3(256), 0, s, a);
       break;
     case DenseOut::kAddBF16:
-      if (wide) launch_wide<kAddBF16>(gs, s, a, true);
+      if (wide) launch_wide<kAddBF16>(gs, s, a);
       else if (two) hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kAddBF16, true>), gk2, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((ffn_skinny_kernel<2, kSkinnyKU, kAddBF16>), gk2, dim3(256), 0, s, a);
       break;
@@ -573,16 +543,8 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
   a.K = sh.d;
   a.E = sh.E;
   a.hsplit = sh.hsplit ? 1 : 0;
-  // fewer rows than one whole tile: the tile builder cannot choose eight waves
-  const bool may_fill = sh.T * sh.k + (sh.shared ? sh.T : 0) >= kWideBM;
-  if (wide && wide8(sh)) {
-    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, true);
-  } else if (wide && may_fill) {
-    a.wsel = ntiles + 1;
-    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, false);
-    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, true);
-  } else if (wide) {
-    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a, false);
+  if (wide) {
+    launch_wide<kSwiGLU>(grid_for(sh, BM, kWideBNGateUp, a.N), s, a);
   } else {
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyGuNF, kSkinnyGuKU, kSwiGLU>),
                        grid_for(sh, BM, 64 * kSkinnyGuNF, a.N), dim3(256), 0, s, a);
@@ -620,7 +582,7 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.wk = sh.hsplit ? sh.I : 0;
   a.E = sh.E;
   if (wide)
-    launch_wide<kF32>(grid_for(sh, BM, kWideBNDown, a.N), s, a, true);
+    launch_wide<kF32>(grid_for(sh, BM, kWideBNDown, a.N), s, a);
   else if (sh.hsplit)
     hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32, true>),
                        grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);

@@ -31,8 +31,6 @@ struct FfnArgs {
   float* Ys;              // down: y_shared [T, N] fp32
   const Tile* tiles;
   const int32_t* ntiles;
-  const int32_t* wsel;    // 256-row bf16 kernel: the wave count the tile builder chose (a
-                          // workgroup of another count returns at once); null: no check
   int32_t k;              // slots per token (gate/up gather: token = slot / k)
   int32_t N, K, E;
   int32_t ksplit;         // 256-row kernel, fp32 output: K slices (0 or 1: none)

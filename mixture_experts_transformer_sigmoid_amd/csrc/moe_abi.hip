@@ -100,7 +100,7 @@ Layout layout(const moe_dims& d) {
   L.hist = take(nb * E * 4);
   L.base = take(nb * E * 4);
   L.tiles = take(max_tiles * sizeof(Tile));
-  L.ntiles = take(8);  // tile count, waves for the gate/up launch
+  L.ntiles = take(4);
   L.h = take(rows * h_width(d) * 2);
   L.y = take(rows * (size_t)d.d_model * 4);
   L.total = off;
@@ -237,7 +237,7 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
   P.hist = take(nb * E * 4);
   P.base = take(nb * E * 4);
   P.tiles = take(max_tiles * sizeof(Tile));
-  P.ntiles = take(8);  // tile count, waves for the gate/up launch
+  P.ntiles = take(4);
   P.lat = take(T * (size_t)L * 2);
   P.h = take(slots * h_width(d) * 2);
   P.hs = take(has_shared(d) ? T * h_width(d) * 2 : 0);

@@ -20,15 +20,11 @@ namespace {
 constexpr int kMaxSharedParts = 8;
 
 // The list for one set of offsets, built by one workgroup of 1024 threads (every thread
-// must call it).  offsets may point to global or LDS memory.  ntiles[0] receives the
-// number of tiles; ntiles[1] the waves a 256-row bf16 gate/up workgroup should run, 8 when
-// at least half of the rows sit in full tiles (their workgroups keep both waves of a SIMD
-// busy), else 4.
+// must call it).  offsets may point to global or LDS memory.
 __device__ void build_tiles_block(const int32_t* offsets, int E, int64_t routed_rows,
                                   int64_t shared_rows, int BM, int parts, int64_t capacity,
                                   Tile* __restrict__ tiles, int32_t* __restrict__ ntiles) {
   __shared__ int32_t wsum[16];
-  __shared__ int32_t wfull[16];
   __shared__ int32_t routed_total;
   __shared__ int32_t set_start[kMaxSharedParts + 1];  // routed tiles before expert E*i/P
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -46,11 +42,6 @@ __device__ void build_tiles_block(const int32_t* offsets, int E, int64_t routed_
     if (lane >= off) v += o;
   }
   if (lane == 63) wsum[wave] = v;
-  // rows of this expert that fill whole tiles
-  int32_t full = (o1 - o0) / BM * BM;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) full += __shfl_xor(full, off);
-  if (lane == 0) wfull[wave] = full;
   __syncthreads();
   if (tid == 0) {
     int32_t acc = 0;
@@ -112,12 +103,7 @@ __device__ void build_tiles_block(const int32_t* offsets, int E, int64_t routed_
     t.pad[0] = t.pad[1] = t.pad[2] = 0;
     tiles[first + (j - shared_before(i))] = t;
   }
-  if (tid == 0) {
-    ntiles[0] = R + (int32_t)ns;
-    int64_t fr = shared_rows / BM * BM;
-    for (int w = 0; w < 16; ++w) fr += wfull[w];
-    ntiles[1] = 2 * fr >= routed_rows + shared_rows ? 8 : 4;
-  }
+  if (tid == 0) *ntiles = R + (int32_t)ns;
 }
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,

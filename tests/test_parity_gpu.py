@@ -472,11 +472,11 @@ def test_wide_kernel_main_loop_every_token():
     assert c.max() > 256          # some experts span two row tiles
 
 
-def test_wide_kernel_eight_waves_every_token():
-    """512 rows per group and more take the eight-wave 256-row kernel: 2048 tokens, top-2 of
-    8 experts plus the shared one (683 rows per group, experts of two to three row tiles),
-    with h in two bf16 parts (top_k <= 2) so the down GEMM reads K = 2I.  Every token is
-    compared, and 32 tokens' intermediates."""
+def test_wide_kernel_full_tiles_two_part_h_every_token():
+    """Full 256-row tiles with h in two bf16 parts: 2048 tokens, top-2 of 8 experts plus the
+    shared one (683 rows per group, experts of two to three row tiles); top_k <= 2 keeps h
+    in two parts, so the down GEMM reads K = 2I.  Every token is compared, and 32 tokens'
+    intermediates."""
     cfg = dict(tokens=2048, d_model=512, n_experts=8, top_k=2, d_expert=256, d_shared=256,
                routed_scale=2.827, bias="uniform")
     inp = to_dev(S.make_inputs(cfg, "cpu", seed=31))
@@ -486,11 +486,10 @@ def test_wide_kernel_eight_waves_every_token():
     assert c.sum() + cfg["tokens"] >= 512 * (cfg["n_experts"] + 1)
 
 
-def test_wide_kernel_waves_chosen_on_device_every_token():
-    """Groups averaging under 512 rows leave the gate/up wave count to the device.  A bias of
-    +1 on four of 64 experts sends both slots of every token to them (about 1,024 rows each,
-    whole 256-row tiles), so the tile builder picks eight waves while the host sees 95 rows
-    per group; h is in two bf16 parts (top-2).  Every token is compared, and 32 tokens'
+def test_wide_kernel_concentrated_routing_every_token():
+    """A bias of +1 on four of 64 experts sends both slots of every token to them (about
+    1,024 rows each, whole 256-row tiles) and leaves 60 experts empty, as a skewed routing
+    does; h is in two bf16 parts (top-2).  Every token is compared, and 32 tokens'
     intermediates."""
     cfg = dict(tokens=2048, d_model=512, n_experts=64, top_k=2, d_expert=256, d_shared=256,
                routed_scale=2.827, bias="uniform")
