@@ -85,7 +85,7 @@ def lib():
         "moe_permute": [D, _P, _P, _P, _P, _P, _P, _S, _P],
         "moe_expert_gate_up": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
         "moe_expert_down": [D, _P, _P, _P, _P, _P, _P, _P, _S, _P],
-        "moe_expert_ffn": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+        "moe_expert_ffn": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
         "moe_combine": [D, _P, _P, _P, _P, _P, _P],
         "moe_forward": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
         "moe_forward_noalloc": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],

@@ -29,6 +29,41 @@ def test_library_exports_every_declared_symbol():
     assert sorted(B.EXPORTS) == names
 
 
+def _header_params():
+    """Parameter types of every moe_status function in include/moe.h, in order."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"moe_status\s+(moe_\w+)\s*\(([^)]*)\)\s*;", src):
+        out[name] = [re.sub(r"\w+$", "", p.strip()).strip() for p in params.split(",")]
+    return out
+
+
+def _ctype_of(c):
+    """The ctypes class the binding should declare for one C parameter type."""
+    c = c.replace("const ", "").replace(" ", "")
+    if c.startswith("moe_dims*"):
+        return ctypes.POINTER(B.MoeDims)
+    if c.startswith("moe_fp8_weights*"):
+        return ctypes.POINTER(B.MoeFp8Weights)
+    if c.startswith("size_t*"):
+        return ctypes.POINTER(ctypes.c_size_t)
+    if c.endswith("*"):
+        return ctypes.c_void_p
+    return {"size_t": ctypes.c_size_t, "float": ctypes.c_float, "int32_t": ctypes.c_int32}[c]
+
+
+def test_binding_argtypes_follow_header():
+    """Each entry point's argtypes match the header's parameter list one for one, so a
+    missing or misplaced argument fails here rather than as a ctypes error on the GPU."""
+    L = M.lib()
+    decl = _header_params()
+    assert len(decl) == len(B.EXPORTS) - 1          # every export but moe_status_str
+    for name, params in decl.items():
+        want = [_ctype_of(c) for c in params]
+        got = list(getattr(L, name).argtypes)
+        assert got == want, (name, params)
+
+
 def test_status_strings():
     for code in range(6):
         assert M.status_str(code).startswith("MOE_")

@@ -504,6 +504,25 @@ def test_wide_kernel_concentrated_routing_every_token():
     assert 2 * full >= int(c.sum()) + cfg["tokens"]
 
 
+@pytest.mark.parametrize("T", [64, 600])
+def test_expert_ffn_equals_gate_up_then_down(T):
+    """moe_expert_ffn (h kept in the workspace) gives bit-identical expert outputs to
+    moe_expert_gate_up followed by moe_expert_down, on both GEMM kernels (64 tokens: 11 rows
+    per group; 600: 106) and with h in two bf16 parts (top-2)."""
+    cfg = S.with_overrides("tiny", tokens=T)
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=40 + T))
+    g = run_split(cfg, inp)
+    dims = g["dims"]
+    ws = M.workspace(dims)
+    y_r = torch.full_like(g["y_r"], float("nan"))
+    y_s = torch.full_like(g["y_s"], float("nan"))
+    M.moe_expert_ffn(dims, inp["x"], g["perm"], g["offsets"], inp["w1"], inp["w3"], inp["w2"],
+                     inp["ws1"], inp["ws3"], inp["ws2"], y_r, y_s, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_r.view(torch.int32), g["y_r"].view(torch.int32))
+    assert torch.equal(y_s.view(torch.int32), g["y_s"].view(torch.int32))
+
+
 def test_tie_break_lower_index():
     cfg = S.with_overrides("tiny", top_k=1)
     inp = S.make_inputs(cfg, "cpu", seed=11)
