@@ -13,8 +13,8 @@
  *   out = y_routed + y_shared
  *
  * and the routing notes of "nnterp encyclopedia · kimi_k2" ("The mixture of experts":
- * every expert a candidate, gates are the chosen sigmoids without the bias, renormalised
- * and scaled so they sum to alpha at every token).
+ * all experts eligible, each gate the selected expert's sigmoid score with the bias left
+ * out, renormalised and scaled so the gates of a token sum to alpha).
  *
  * Conventions for every entry point
  *   - All array pointers are DEVICE pointers; `dims` is a host pointer.  bf16 arrays are

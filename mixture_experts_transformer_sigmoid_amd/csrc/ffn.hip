@@ -158,9 +158,9 @@ constexpr int kLdsNO = kLdsWaves == 4 ? 4 : 2;  // 32-output fragments per wave
 
 struct LdsCtx {
   __amdgpu_buffer_rsrc_t act;  // activation rows (x, or the tile's rows of h)
-  __amdgpu_buffer_rsrc_t wgt;  // this wave's weight matrix (gate/up: W1 for waves 0-1,
-                               // W3 for waves 2-3)
-  uint32_t aoff[8];            // per-lane byte offset of the wave's activation units
+  __amdgpu_buffer_rsrc_t wgt;  // this wave's weight matrix (gate/up: W1 for the first
+                               // half of the waves, W3 for the second)
+  uint32_t aoff[kLdsUnits];    // per-lane byte offset of the wave's activation units
   uint32_t woff[2];            // per-lane byte offset of the wave's even / odd weight
                                // units, less the unit stride
   uint32_t wstride;            // bytes between the wave's consecutive weight units (8 rows)
@@ -438,11 +438,11 @@ __global__ __launch_bounds__(64 * kLdsWaves, 1) void ffn_lds_kernel(const FfnArg
 
 int64_t ffn_max_tiles(const FfnShape& sh) { return max_tiles_for(sh, kSkinnyBM); }
 
-// bf16 weights: the 256-row kernel from 5 rows per group on.  The whole K2-shape layer
-// (d 7168, 384 experts, top-8, I 2048) over T = 64..640, each kernel forced (one box, two
-// passes, ms): T 64 4.16 skinny / 4.31 256-row, 128 5.25 / 5.25, 192 5.55 / 5.55,
-// 224 5.64 / 5.58, 256 5.67 / 5.61, 448 6.14 / 5.83, 640 7.37 / 6.01.  Switching at 16 rows
-// per group, as before, left T = 200..680 up to 18% slow.
+// bf16 weights: the 256-row kernel from 5 rows per group on (and from d = 512 on).  The
+// whole K2-shape layer (d 7168, 384 experts, top-8, I 2048) over T = 64..640, each kernel
+// forced (one box, two passes, ms): T 64 4.16 skinny / 4.31 256-row, 128 5.25 / 5.25,
+// 192 5.55 / 5.55, 224 5.64 / 5.58, 256 5.67 / 5.61, 448 6.14 / 5.83, 640 7.37 / 6.01.
+// Switching at 16 rows per group left T = 200..680 up to 18% slow.
 constexpr int kWideRowsBf16 = 5;
 
 TileSpec ffn_tile_spec(const FfnShape& sh) {

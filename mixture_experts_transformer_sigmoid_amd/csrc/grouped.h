@@ -262,14 +262,29 @@ int64_t max_tiles_for(const FfnShape& sh, int BM) {
 // kernel's tiles each read the one weight matrix, mostly from L2.
 constexpr int64_t kSingleGroupWideRows = 512;
 
+// The 256-row kernels also need the gate/up GEMM's reduction (the model width d) to be at
+// least this long.  Their fixed cost per tile (the first two chunks' loads, the staged
+// epilogue) is spread over d / 64 chunks; at d = 256 (four chunks) the skinny kernels are
+// faster at every batch measured.  Whole layer, 16 experts, top-2, I = 128, back to back,
+// skinny against 256-row (two passes on one box, us): bf16 T = 64 26.2-26.7 / 31.5-32.0,
+// T = 256 27.0-27.9 / 42.5-42.6, T = 1024 51.4-52.5 / 61.7-62.6; FP8 29.0-29.2 / 30.0-30.4,
+// 29.3-29.6 / 33.9-34.7, 48.1 / 52.2-52.7.  From d = 512 on the 256-row kernels win at every
+// shape measured, also with 48 workgroups per launch: bf16 d = 512, 8 experts, top-2,
+// T = 2048 77.6-78.0 against 119.5-119.7 us skinny; d = 1024, 16 experts, top-4,
+// T = 1024 91.5-92.7 against 221.6-222.3; d = 4096, 128 experts, top-8, T = 2048 913.6-926.7
+// against 4838-4858; FP8 65.6-66.2 against 79.6-79.8, 79.3-79.4 against 140.6-140.9 and
+// 824.3-826.2 against 2314.
+constexpr int kWideMinK = 512;
+
 // Average rows per group (routed experts plus the shared expert) decides the kernel: up to
-// rows_per_group (decode) -> skinny kernel; more -> the 256-row kernel (bf16 or FP8).  Each weight type passes its own crossover, measured with the routed experts
-// present; a launch of one group uses kSingleGroupWideRows instead.
+// rows_per_group (decode) -> skinny kernel; more -> the 256-row kernel (bf16 or FP8), if d
+// is at least kWideMinK.  Each weight type passes its own crossover, measured with the
+// routed experts present; a launch of one group uses kSingleGroupWideRows instead.
 bool use_wide(const FfnShape& sh, int rows_per_group) {
   const int64_t rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
   const int64_t groups = sh.E + (sh.shared ? 1 : 0);
   if (groups <= 1) return rows > kSingleGroupWideRows;
-  return rows > (int64_t)rows_per_group * groups;
+  return sh.d >= kWideMinK && rows > (int64_t)rows_per_group * groups;
 }
 
 TileSpec tile_spec_for(const FfnShape& sh, int BM) {

@@ -1,7 +1,7 @@
 // Per-token top-k and gates, one wave per token: "Kimi K2 · Transformer blocks", MoE
 // equations E_sel (the k largest biased scores s + b) and G_i (alpha * s_i over the sum of
 // the chosen s, the bias left out); "nnterp encyclopedia · kimi_k2", "The mixture of
-// experts" (every expert a candidate, the gates the chosen sigmoids without the bias).
+// experts" (all experts eligible; the gates from the selected sigmoid scores, bias excluded).
 // Used by the selection kernels of route.hip.  Every definition lives in an unnamed
 // namespace: each source file that includes this gets its own copy.
 #pragma once
@@ -16,8 +16,9 @@ namespace {
 // Lane l holds experts l, l + 64, ..., l + 64 (EPL - 1).  Scores of experts >= E, and NaN
 // scores, must already be -inf.  k rounds of a wave-wide argmax over (score, -index) pick
 // the experts in descending score, ties to the lower index; the gates are alpha * s / den
-// with den the fp32 sum of the chosen sigmoids in pick order (0 if den is 0).  Lane j < k
-// writes pick j to idx[j] / w[j] (global, or null) and idx_lds[j] (LDS, or null).
+// with den the fp32 sum of the picked experts' sigmoid scores in pick order (0 if den is
+// 0).  Lane j < k writes pick j to idx[j] / w[j] (global, or null) and idx_lds[j] (LDS, or
+// null).
 template <int EPL>
 __device__ __forceinline__ void select_topk(const float (&score)[EPL], const float (&sig)[EPL],
                                             int E, int k, float alpha, int lane, int32_t* idx,

@@ -15,9 +15,9 @@ Sources (the pages this follows; cited by page title and the part of the page):
       y_routed = sum_{i=1..384} G_i E_i ; y_shared = same SwiGLU with the shared
       expert's weights ; Delta_ffn = y_routed + y_shared,
   and the table "Exact per-instance accounting" (MoE parameters 16,958,226,816).
-* "nnterp encyclopedia · kimi_k2", section "The mixture of experts" (selection on
-  sigmoid plus a selection bias, every expert a candidate, gates are the chosen
-  sigmoids without the bias, renormalised and multiplied by 2.827) and section
+* "nnterp encyclopedia · kimi_k2", section "The mixture of experts" (experts selected on
+  sigmoid + bias, all 384 eligible, each gate the selected expert's sigmoid score with
+  the bias left out, renormalised and multiplied by 2.827) and section
   "Config" (384 experts, 8 per token, moe_intermediate_size 2048, one shared expert,
   routed_scaling_factor 2.827, norm_topk_prob true, n_group = topk_group = 1).
 * "Kimi K3 · Latent up-projection", the printed moe_infer: count tokens per expert,

@@ -153,9 +153,10 @@ def test_fp8_tiny_skinny():
 
 @pytest.mark.parametrize("T", [1, 37, 300])
 def test_fp8_ragged(T):
-    # T = 300 puts 1200 rows on 25 groups (48 per group): the 256-row kernel, with K = 384
-    # (six 64-k chunks: one pass of its six-chunk loop) and K = 256 (four chunks: the tail)
-    cfg = S.with_overrides("tiny", tokens=T, d_model=384, n_experts=24, top_k=3, d_expert=256,
+    # T = 300 puts 1200 rows on 25 groups (48 per group): the 256-row kernel, with K = 512
+    # (eight 64-k chunks: one pass of its six-chunk loop and a tail of two) and K = 256 (four
+    # chunks: the tail alone)
+    cfg = S.with_overrides("tiny", tokens=T, d_model=512, n_experts=24, top_k=3, d_expert=256,
                            d_shared=256)
     full_check(cfg, fp8_inputs(cfg, seed=T))
 
@@ -164,8 +165,9 @@ def test_fp8_wide_kernel_no_shared():
     # top-8 of 16 as at K2: without the shared expert the output RMS is small and with
     # two or three large gates the bf16 rounding of h and of the output sit at the edge of
     # the 2e-2 * RMS bar (1.01 of it at k = 3, with h and Y exact); eight gates of ~0.35
-    # average that rounding down, as they do at the K2 shape
-    cfg = S.with_overrides("tiny", tokens=600, n_experts=16, top_k=8, d_shared=0)
+    # average that rounding down, as they do at the K2 shape (d = 512: the 256-row kernel
+    # needs a reduction of at least 512)
+    cfg = S.with_overrides("tiny", tokens=600, d_model=512, n_experts=16, top_k=8, d_shared=0)
     full_check(cfg, fp8_inputs(cfg, seed=3))
 
 
@@ -192,9 +194,9 @@ def test_fp8_zero_and_extreme_scales():
 
 def test_fp8_zero_and_extreme_scales_wide():
     # the same scale edits on the 256-row kernel (600 tokens, top-8 of 16: ~300 rows per
-    # expert, one full row tile and one partial one): its per-128-k-block partial sums must
-    # keep the zero block and the extreme scales exact too
-    cfg = S.with_overrides("tiny", tokens=600, n_experts=16, top_k=8)
+    # expert, one full row tile and one partial one; d = 512, four 128-k blocks): its
+    # per-128-k-block partial sums must keep the zero block and the extreme scales exact too
+    cfg = S.with_overrides("tiny", tokens=600, d_model=512, n_experts=16, top_k=8)
     inp = fp8_inputs(cfg, seed=5)
     inp["w1_scale"][0, 0, 1] = 0.0
     inp["w3_scale"][1] *= 2.0 ** -20
@@ -224,15 +226,28 @@ def test_fp8_wide_kernel_main_loop_every_token():
 
 @pytest.mark.parametrize("T", [33, 2048])
 def test_fp8_max_experts_1024(T):
-    # the largest E (16 experts per lane in the selection), top-8: 33 tokens take the skinny
-    # kernel, 2048 (18 rows per group) the 256-row one, its tiles of 1 to ~40 rows; every
-    # token compared.  Not 4096: over its 524k outputs the largest, 5.6 RMS, lies where the
-    # bf16 output step alone (half an ulp, 0.0156) is 91% of the bar, and the kernels'
-    # schedule replayed on the host (h and the output in bf16) reaches 1.08 of the bar there,
-    # the GPU matching that replay; at 2048 tokens the replay stays at 0.82.
+    # the largest E (16 experts per lane in the selection), top-8, at d = 128 (the skinny
+    # kernels), every token compared.  Larger batches put a larger output in play where the
+    # bf16 output step alone (half an ulp, 0.0156 from 4 up) is most of the bar: the
+    # kernels' schedule replayed on the host (h and the output in bf16), which the GPU
+    # matches, reaches 1.08 of the bar at 4096 tokens; at 2048 it stays at 0.82.  The
+    # 256-row kernel would need more than 16 rows per group at d >= 512, i.e. at least
+    # 1,823 tokens: the same replay then reaches 0.95-1.27 of the bar (2048 tokens, seeds
+    # 0-2), so no every-token case there can hold it.  The tile list of 1,025 groups on the
+    # 256-row kernels is covered by the bf16 case at d = 512, the FP8 256-row kernel on
+    # tiles of a few rows by test_fp8_wide_kernel_small_tiles.
     cfg = S.with_overrides("tiny", tokens=T, d_model=128, n_experts=1024, top_k=8,
                            d_expert=256, d_shared=256)
     full_check(cfg, fp8_inputs(cfg, seed=7 + T), inter_tokens=4)
+
+
+def test_fp8_wide_kernel_small_tiles():
+    # 128 experts, top-8, 300 tokens at d = 512: 21 rows per group, just past the FP8
+    # switch to the 256-row kernel, so most row tiles hold a few to a few dozen rows of
+    # 256.  Every token compared (schedule replay: 0.82 of the bar).
+    cfg = S.with_overrides("tiny", tokens=300, d_model=512, n_experts=128, top_k=8,
+                           d_expert=256, d_shared=256)
+    full_check(cfg, fp8_inputs(cfg, seed=8), inter_tokens=4)
 
 
 @pytest.fixture(scope="module")

@@ -363,7 +363,8 @@ def test_ragged_shapes(T):
 @pytest.mark.parametrize("T,concentrated", [(37, False), (150, False), (150, True)])
 def test_skinny_kernel_ragged(T, concentrated):
     """The skinny (16-row tile) GEMMs on ragged shapes.  A bf16 layer takes them up to 5
-    rows per group on average: here at most 150 * 3 / 97 = 4.6.  N = 192 and 320 are not
+    rows per group on average (here at most 150 * 3 / 97 = 4.6), and at any batch when d is
+    below 512 (as for the other small configs here).  N = 192 and 320 are not
     multiples of the 64- and 128-feature blocks.  Concentrated: every token on experts 0
     and 1, which then span ten 16-row tiles each, the last one partly filled."""
     cfg = dict(tokens=T, d_model=320, n_experts=96, top_k=2, d_expert=192, d_shared=192,
@@ -504,12 +505,28 @@ def test_wide_kernel_concentrated_routing_every_token():
     assert 2 * full >= int(c.sum()) + cfg["tokens"]
 
 
-@pytest.mark.parametrize("T", [64, 600])
+@pytest.mark.parametrize("k,Is,seed", [(3, 448, 62), (2, 448, 61), (8, 0, 62)])
+def test_wide_kernel_ragged_n_every_token(k, Is, seed):
+    """The 256-row kernels with output widths that are not whole feature blocks: d = 576
+    (down: two blocks of 256 and one of 64 features) and I = 448 (gate/up: three blocks of
+    128 and one of 64), 300 tokens over 24 experts (36 to 100 rows per group).  K = 576 is
+    nine chunks of 64 (one pass of the six-chunk loop, a tail of three) and K = 448 seven
+    (K = 896 with h in two parts at top-2).  Top-8 without the shared expert as well.
+    Every token is compared, and 32 tokens' intermediates.  The kernels' schedule replayed
+    on the host reaches 0.75, 0.58 and 0.75 of the output bar on these inputs."""
+    cfg = dict(tokens=300, d_model=576, n_experts=24, top_k=k, d_expert=448, d_shared=Is,
+               routed_scale=2.827, bias="uniform")
+    inp = to_dev(S.make_inputs(cfg, "cpu", seed=seed, shared=Is > 0))
+    full_check(cfg, inp, intermediates=32)
+
+
+@pytest.mark.parametrize("T", [16, 600])
 def test_expert_ffn_equals_gate_up_then_down(T):
     """moe_expert_ffn (h kept in the workspace) gives bit-identical expert outputs to
-    moe_expert_gate_up followed by moe_expert_down, on both GEMM kernels (64 tokens: 11 rows
-    per group; 600: 106) and with h in two bf16 parts (top-2)."""
-    cfg = S.with_overrides("tiny", tokens=T)
+    moe_expert_gate_up followed by moe_expert_down, on both GEMM kernels (d = 512; 16 tokens:
+    3 rows per group, the skinny kernels; 600: 106, the 256-row ones) and with h in two
+    bf16 parts (top-2)."""
+    cfg = S.with_overrides("tiny", tokens=T, d_model=512)
     inp = to_dev(S.make_inputs(cfg, "cpu", seed=40 + T))
     g = run_split(cfg, inp)
     dims = g["dims"]
