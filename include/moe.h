@@ -28,6 +28,8 @@
  *   - The caller owns all memory.  The library allocates nothing, keeps no state between
  *     calls and never synchronises the host; all work is queued on `stream` (a
  *     hipStream_t; NULL = the default stream).  Concurrent calls need their own workspace.
+ *     (The one exception, moe_forward_noalloc, works in a device array the library holds
+ *     instead of a workspace.)
  *   - Every output is fully overwritten.  tokens == 0 is a valid no-op.
  *   - Errors are status codes, checked on the host BEFORE anything is launched:
  *       MOE_EINVAL       null / misaligned (16 B) pointer, impossible dims

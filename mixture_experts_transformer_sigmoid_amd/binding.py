@@ -128,7 +128,16 @@ def dims_for(cfg: dict, tokens=None) -> MoeDims:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """A tensor's device address.  Host tensors and strided views are refused: the library
+    cannot tell a host address from a device one (a kernel reading it faults), and it reads
+    every array densely in the layout moe.h gives."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"libmoe takes device tensors; got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors; got a strided view")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):

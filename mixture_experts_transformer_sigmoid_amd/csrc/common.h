@@ -191,25 +191,12 @@ hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias,
 hipError_t launch_router_select(const float* score, const float* sig, int64_t T, int E, int k,
                                 float alpha, int32_t* idx, float* w, hipStream_t s);
 
-// The selection handed to the permutation: launch_router_scores' output, the routing
-// constants, and where the chosen experts and gates go.
-struct SelectIn {
-  const float* score;
-  const float* sig;
-  float alpha;
-  int32_t* idx;
-  float* w;
-};
-
 // ts (or null): also build the tile list of a grouped launch for the new offsets into
 // tiles / ntiles, so that the launch can skip building it.
-// sel (or null): the top-k is first taken from sel's scores by the selection launch
-// (topk_idx is then ignored and sel->idx, sel->w are written).
 hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* hist,
                           int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm,
                           int32_t* inv, hipStream_t s, const TileSpec* ts = nullptr,
-                          Tile* tiles = nullptr, int32_t* ntiles = nullptr,
-                          const SelectIn* sel = nullptr);
+                          Tile* tiles = nullptr, int32_t* ntiles = nullptr);
 int64_t permute_blocks(int64_t T);
 
 struct FfnShape {

@@ -492,11 +492,10 @@ FfnArgs fp8_args(const FfnShape& sh, const Fp8Weights& w, bool gateup, Tile* til
 }  // namespace
 
 // FP8 weights: the 256-row kernel above 16 rows per group (and from d = 512 on, as with
-// bf16 weights).  It converts every weight it
-// reads and applies a scale per 128-k block, so the skinny kernel stays ahead longer than
-// with bf16 weights: K2-shape layer, ms, skinny / 256-row: T 128 2.78 / 4.06, 256 3.05 /
-// 4.32, 448 3.32 / 4.44, 640 3.71 / 4.53, 1024 5.20 / 4.59, 2048 8.65 / 4.95 (at T = 640
-// there are 15 rows per group, at 1024 24).
+// bf16 weights).  It converts every weight it reads and applies a scale per 128-k block, so
+// the skinny kernel stays ahead longer than with bf16 weights: K2-shape layer, ms, skinny /
+// 256-row: T 128 2.78 / 4.06, 256 3.05 / 4.32, 448 3.32 / 4.44, 640 3.71 / 4.53, 1024 5.20 /
+// 4.59, 2048 8.65 / 4.95 (at T = 640 there are 15 rows per group, at 1024 24).
 #ifndef MOE_F8_WIDE_ROWS
 #define MOE_F8_WIDE_ROWS 16
 #endif

@@ -250,11 +250,11 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
 
 // Routing and permutation of a layer entry point, into the workspace arrays at the given
 // offsets (and the tile list of ts when ts is non-null).  Up to kRouterSmallT tokens: the
-// router kernel writes scores and sigmoids and the permutation takes the top-k itself (in
-// its prologue up to 256 tokens, else as a launch of its own).  With norm non-null, x is
-// the residual stream x' and the experts' input x_ffn = RMSNorm(x') goes to norm->x_ffn:
-// written by the router kernel up to kRouterSmallT tokens, else by the norm kernel before
-// the router.  The experts' input (x, or norm->x_ffn) is returned through x_in.
+// router kernel writes scores and sigmoids, then the selection launch takes the top-k and
+// the gates from them.  With norm non-null, x is the residual stream x' and the experts'
+// input x_ffn = RMSNorm(x') goes to norm->x_ffn: written by the router kernel up to
+// kRouterSmallT tokens, else by the norm kernel before the router.  The experts' input (x,
+// or norm->x_ffn) is returned through x_in.
 struct RouteBufs {
   size_t zpart, wsplit, idx, w, counts, offsets, perm, inv, hist, base, tiles, ntiles;
 };
@@ -286,9 +286,10 @@ moe_status route_permute(const moe_dims& d, const uint16_t* x, const moe::Router
     MOE_TRY(hip_status(moe::launch_router_scores(x, norm, w_router, bias, T, d.d_model, E, score,
                                                  sig, nullptr, s)));
     *x_in = norm != nullptr ? norm->x_ffn : x;
-    const moe::SelectIn sel{score, sig, d.routed_scale, idx, w};
-    return hip_status(moe::launch_permute(nullptr, T, E, d.top_k, hist, base, counts, offsets,
-                                          perm, inv, s, ts, tiles, ntiles, &sel));
+    MOE_TRY(hip_status(
+        moe::launch_router_select(score, sig, T, E, d.top_k, d.routed_scale, idx, w, s)));
+    return hip_status(moe::launch_permute(idx, T, E, d.top_k, hist, base, counts, offsets, perm,
+                                          inv, s, ts, tiles, ntiles));
   }
   if (norm != nullptr) {
     MOE_TRY(hip_status(

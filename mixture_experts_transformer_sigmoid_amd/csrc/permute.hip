@@ -241,14 +241,7 @@ int64_t permute_blocks(int64_t T) { return (T + kTokPerBlock - 1) / kTokPerBlock
 hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int E, int k, int32_t* hist,
                           int32_t* base, int32_t* counts, int32_t* offsets, int32_t* perm,
                           int32_t* inv, hipStream_t s, const TileSpec* ts, Tile* tiles,
-                          int32_t* ntiles, const SelectIn* sel) {
-  if (sel != nullptr) {
-    // the routing's top-k, one wave per token, from the router's scores
-    hipError_t err = launch_router_select(sel->score, sel->sig, T, E, k, sel->alpha, sel->idx,
-                                          sel->w, s);
-    if (err != hipSuccess) return err;
-    topk_idx = sel->idx;
-  }
+                          int32_t* ntiles) {
   if (T <= kTokPerBlock) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s, topk_idx, T, E, k, counts,
                        offsets, perm, inv, ts != nullptr ? *ts : TileSpec{},

@@ -162,6 +162,16 @@ def test_binding_raises_on_error():
     assert ei.value.status == M.MOE_EUNSUPPORTED
 
 
+def test_binding_refuses_host_tensors():
+    """A host tensor never reaches the library (a kernel would fault on its address)."""
+    import torch
+    d = M.moe_dims(4, 64, 4, 2, 64, 64)
+    y = torch.zeros(8, 64)
+    with pytest.raises(ValueError, match="device tensors"):
+        M.moe_combine(d, y, torch.zeros(8, dtype=torch.int32), torch.zeros(8), None,
+                      torch.zeros(4, 64, dtype=torch.bfloat16))
+
+
 def test_latent_dims_checked():
     n = ctypes.c_size_t(0)
     L = M.lib()
