@@ -4,8 +4,8 @@
 // "Kimi K3 · Latent up-projection".  fp32 accumulation in slot order, one bf16 rounding.
 //
 // Each thread owns 8 consecutive features of one token (32-byte fp32 loads, one 16-byte
-// bf16 store), a block 1,024 features;
-// a token's k expert rows are gathered through inv_perm.
+// bf16 store), a block 1,024 features; a token's k expert rows are gathered through
+// inv_perm.
 #include "common.h"
 
 namespace moe {
