@@ -128,12 +128,12 @@ struct TileSpec {
 };
 
 // Router.  Up to kRouterSmallT tokens, one kernel computes each (16 tokens x 16 experts)
-// tile of z over the whole K with the sigmoid and the bias in its epilogue, and writes the
-// biased scores and the sigmoids, [T, E] fp32 each (router_zpart_floats holds both); the
-// top-k and the gates are then taken per token by one wave of the selection launch.
-// Above it, the bf16 (hi, mid, lo) copy
-// of W_r (w_split, [3 router_part_rows(E), d]) feeds the 256-row GEMM kernel, whose
-// partial logits (z_part) the selection kernel adds in fp64.  logits may be null.
+// tile of z over the whole K with the sigmoid and the bias in its epilogue.  With at most
+// 16 experts it also takes each token's top-k and gates; otherwise it writes the biased
+// scores and the sigmoids, [T, E] fp32 each (router_zpart_floats holds both), and one wave
+// per token of the selection launch takes them.  Above kRouterSmallT, the bf16 (hi, mid,
+// lo) copy of W_r (w_split, [3 router_part_rows(E), d]) feeds the 256-row GEMM kernel,
+// whose partial logits (z_part) the selection kernel adds in fp64.  logits may be null.
 constexpr int64_t kRouterSmallT = 512;
 // Rows per part (hi, mid, lo) of the split router weights and of the partial logits the
 // 256-row kernel writes: E rounded up to a multiple of 4 (the padding rows are zero).
@@ -173,23 +173,23 @@ struct RouterNorm {
   uint16_t* x_ffn;
 };
 
-// Up to kRouterSmallT tokens: the scores (score = fl32(sigmoid(z) + b), NaN -> -inf) and
-// sigmoids [T, E] fp32; with norm non-null, x is the residual stream and the router reads
-// its normalised rows (and writes them to norm->x_ffn).
-hipError_t launch_router_scores(const uint16_t* x, const RouterNorm* norm, const float* w_r,
-                                const float* bias, int64_t T, int d, int E, float* score,
-                                float* sig, float* logits, hipStream_t s);
+// The routing up to kRouterSmallT tokens: the scores (score = fl32(sigmoid(z) + b), NaN ->
+// -inf; score and sig, [T, E] fp32 each, hold them between the launches when there are
+// two), then the top-k into idx and the gates into w: one launch up to 16 experts, two
+// above.  With norm non-null, x is the residual stream and the router reads its normalised
+// rows (and writes them to norm->x_ffn).
+hipError_t launch_router_small(const uint16_t* x, const RouterNorm* norm, const float* w_r,
+                               const float* bias, int64_t T, int d, int E, int k, float alpha,
+                               float* score, float* sig, float* logits, int32_t* idx, float* w,
+                               hipStream_t s);
 
-// The whole routing: scores and selection (two launches up to kRouterSmallT tokens), or the
-// split, GEMM and selection launches above.
+// The whole routing: launch_router_small up to kRouterSmallT tokens, else the split, GEMM
+// and selection launches.
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
                          int E, int k, float alpha, uint16_t* w_split, float* z_part,
                          Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,
                          float* topk_w, hipStream_t s);
 
-// The per-token top-k of launch_router_scores' output, written to idx / w.
-hipError_t launch_router_select(const float* score, const float* sig, int64_t T, int E, int k,
-                                float alpha, int32_t* idx, float* w, hipStream_t s);
 
 // ts (or null): also build the tile list of a grouped launch for the new offsets into
 // tiles / ntiles, so that the launch can skip building it.

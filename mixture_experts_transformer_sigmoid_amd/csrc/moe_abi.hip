@@ -250,8 +250,8 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
 
 // Routing and permutation of a layer entry point, into the workspace arrays at the given
 // offsets (and the tile list of ts when ts is non-null).  Up to kRouterSmallT tokens: the
-// router kernel writes scores and sigmoids, then the selection launch takes the top-k and
-// the gates from them.  With norm non-null, x is the residual stream x' and the experts'
+// router kernel computes the scores, and takes the top-k and the gates itself up to 16
+// experts (else a selection launch does).  With norm non-null, x is the residual stream x' and the experts'
 // input x_ffn = RMSNorm(x') goes to norm->x_ffn: written by the router kernel up to
 // kRouterSmallT tokens, else by the norm kernel before the router.  The experts' input (x,
 // or norm->x_ffn) is returned through x_in.
@@ -282,12 +282,10 @@ moe_status route_permute(const moe_dims& d, const uint16_t* x, const moe::Router
   int32_t* inv = at<int32_t>(ws, B.inv);
   if (T <= moe::kRouterSmallT) {
     float* score = at<float>(ws, B.zpart);
-    float* sig = score + T * E;
-    MOE_TRY(hip_status(moe::launch_router_scores(x, norm, w_router, bias, T, d.d_model, E, score,
-                                                 sig, nullptr, s)));
+    MOE_TRY(hip_status(moe::launch_router_small(x, norm, w_router, bias, T, d.d_model, E, d.top_k,
+                                                d.routed_scale, score, score + T * E, nullptr,
+                                                idx, w, s)));
     *x_in = norm != nullptr ? norm->x_ffn : x;
-    MOE_TRY(hip_status(
-        moe::launch_router_select(score, sig, T, E, d.top_k, d.routed_scale, idx, w, s)));
     return hip_status(moe::launch_permute(idx, T, E, d.top_k, hist, base, counts, offsets, perm,
                                           inv, s, ts, tiles, ntiles));
   }

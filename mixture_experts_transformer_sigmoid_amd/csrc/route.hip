@@ -9,7 +9,9 @@
 // product is exact in fp32.  Above kRouterSmallT tokens the three partial logits are
 // accumulated in fp32 by the grouped-GEMM kernels (one group, 3E outputs) and added in
 // fp64 by the selection kernel.  For fewer tokens (decode) router_scores_kernel does the
-// split in registers, owns whole logits, and applies the sigmoid and the bias itself.
+// split in registers, owns whole logits, and applies the sigmoid and the bias itself; with
+// at most 16 experts one of its workgroups holds every logit of its tokens and takes their
+// top-k and gates as well.
 // (The split follows the bf16x3 scheme of Henry, Tang and Heinecke, "Leveraging the
 // bfloat16 artificial intelligence datatype for higher-precision computations", 2019.)
 #include <math.h>
@@ -112,14 +114,19 @@ __device__ __forceinline__ u32x4_t norm8(const u32x4_t& v, double rinv, const u3
   return o;
 }
 
-template <bool NORM>
+// SELECT (E <= 16, one expert tile): the workgroup's scores stay in LDS, and one wave per
+// token takes the top-k and the gates from them with the selection kernel's select_topk, so
+// the routing is the same bit for bit; score and sig are then not written.
+template <bool NORM, bool SELECT>
 __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
     uint16_t* __restrict__ x_ffn, const float* __restrict__ w_r, const float* __restrict__ bias,
     int64_t T, int d, int E, float* __restrict__ score, float* __restrict__ sig,
-    float* __restrict__ logits) {
+    float* __restrict__ logits, int k, float alpha, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
   __shared__ f32x4_t part[kRouterWaves][3][64];
   __shared__ double rinv_s[16];
+  __shared__ float sel_sc[SELECT ? 16 : 1][16], sel_sg[SELECT ? 16 : 1][16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * 16;
   const int e0 = blockIdx.y * 16;
@@ -203,24 +210,44 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
 #pragma unroll
   for (int p = 0; p < 3; ++p) part[wave][p][lane] = acc[p];
   __syncthreads();
-  if (tid >= 256) return;
-  const int i = tid >> 4, jj = tid & 15;   // token t0 + i, expert e0 + jj
-  const int src = (jj >> 2) * 16 + i, reg = jj & 3;
-  double zd = 0.0;
+  if (tid < 256) {
+    const int i = tid >> 4, jj = tid & 15;   // token t0 + i, expert e0 + jj
+    const int src = (jj >> 2) * 16 + i, reg = jj & 3;
+    double zd = 0.0;
 #pragma unroll
-  for (int w = 0; w < kRouterWaves; ++w)
+    for (int w = 0; w < kRouterWaves; ++w)
 #pragma unroll
-    for (int p = 0; p < 3; ++p) zd += (double)part[w][p][src][reg];
-  const int64_t tt = t0 + i;
-  const int ee = e0 + jj;
-  if (tt >= T || ee >= E) return;
-  const float z = (float)zd;
-  if (logits != nullptr) logits[tt * E + ee] = z;
-  const float s = 1.0f / (1.0f + expf(-z));
-  float v = s + bias[ee];
-  if (v != v) v = -INFINITY;
-  score[tt * E + ee] = v;
-  sig[tt * E + ee] = s;
+      for (int p = 0; p < 3; ++p) zd += (double)part[w][p][src][reg];
+    const int64_t tt = t0 + i;
+    const int ee = e0 + jj;
+    float v = -INFINITY, s = 0.0f;
+    if (tt < T && ee < E) {
+      const float z = (float)zd;
+      if (logits != nullptr) logits[tt * E + ee] = z;
+      s = 1.0f / (1.0f + expf(-z));
+      v = s + bias[ee];
+      if (v != v) v = -INFINITY;
+      if constexpr (!SELECT) {
+        score[tt * E + ee] = v;
+        sig[tt * E + ee] = s;
+      }
+    }
+    if constexpr (SELECT) {
+      sel_sc[i][jj] = v;
+      sel_sg[i][jj] = s;
+    }
+  }
+  if constexpr (SELECT) {
+    __syncthreads();
+    // lane l holds expert l (lanes from E on: -inf), as the selection kernel loads them
+    for (int i = wave; i < 16; i += kRouterWaves) {
+      const int64_t tt = t0 + i;
+      if (tt >= T) break;
+      float sc[1] = {lane < E ? sel_sc[i][lane] : -INFINITY};
+      float sg[1] = {lane < E ? sel_sg[i][lane] : 0.0f};
+      select_topk<1>(sc, sg, E, k, alpha, lane, topk_idx + tt * k, topk_w + tt * k, nullptr);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- top-k + gates
@@ -311,25 +338,12 @@ void select_launch(const float* z_part, int np, int row_parts, int pstride, cons
                        row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
 }
 
-}  // namespace
-
-hipError_t launch_router_scores(const uint16_t* x, const RouterNorm* norm, const float* w_r,
-                                const float* bias, int64_t T, int d, int E, float* score,
-                                float* sig, float* logits, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16));
-  if (norm != nullptr)
-    hipLaunchKernelGGL(router_scores_kernel<true>, grid, dim3(64 * kRouterWaves), 0, s, x, norm->gain,
-                       norm->eps, norm->x_ffn, w_r, bias, T, d, E, score, sig, logits);
-  else
-    hipLaunchKernelGGL(router_scores_kernel<false>, grid, dim3(64 * kRouterWaves), 0, s, x, nullptr, 0.0f,
-                       nullptr, w_r, bias, T, d, E, score, sig, logits);
-  return hipGetLastError();
-}
+// Up to this many experts one router_scores_kernel workgroup covers every expert of its
+// tokens and selects in place (SELECT); above, the selection is a launch of its own.
+constexpr int kRouterSelectMaxE = 16;
 
 hipError_t launch_router_select(const float* score, const float* sig, int64_t T, int E, int k,
                                 float alpha, int32_t* idx, float* w, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
   const dim3 grid((unsigned)((T + 3) / 4));
 #define MOE_SELECT_SCORES(N)                                                                  \
   hipLaunchKernelGGL(router_select_scores_kernel<N>, grid, dim3(256), 0, s, score, sig, T, E, \
@@ -346,6 +360,34 @@ hipError_t launch_router_select(const float* score, const float* sig, int64_t T,
   return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_router_small(const uint16_t* x, const RouterNorm* norm, const float* w_r,
+                               const float* bias, int64_t T, int d, int E, int k, float alpha,
+                               float* score, float* sig, float* logits, int32_t* idx, float* w,
+                               hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16));
+  const bool sel = E <= kRouterSelectMaxE;
+  const float* gain = norm != nullptr ? norm->gain : nullptr;
+  const float eps = norm != nullptr ? norm->eps : 0.0f;
+  uint16_t* x_ffn = norm != nullptr ? norm->x_ffn : nullptr;
+#define MOE_SCORES(NORM, SEL)                                                                  \
+  hipLaunchKernelGGL((router_scores_kernel<NORM, SEL>), grid, dim3(64 * kRouterWaves), 0, s, x, \
+                     gain, eps, x_ffn, w_r, bias, T, d, E, score, sig, logits, k, alpha, idx, w)
+  if (norm != nullptr) {
+    if (sel) MOE_SCORES(true, true);
+    else MOE_SCORES(true, false);
+  } else {
+    if (sel) MOE_SCORES(false, true);
+    else MOE_SCORES(false, false);
+  }
+#undef MOE_SCORES
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess || sel) return err;
+  return launch_router_select(score, sig, T, E, k, alpha, idx, w, s);
+}
+
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
                          int E, int k, float alpha, uint16_t* w_split, float* z_part,
                          Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,
@@ -354,11 +396,8 @@ hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias,
   hipError_t err;
   if (T <= kRouterSmallT) {
     // scores [T, E] and sigmoids [T, E] in z_part
-    float* score = z_part;
-    float* sig = z_part + T * E;
-    err = launch_router_scores(x, nullptr, w_r, bias, T, d, E, score, sig, logits, s);
-    if (err != hipSuccess) return err;
-    return launch_router_select(score, sig, T, E, k, alpha, topk_idx, topk_w, s);
+    return launch_router_small(x, nullptr, w_r, bias, T, d, E, k, alpha, z_part, z_part + T * E,
+                               logits, topk_idx, topk_w, s);
   }
   const int Ep = router_part_rows(E);
   const int64_t n = (int64_t)E * d, np_ = (int64_t)Ep * d;
