@@ -446,6 +446,18 @@ def test_expert_count_not_a_multiple_of_four(E, T, k):
     full_check(cfg, to_dev(S.make_inputs(cfg, "cpu", seed=20 + E)), intermediates=True)
 
 
+@pytest.mark.parametrize("E,T", [(16, 45), (17, 45), (16, 300), (17, 300)])
+def test_router_selection_in_place_boundary(E, T):
+    """Up to 16 experts the router kernel takes the top-k and the gates itself; 17 experts
+    need a second expert tile and the selection launch.  Both sides of the boundary, with a
+    ragged last block of 16 tokens, every token compared (top-8, so k is at its largest).
+    I = 256: at I = 128 and top-8 the kernels' schedule replayed on the host reaches 0.86 to
+    1.21 of the output bar over 200-300 tokens; here 0.64 to 0.76."""
+    cfg = dict(tokens=T, d_model=256, n_experts=E, top_k=8, d_expert=256, d_shared=256,
+               routed_scale=2.827, bias="uniform")
+    full_check(cfg, to_dev(S.make_inputs(cfg, "cpu", seed=60 + E + T)), intermediates=True)
+
+
 def test_near_ties_get_a_valid_topk():
     """Experts 3 and 5 share a router row and a bias, so every token scores them equally:
     whenever they straddle the k-th place the gap is 0 and the token leaves the bit-exact
