@@ -196,7 +196,7 @@ moe_status moe_forward_noalloc(const moe_dims* dims, const uint16_t* x, const fl
  * (4-byte aligned; a bf16 checkpoint gain converts exactly); norm_eps >= 0, finite.
  * The norm is computed in fp64 and rounded to fp32, then to bf16 (round-to-nearest-even
  * both times); Delta_ffn is moe_forward's fp32 sum, the residual is added to it in fp32
- * and the total rounded to bf16 once.  out must not alias x_res.
+ * and the total rounded to bf16 once.  out and x_res must not overlap (MOE_EINVAL).
  * Workspace: moe_block_workspace_bytes (moe_workspace_bytes plus the bf16 x_ffn, which
  * the call leaves at byte offset moe_workspace_bytes(dims) of ws). */
 moe_status moe_block_workspace_bytes(const moe_dims* dims, size_t* bytes);

@@ -504,7 +504,13 @@ moe_status moe_forward_block(const moe_dims* dims, const uint16_t* x_res, const 
   MOE_TRY(check_dims(dims));
   const moe_dims& d = *dims;
   if (d.tokens == 0) return MOE_OK;
-  MOE_NEED(aligned(x_res, 16) && aligned(norm_w, 4) && x_res != out);
+  MOE_NEED(aligned(x_res, 16) && aligned(norm_w, 4));
+  {
+    // out and x_res must not share any byte (both [T, d] bf16)
+    const uintptr_t a = (uintptr_t)x_res, o = (uintptr_t)out;
+    const uintptr_t n = (uintptr_t)d.tokens * (uintptr_t)d.d_model * 2u;
+    MOE_NEED(o + n <= a || a + n <= o);
+  }
   if (!(norm_eps >= 0.0f) || !isfinite(norm_eps)) return MOE_EINVAL;
   MOE_TRY(check_forward_args(d, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, ws, ws_bytes));
   const size_t base = layout(d).total;

@@ -192,7 +192,7 @@ def test_block_arguments_checked():
     L = M.lib()
     d = _k2(128)
     P = _fake(0x100000)
-    Q = _fake(0x200000)
+    Q = _fake(0x10000000)        # [T, d] bf16 is 1.8 MB: far from P
     base = M.moe_workspace_bytes(d)
     need = M.moe_block_workspace_bytes(d)
     assert need == base + 128 * 7168 * 2
@@ -201,8 +201,10 @@ def test_block_arguments_checked():
     # the x_ffn buffer is part of the workspace
     assert L.moe_forward_block(*args(P, P, 1e-6, Q, base)) == M.MOE_EWORKSPACE
     assert L.moe_forward_block(*args(P, P, 1e-6, Q, need - 1)) == M.MOE_EWORKSPACE
-    # output aliasing the residual, null gain, bad eps
+    # output aliasing the residual, or overlapping it by one row, null gain, bad eps
     assert L.moe_forward_block(*args(P, P, 1e-6, P, need)) == M.MOE_EINVAL
+    assert L.moe_forward_block(*args(P, P, 1e-6, _fake(0x100000 + 7168 * 2), need)) == M.MOE_EINVAL
+    assert L.moe_forward_block(*args(_fake(0x100000 + 7168 * 2), P, 1e-6, P, need)) == M.MOE_EINVAL
     assert L.moe_forward_block(*args(P, None, 1e-6, Q, need)) == M.MOE_EINVAL
     assert L.moe_forward_block(*args(P, P, -1.0, Q, need)) == M.MOE_EINVAL
     assert L.moe_forward_block(*args(P, P, float("nan"), Q, need)) == M.MOE_EINVAL
