@@ -149,12 +149,10 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(const FfnArgs a) {
 // slot, so the global reads stay 128 contiguous bytes per row, and an MFMA operand read
 // (16 consecutive rows, one piece) touches 16 distinct 16-byte bank groups.
 constexpr int kLdsChunkK = 64;
-// Waves per workgroup: 8.  The kernel is also written for 4 (one per SIMD, 128 rows x 128
-// outputs each); eight measured faster at the K2 shape (see the launch below).
+// Eight waves per workgroup (four, one per SIMD, measured slower: see the launch below).
 constexpr int kLdsWaves = 8;
-static_assert(kLdsWaves == 4 || kLdsWaves == 8, "waves per 256-row workgroup");
-constexpr int kLdsUnits = 32 / kLdsWaves;       // 1 KiB transfers per wave and operand
-constexpr int kLdsNO = kLdsWaves == 4 ? 4 : 2;  // 32-output fragments per wave
+constexpr int kLdsUnits = 32 / kLdsWaves;  // 1 KiB transfers per wave and operand (4)
+constexpr int kLdsNO = 2;                  // 32-output fragments per wave
 
 struct LdsCtx {
   __amdgpu_buffer_rsrc_t act;  // activation rows (x, or the tile's rows of h)
@@ -189,26 +187,21 @@ __device__ __forceinline__ void lds_fetch_w(const LdsCtx& x, u32x4_t* wgt, int w
 // wrd/ard, so the fragment offsets are immediates).
 template <bool GATEUP>
 __device__ __forceinline__ constexpr int wfrag_row(int o) {
-  // four fragments: gate/up o = 0, 1 are W1 rows 32 o of the wave's 64 features, o = 2, 3
-  // the same features of W3 (128 rows further); otherwise 32 o.  Two fragments: gate/up
-  // o = 0 the wave's 32 W1 features, o = 1 the same of W3; otherwise 32 o.
-  return kLdsNO == 4 ? (GATEUP ? 128 * (o >> 1) + 32 * (o & 1) : 32 * o)
-                     : (GATEUP ? 128 * o : 32 * o);
+  // gate/up: o = 0 the wave's 32 W1 features, o = 1 the same features of W3 (128 rows
+  // further); otherwise 32 o
+  return GATEUP ? 128 * o : 32 * o;
 }
 
 // Chunk c reads activation buffer Acur and weight buffer Wcur; during it the activations
 // of chunk c + 1 go to Anext (sub-steps 0 and 1, half of the wave's units each) and the
-// weights of chunk c + 2 to Wnext2 (sub-steps 2 and 3).  All buffers are separate LDS arrays, so the
-// compiler can tell which pending transfer an LDS read depends on.  At the barrier before
-// chunk c + 1 only the wave's weight transfers of chunk c + 2 (8 with four waves, 4 with
-// eight) may still be in flight: the activation transfers of chunk c + 1 were issued
-// before them, and transfers complete in order.
+// weights of chunk c + 2 to Wnext2 (sub-steps 2 and 3).  All buffers are separate LDS
+// arrays, so the compiler can tell which pending transfer an LDS read depends on.  At the
+// barrier before chunk c + 1 only the wave's 4 weight transfers of chunk c + 2 may still be
+// in flight: the activation transfers of chunk c + 1 were issued before them, and
+// transfers complete in order.
 __device__ __forceinline__ void lds_sync_chunk() {
-  static_assert(kLdsUnits == 8 || kLdsUnits == 4, "weight transfers per wave");
-  if constexpr (kLdsUnits == 8)
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+  static_assert(kLdsUnits == 4, "the wait below counts the wave's weight transfers");
+  asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -314,7 +307,7 @@ __device__ __forceinline__ void lds_tile(const FfnArgs& a, const LdsCtx& x, cons
   lds_barrier();
   if constexpr (NF > 0) {
     // staging: the first half of the waves in the even buffer, the rest in the odd one
-    // (16 KiB each with four waves, 8 KiB with eight)
+    // (8 KiB per wave)
     constexpr int HW = kLdsWaves / 2, SL = 2048 / HW;
     if (wave < HW)
       lds_epilogue<EPI, NF, kLdsNO>(a, b.A + (wave % HW) * SL, acc, arow, 64, tile, nbase,
@@ -345,7 +338,7 @@ __global__ __launch_bounds__(64 * kLdsWaves, 1) void ffn_lds_kernel(const FfnArg
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // wave (wm, wn): rows half wm, outputs part wn (of 2 with four waves, of 4 with eight)
+  // wave (wm, wn): rows half wm, outputs part wn (of 4)
   const int wm = wave / (kLdsWaves / 2), wn = wave % (kLdsWaves / 2);
   const int K = a.K, N = a.N;
   const int nrows = tile.row_end - tile.row_begin;
@@ -400,8 +393,8 @@ __global__ __launch_bounds__(64 * kLdsWaves, 1) void ffn_lds_kernel(const FfnArg
   // the two row halves interleave 32-row fragments (wave wm: tile rows 64 t + 32 wm ..),
   // so a partly filled tile keeps both halves equally busy
   const int arow = 32 * wm;
-  // first weight row of this wave's fragments: gate/up W1 rows 64 wn (W3 rows 128 + 64 wn),
-  // with eight waves 32 wn; otherwise 128 wn, with eight waves 64 wn
+  // first weight row of this wave's fragments: gate/up W1 rows 32 wn (W3 rows 128 + 32 wn);
+  // otherwise 64 wn
   constexpr int OPW = 256 / (kLdsWaves / 2);  // weight rows of the wave's fragments
   const int wrow0 = (GATEUP ? OPW / 2 : OPW) * wn;
   {
