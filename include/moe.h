@@ -25,11 +25,19 @@
  *       ws1, ws3 [Is, d]    bf16        ws2      [d, Is]   bf16     (shared expert)
  *   - Row p of the "grouped" order: the T*k (token, slot) pairs sorted by expert, expert 0
  *     first; inside an expert's segment tokens ascend.  Slot id = t*k + slot.
- *   - The caller owns all memory.  The library allocates nothing, keeps no state between
- *     calls and never synchronises the host; all work is queued on `stream` (a
- *     hipStream_t; NULL = the default stream).  Concurrent calls need their own workspace.
- *     (The one exception, moe_forward_noalloc, works in a device array the library holds
- *     instead of a workspace.)
+ *   - The caller owns all memory.  The library allocates nothing and never synchronises
+ *     the host; all work is queued on `stream` (a hipStream_t; NULL = the default stream).
+ *     Concurrent calls need their own workspace.  (The one exception, moe_forward_noalloc,
+ *     works in a device array the library holds instead of a workspace.)
+ *   - No result depends on an earlier call.  The routing of up to 512 tokens over more
+ *     than 16 experts counts, per block of 16 tokens, the router workgroups that have
+ *     finished, in a small counter array the library holds on each GPU (zero at load, and
+ *     back to zero at the end of every routing launch).  Each workspace address is given
+ *     its own slot of 1024; a workspace keeps its slot while it is among the 1024 most
+ *     recently used on that GPU, and forever once a call on it has been captured into a
+ *     graph.  So calls that may overlap, having their own workspaces, never share
+ *     counters; capturing calls on more than 1024 workspaces of one GPU fails with
+ *     MOE_EHIP.
  *   - Every output is fully overwritten.  tokens == 0 is a valid no-op.
  *   - Errors are status codes, checked on the host BEFORE anything is launched:
  *       MOE_EINVAL       null / misaligned (16 B) pointer, impossible dims

@@ -128,10 +128,10 @@ struct TileSpec {
 };
 
 // Router.  Up to kRouterSmallT tokens, one kernel computes each (16 tokens x 16 experts)
-// tile of z over the whole K with the sigmoid and the bias in its epilogue.  With at most
-// 16 experts it also takes each token's top-k and gates; otherwise it writes the biased
-// scores and the sigmoids, [T, E] fp32 each (router_zpart_floats holds both), and one wave
-// per token of the selection launch takes them.  Above kRouterSmallT, the bf16 (hi, mid,
+// tile of z over the whole K with the sigmoid and the bias in its epilogue, and takes each
+// token's top-k and gates: from LDS with at most 16 experts, else from the biased scores
+// and the sigmoids, [T, E] fp32 each (router_zpart_floats holds both), in the last
+// workgroup of each token block to finish.  Above kRouterSmallT, the bf16 (hi, mid,
 // lo) copy of W_r (w_split, [3 router_part_rows(E), d]) feeds the 256-row GEMM kernel,
 // whose partial logits (z_part) the selection kernel adds in fp64.  logits may be null.
 constexpr int64_t kRouterSmallT = 512;
@@ -173,22 +173,23 @@ struct RouterNorm {
   uint16_t* x_ffn;
 };
 
-// The routing up to kRouterSmallT tokens: the scores (score = fl32(sigmoid(z) + b), NaN ->
-// -inf; score and sig, [T, E] fp32 each, hold them between the launches when there are
-// two), then the top-k into idx and the gates into w: one launch up to 16 experts, two
-// above.  With norm non-null, x is the residual stream and the router reads its normalised
-// rows (and writes them to norm->x_ffn).
+// The routing up to kRouterSmallT tokens, one launch: the scores (score = fl32(sigmoid(z) +
+// b), NaN -> -inf; above 16 experts score and sig, [T, E] fp32 each, carry them from the
+// workgroups of a token block to its last one), then the top-k into idx and the gates into
+// w.  ws identifies the call's workspace: the launch counts arrivals in that workspace's
+// slot of the library's counters.  With norm non-null, x is the residual stream and the
+// router reads its normalised rows (and writes them to norm->x_ffn).
 hipError_t launch_router_small(const uint16_t* x, const RouterNorm* norm, const float* w_r,
                                const float* bias, int64_t T, int d, int E, int k, float alpha,
                                float* score, float* sig, float* logits, int32_t* idx, float* w,
-                               hipStream_t s);
+                               const void* ws, hipStream_t s);
 
 // The whole routing: launch_router_small up to kRouterSmallT tokens, else the split, GEMM
 // and selection launches.
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
                          int E, int k, float alpha, uint16_t* w_split, float* z_part,
                          Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,
-                         float* topk_w, hipStream_t s);
+                         float* topk_w, const void* ws, hipStream_t s);
 
 
 // ts (or null): also build the tile list of a grouped launch for the new offsets into

@@ -147,7 +147,7 @@ moe_status route_impl(const moe_dims& d, const uint16_t* x, const float* w_r, co
   return hip_status(moe::launch_router(x, w_r, b, d.tokens, d.d_model, d.n_experts, d.top_k,
                                        d.routed_scale, at<uint16_t>(ws, L.wsplit),
                                        at<float>(ws, L.zpart), at<Tile>(ws, L.tiles),
-                                       at<int32_t>(ws, L.ntiles), logits, idx, w, s));
+                                       at<int32_t>(ws, L.ntiles), logits, idx, w, ws, s));
 }
 
 // ts (or null): the permutation also builds this tile list in the workspace, for the
@@ -249,9 +249,8 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
 }
 
 // Routing and permutation of a layer entry point, into the workspace arrays at the given
-// offsets (and the tile list of ts when ts is non-null).  Up to kRouterSmallT tokens: the
-// router kernel computes the scores, and takes the top-k and the gates itself up to 16
-// experts (else a selection launch does).  With norm non-null, x is the residual stream x' and the experts'
+// offsets (and the tile list of ts when ts is non-null).  Up to kRouterSmallT tokens one
+// router kernel computes the scores and takes the top-k and the gates.  With norm non-null, x is the residual stream x' and the experts'
 // input x_ffn = RMSNorm(x') goes to norm->x_ffn: written by the router kernel up to
 // kRouterSmallT tokens, else by the norm kernel before the router.  The experts' input (x,
 // or norm->x_ffn) is returned through x_in.
@@ -284,7 +283,7 @@ moe_status route_permute(const moe_dims& d, const uint16_t* x, const moe::Router
     float* score = at<float>(ws, B.zpart);
     MOE_TRY(hip_status(moe::launch_router_small(x, norm, w_router, bias, T, d.d_model, E, d.top_k,
                                                 d.routed_scale, score, score + T * E, nullptr,
-                                                idx, w, s)));
+                                                idx, w, ws, s)));
     *x_in = norm != nullptr ? norm->x_ffn : x;
     return hip_status(moe::launch_permute(idx, T, E, d.top_k, hist, base, counts, offsets, perm,
                                           inv, s, ts, tiles, ntiles));
@@ -298,7 +297,7 @@ moe_status route_permute(const moe_dims& d, const uint16_t* x, const moe::Router
   MOE_TRY(hip_status(moe::launch_router(x, w_router, bias, T, d.d_model, E, d.top_k,
                                         d.routed_scale, at<uint16_t>(ws, B.wsplit),
                                         at<float>(ws, B.zpart), tiles, ntiles, nullptr, idx, w,
-                                        s)));
+                                        ws, s)));
   return hip_status(moe::launch_permute(idx, T, E, d.top_k, hist, base, counts, offsets, perm,
                                         inv, s, ts, tiles, ntiles));
 }

@@ -9,18 +9,32 @@
 // product is exact in fp32.  Above kRouterSmallT tokens the three partial logits are
 // accumulated in fp32 by the grouped-GEMM kernels (one group, 3E outputs) and added in
 // fp64 by the selection kernel.  For fewer tokens (decode) router_scores_kernel does the
-// split in registers, owns whole logits, and applies the sigmoid and the bias itself; with
-// at most 16 experts one of its workgroups holds every logit of its tokens and takes their
-// top-k and gates as well.
+// split in registers, owns whole logits, applies the sigmoid and the bias, and takes the
+// top-k and the gates itself: with at most 16 experts one of its workgroups holds every
+// logit of its tokens, and with more the last workgroup of a token block to finish (an
+// arrival count per block) selects for the block.
 // (The split follows the bf16x3 scheme of Henry, Tang and Heinecke, "Leveraging the
 // bfloat16 artificial intelligence datatype for higher-precision computations", 2019.)
 #include <math.h>
+
+#include <mutex>
+#include <unordered_map>
 
 #include "common.h"
 #include "select.h"
 
 namespace moe {
 namespace {
+
+// Arrival counts of the small-batch router: kArrivalBlocks counters (one per 16-token
+// block) in each of kArrivalSlots slots, per GPU.  They are zero when the library is
+// loaded and the last workgroup of each block puts its counter back to zero, so they are
+// zero again whenever no router launch is running.  Each workspace is given a slot of its
+// own (arrival_slot below), so calls that may overlap, which need their own workspaces,
+// never share counters.
+constexpr int kArrivalSlots = 1024;
+constexpr int kArrivalBlocks = (int)(kRouterSmallT / 16);
+__device__ uint32_t g_arrivals[kArrivalSlots * kArrivalBlocks];
 
 // w_split[p][e][j], p = 0 (hi), 1 (mid), 2 (lo), each part Ep = router_part_rows(E) rows
 // of d: rows E .. Ep - 1 are zero, so that every part, and every row of partial logits the
@@ -114,19 +128,33 @@ __device__ __forceinline__ u32x4_t norm8(const u32x4_t& v, double rinv, const u3
   return o;
 }
 
-// SELECT (E <= 16, one expert tile): the workgroup's scores stay in LDS, and one wave per
-// token takes the top-k and the gates from them with the selection kernel's select_topk, so
-// the routing is the same bit for bit; score and sig are then not written.
-template <bool NORM, bool SELECT>
+// A float another workgroup wrote, read at device scope (not from a cache line that may be
+// stale for this CU).
+__device__ __forceinline__ float load_device(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The top-k and the gates of each token of the block (one wave per token, select_topk with
+// EPL experts per lane).  With one expert tile (gridDim.y == 1, E <= 16) the workgroup holds
+// every score of its tokens and selects from LDS; score and sig are then not written.  With
+// more, every workgroup writes its scores and sigmoids to score / sig, makes them visible
+// at device scope and adds one to its block's arrival count in slot `slot` of g_arrivals;
+// the workgroup that brings the count to gridDim.y is the block's last, and it puts the
+// count back to zero and selects from score / sig.  Both select from the same fp32 values,
+// so the routing does not depend on which workgroup selects.
+template <bool NORM, int EPL>
 __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
     uint16_t* __restrict__ x_ffn, const float* __restrict__ w_r, const float* __restrict__ bias,
     int64_t T, int d, int E, float* __restrict__ score, float* __restrict__ sig,
     float* __restrict__ logits, int k, float alpha, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    float* __restrict__ topk_w, int slot) {
+  constexpr bool kCanBeLocal = EPL == 1;
   __shared__ f32x4_t part[kRouterWaves][3][64];
   __shared__ double rinv_s[16];
-  __shared__ float sel_sc[SELECT ? 16 : 1][16], sel_sg[SELECT ? 16 : 1][16];
+  __shared__ float sel_sc[kCanBeLocal ? 16 : 1][16], sel_sg[kCanBeLocal ? 16 : 1][16];
+  __shared__ uint32_t last_s;
+  const bool local = kCanBeLocal && gridDim.y == 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * 16;
   const int e0 = blockIdx.y * 16;
@@ -227,19 +255,19 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
       s = 1.0f / (1.0f + expf(-z));
       v = s + bias[ee];
       if (v != v) v = -INFINITY;
-      if constexpr (!SELECT) {
+      if (!local) {
         score[tt * E + ee] = v;
         sig[tt * E + ee] = s;
       }
     }
-    if constexpr (SELECT) {
+    if (kCanBeLocal && local) {
       sel_sc[i][jj] = v;
       sel_sg[i][jj] = s;
     }
   }
-  if constexpr (SELECT) {
+  if (kCanBeLocal && local) {
     __syncthreads();
-    // lane l holds expert l (lanes from E on: -inf), as the selection kernel loads them
+    // lane l holds expert l (lanes from E on: -inf), as load_scores would give them
     for (int i = wave; i < 16; i += kRouterWaves) {
       const int64_t tt = t0 + i;
       if (tt >= T) break;
@@ -247,23 +275,45 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
       float sg[1] = {lane < E ? sel_sg[i][lane] : 0.0f};
       select_topk<1>(sc, sg, E, k, alpha, lane, topk_idx + tt * k, topk_w + tt * k, nullptr);
     }
+    return;
+  }
+  // this workgroup's scores out to device scope before it is counted
+  if (tid < 256) __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* cnt = g_arrivals + (int64_t)slot * kArrivalBlocks + blockIdx.x;
+    const uint32_t before =
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t last = before + 1 == gridDim.y ? 1u : 0u;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_s = last;
+  }
+  __syncthreads();
+  if (last_s == 0) return;
+  __threadfence();
+  // every workgroup of the block has counted, so all of its scores are out: lane l holds
+  // experts l, l + 64, ... (load_scores' order, at clamped addresses)
+  for (int i = wave; i < 16; i += kRouterWaves) {
+    const int64_t tt = t0 + i;
+    if (tt >= T) break;
+    float sc[EPL], sg[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = min(lane + 64 * j, E - 1);
+      sc[j] = load_device(score + tt * E + e);
+      sg[j] = load_device(sig + tt * E + e);
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j >= E) {
+        sc[j] = -INFINITY;
+        sg[j] = 0.0f;
+      }
+    select_topk<EPL>(sc, sg, E, k, alpha, lane, topk_idx + tt * k, topk_w + tt * k, nullptr);
   }
 }
 
 // ---------------------------------------------------------------- top-k + gates
-// Up to kRouterSmallT tokens: one wave per token over the scores the kernel above wrote.
-template <int EPL>
-__global__ __launch_bounds__(256) void router_select_scores_kernel(
-    const float* __restrict__ score, const float* __restrict__ sig, int64_t T, int E, int k,
-    float alpha, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float sc[EPL], sg[EPL];
-  load_scores<EPL>(score + t * E, sig + t * E, E, lane, sc, sg);
-  select_topk<EPL>(sc, sg, E, k, alpha, lane, topk_idx + t * k, topk_w + t * k, nullptr);
-}
-
 // Above kRouterSmallT tokens: z = the np partial logits (hi, mid, lo of each K slice)
 // summed in fp64, rounded to fp32; then as above.
 template <int EPL, int PB>
@@ -338,26 +388,56 @@ void select_launch(const float* z_part, int np, int row_parts, int pstride, cons
                        row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
 }
 
-// Up to this many experts one router_scores_kernel workgroup covers every expert of its
-// tokens and selects in place (SELECT); above, the selection is a launch of its own.
-constexpr int kRouterSelectMaxE = 16;
+// The arrival slot of a workspace on the current device (key: the workspace's address).
+// A workspace keeps its slot while it is among the kArrivalSlots most recently used; a
+// slot first used while `s` is being captured into a graph is never given to another
+// workspace, since the graph's launches carry it.
+struct ArrivalTable {
+  std::unordered_map<uintptr_t, int> slot_of;
+  uintptr_t key[kArrivalSlots] = {};
+  uint64_t used_at[kArrivalSlots] = {};
+  bool taken[kArrivalSlots] = {};
+  bool pinned[kArrivalSlots] = {};
+  uint64_t clock = 0;
+};
 
-hipError_t launch_router_select(const float* score, const float* sig, int64_t T, int E, int k,
-                                float alpha, int32_t* idx, float* w, hipStream_t s) {
-  const dim3 grid((unsigned)((T + 3) / 4));
-#define MOE_SELECT_SCORES(N)                                                                  \
-  hipLaunchKernelGGL(router_select_scores_kernel<N>, grid, dim3(256), 0, s, score, sig, T, E, \
-                     k, alpha, idx, w)
-  switch (select_epl(E)) {
-    case 1: MOE_SELECT_SCORES(1); break;
-    case 2: MOE_SELECT_SCORES(2); break;
-    case 4: MOE_SELECT_SCORES(4); break;
-    case 6: MOE_SELECT_SCORES(6); break;
-    case 8: MOE_SELECT_SCORES(8); break;
-    default: MOE_SELECT_SCORES(16); break;
+hipError_t arrival_slot(const void* ws, hipStream_t s, int* slot) {
+  static std::mutex mu;
+  static std::unordered_map<int, ArrivalTable> tables;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  err = hipStreamIsCapturing(s, &cap);
+  if (err != hipSuccess) return err;
+  const uintptr_t key = reinterpret_cast<uintptr_t>(ws);
+  std::lock_guard<std::mutex> lock(mu);
+  ArrivalTable& tb = tables[dev];
+  ++tb.clock;
+  int i;
+  const auto it = tb.slot_of.find(key);
+  if (it != tb.slot_of.end()) {
+    i = it->second;
+  } else {
+    // a free slot, else the least recently used one that no graph holds
+    i = -1;
+    for (int j = 0; j < kArrivalSlots; ++j) {
+      if (!tb.taken[j]) {
+        i = j;
+        break;
+      }
+      if (!tb.pinned[j] && (i < 0 || tb.used_at[j] < tb.used_at[i])) i = j;
+    }
+    if (i < 0) return hipErrorOutOfMemory;
+    if (tb.taken[i]) tb.slot_of.erase(tb.key[i]);
+    tb.taken[i] = true;
+    tb.key[i] = key;
+    tb.slot_of[key] = i;
   }
-#undef MOE_SELECT_SCORES
-  return hipGetLastError();
+  tb.used_at[i] = tb.clock;
+  if (cap != hipStreamCaptureStatusNone) tb.pinned[i] = true;
+  *slot = i;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -365,39 +445,51 @@ hipError_t launch_router_select(const float* score, const float* sig, int64_t T,
 hipError_t launch_router_small(const uint16_t* x, const RouterNorm* norm, const float* w_r,
                                const float* bias, int64_t T, int d, int E, int k, float alpha,
                                float* score, float* sig, float* logits, int32_t* idx, float* w,
-                               hipStream_t s) {
+                               const void* ws, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (T > kRouterSmallT) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16));
-  const bool sel = E <= kRouterSelectMaxE;
+  int slot = 0;
+  if (grid.y > 1) {
+    const hipError_t err = arrival_slot(ws, s, &slot);
+    if (err != hipSuccess) return err;
+  }
   const float* gain = norm != nullptr ? norm->gain : nullptr;
   const float eps = norm != nullptr ? norm->eps : 0.0f;
   uint16_t* x_ffn = norm != nullptr ? norm->x_ffn : nullptr;
-#define MOE_SCORES(NORM, SEL)                                                                  \
-  hipLaunchKernelGGL((router_scores_kernel<NORM, SEL>), grid, dim3(64 * kRouterWaves), 0, s, x, \
-                     gain, eps, x_ffn, w_r, bias, T, d, E, score, sig, logits, k, alpha, idx, w)
-  if (norm != nullptr) {
-    if (sel) MOE_SCORES(true, true);
-    else MOE_SCORES(true, false);
-  } else {
-    if (sel) MOE_SCORES(false, true);
-    else MOE_SCORES(false, false);
+#define MOE_SCORES(NORM, EPL)                                                                  \
+  hipLaunchKernelGGL((router_scores_kernel<NORM, EPL>), grid, dim3(64 * kRouterWaves), 0, s, x, \
+                     gain, eps, x_ffn, w_r, bias, T, d, E, score, sig, logits, k, alpha, idx, w, \
+                     slot)
+#define MOE_SCORES_EPL(NORM)             \
+  switch (select_epl(E)) {               \
+    case 1: MOE_SCORES(NORM, 1); break;  \
+    case 2: MOE_SCORES(NORM, 2); break;  \
+    case 4: MOE_SCORES(NORM, 4); break;  \
+    case 6: MOE_SCORES(NORM, 6); break;  \
+    case 8: MOE_SCORES(NORM, 8); break;  \
+    default: MOE_SCORES(NORM, 16); break; \
   }
+  if (norm != nullptr) {
+    MOE_SCORES_EPL(true)
+  } else {
+    MOE_SCORES_EPL(false)
+  }
+#undef MOE_SCORES_EPL
 #undef MOE_SCORES
-  const hipError_t err = hipGetLastError();
-  if (err != hipSuccess || sel) return err;
-  return launch_router_select(score, sig, T, E, k, alpha, idx, w, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_router(const uint16_t* x, const float* w_r, const float* bias, int64_t T, int d,
                          int E, int k, float alpha, uint16_t* w_split, float* z_part,
                          Tile* tiles, int32_t* ntiles, float* logits, int32_t* topk_idx,
-                         float* topk_w, hipStream_t s) {
+                         float* topk_w, const void* ws, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   hipError_t err;
   if (T <= kRouterSmallT) {
     // scores [T, E] and sigmoids [T, E] in z_part
     return launch_router_small(x, nullptr, w_r, bias, T, d, E, k, alpha, z_part, z_part + T * E,
-                               logits, topk_idx, topk_w, s);
+                               logits, topk_idx, topk_w, ws, s);
   }
   const int Ep = router_part_rows(E);
   const int64_t n = (int64_t)E * d, np_ = (int64_t)Ep * d;

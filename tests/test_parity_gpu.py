@@ -448,8 +448,9 @@ def test_expert_count_not_a_multiple_of_four(E, T, k):
 
 @pytest.mark.parametrize("E,T", [(16, 45), (17, 45), (16, 300), (17, 300)])
 def test_router_selection_in_place_boundary(E, T):
-    """Up to 16 experts the router kernel takes the top-k and the gates itself; 17 experts
-    need a second expert tile and the selection launch.  Both sides of the boundary, with a
+    """Up to 16 experts one router workgroup holds every score of its tokens and selects
+    from LDS; 17 experts need a second expert tile, and the last workgroup of each token
+    block to finish selects from the scores in memory.  Both sides of the boundary, with a
     ragged last block of 16 tokens, every token compared (top-8, so k is at its largest).
     I = 256: at I = 128 and top-8 the kernels' schedule replayed on the host reaches 0.86 to
     1.21 of the output bar over 200-300 tokens; here 0.64 to 0.76."""
