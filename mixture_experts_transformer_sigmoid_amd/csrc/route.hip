@@ -137,11 +137,12 @@ __device__ __forceinline__ float load_device(const float* p) {
 // The top-k and the gates of each token of the block (one wave per token, select_topk with
 // EPL experts per lane).  With one expert tile (gridDim.y == 1, E <= 16) the workgroup holds
 // every score of its tokens and selects from LDS; score and sig are then not written.  With
-// more, every workgroup writes its scores and sigmoids to score / sig, makes them visible
-// at device scope and adds one to its block's arrival count in slot `slot` of g_arrivals;
-// the workgroup that brings the count to gridDim.y is the block's last, and it puts the
-// count back to zero and selects from score / sig.  Both select from the same fp32 values,
-// so the routing does not depend on which workgroup selects.
+// more, every workgroup writes its scores and sigmoids to score / sig and adds one to its
+// block's arrival count in slot `slot` of g_arrivals (a release at device scope); the
+// workgroup that brings the count to gridDim.y is the block's last: it acquires, puts the
+// count back to zero and selects from score / sig.  Both ways select from the same fp32
+// values, so the routing does not depend on which workgroup selects.  No workgroup waits
+// for another.
 template <bool NORM, int EPL>
 __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
   constexpr bool kCanBeLocal = EPL == 1;
   __shared__ f32x4_t part[kRouterWaves][3][64];
   __shared__ double rinv_s[16];
-  __shared__ float sel_sc[kCanBeLocal ? 16 : 1][16], sel_sg[kCanBeLocal ? 16 : 1][16];
+  __shared__ float sel_sc[16][16], sel_sg[16][16];
   __shared__ uint32_t last_s;
   const bool local = kCanBeLocal && gridDim.y == 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
@@ -255,18 +256,12 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
       s = 1.0f / (1.0f + expf(-z));
       v = s + bias[ee];
       if (v != v) v = -INFINITY;
-      if (!local) {
-        score[tt * E + ee] = v;
-        sig[tt * E + ee] = s;
-      }
     }
-    if (kCanBeLocal && local) {
-      sel_sc[i][jj] = v;
-      sel_sg[i][jj] = s;
-    }
+    sel_sc[i][jj] = v;
+    sel_sg[i][jj] = s;
   }
+  __syncthreads();
   if (kCanBeLocal && local) {
-    __syncthreads();
     // lane l holds expert l (lanes from E on: -inf), as load_scores would give them
     for (int i = wave; i < 16; i += kRouterWaves) {
       const int64_t tt = t0 + i;
@@ -277,22 +272,38 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
     }
     return;
   }
-  // this workgroup's scores out to device scope before it is counted
-  if (tid < 256) __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t* cnt = g_arrivals + (int64_t)slot * kArrivalBlocks + blockIdx.x;
-    const uint32_t before =
-        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t last = before + 1 == gridDim.y ? 1u : 0u;
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_s = last;
+  if (wave == 0) {
+    // wave 0 writes the tile (lane: experts e0 + (lane & 15) of tokens t0 + (lane >> 4) +
+    // 4 j) and counts the workgroup's arrival with a release at device scope (its stores
+    // go out of this XCD's L2 first).  The block's last workgroup acquires at device scope
+    // before any of its waves reads the other workgroups' scores; the others return.
+    const int ee = e0 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = (lane >> 4) + 4 * j;
+      const int64_t tt = t0 + i;
+      if (tt < T && ee < E) {
+        score[tt * E + ee] = sel_sc[i][lane & 15];
+        sig[tt * E + ee] = sel_sg[i][lane & 15];
+      }
+    }
+    if (lane == 0) {
+      uint32_t* cnt = g_arrivals + (int64_t)slot * kArrivalBlocks + blockIdx.x;
+      const uint32_t before =
+          __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t last = before + 1 == gridDim.y ? 1u : 0u;
+      if (last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      last_s = last;
+    }
   }
   __syncthreads();
   if (last_s == 0) return;
-  __threadfence();
-  // every workgroup of the block has counted, so all of its scores are out: lane l holds
-  // experts l, l + 64, ... (load_scores' order, at clamped addresses)
+  // every workgroup of the block has counted, so all of its scores are out (the barrier
+  // orders every wave's loads after wave 0's acquire): lane l holds experts l, l + 64, ...
+  // (load_scores' order, at clamped addresses)
   for (int i = wave; i < 16; i += kRouterWaves) {
     const int64_t tt = t0 + i;
     if (tt >= T) break;
