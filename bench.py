@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -133,10 +134,12 @@ def mfma_for(kernel_substr, grid):
     return None
 
 
-def traffic_for(kernel_substr):
+def traffic_for(kernel_substr, algorithmic_bytes):
     """HBM bytes per launch of a kernel from the committed counter summary, or None when it
-    is missing, the kernel ran with more than one grid there (several workloads), or the
-    kernel sources changed since the counters were taken."""
+    is missing or the kernel sources changed since the counters were taken.  One kernel can
+    serve several workloads (the decode gate/up kernel also runs the tiny config), each with
+    its own launch grid: the entry taken is the one whose bytes are nearest the launch's
+    algorithmic bytes, and only if within a factor of 2 of them."""
     try:
         with open(TRAFFIC_JSON) as f:
             t = json.load(f)
@@ -144,12 +147,19 @@ def traffic_for(kernel_substr):
         return None
     if t.get("source_sha256") != kernel_source_hash():
         return None
+    best = None
     for name, grids in t["kernels"].items():
-        if kernel_substr in name and len(grids) == 1:
-            v = next(iter(grids.values()))
-            if "read_bytes" in v and "write_bytes" in v:
-                return v["read_bytes"] + v["write_bytes"]
-    return None
+        if kernel_substr not in name:
+            continue
+        for v in grids.values():
+            if "read_bytes" not in v or "write_bytes" not in v:
+                continue
+            b = v["read_bytes"] + v["write_bytes"]
+            if best is None or abs(math.log(b / algorithmic_bytes)) < abs(math.log(best / algorithmic_bytes)):
+                best = b
+    if best is None or abs(math.log(best / algorithmic_bytes)) > math.log(2.0):
+        return None
+    return best
 
 
 def parse():
@@ -647,7 +657,7 @@ def main():
                                "weights/activations, fp32 router and accumulation",
                    "tokens": T, "active_experts": active},
         "roofline": {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic_for(GATEUP_KERNEL[args.workload]),
+                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic_for(GATEUP_KERNEL[args.workload], alg["gateup_bytes"]),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": GATEUP_KERNEL[args.workload] + " (+ its tile-list launch)",
                      "ms_per_launch": gu_ms, "bytes_per_launch": alg["gateup_bytes"]},

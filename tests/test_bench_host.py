@@ -53,8 +53,8 @@ def test_traffic_summary_scaled_by_the_copy(tmp_path, monkeypatch):
     assert g["launches"] == 2
     assert g["read_bytes"] == pytest.approx(2000.0 * 1024 * 2)   # mean 2000 KiB x 2
     assert g["write_bytes"] == pytest.approx(20.0 * 1024)
-    assert bench.traffic_for("ffn_skinny_kernel<1, 16, 0>") == pytest.approx(
-        2000.0 * 1024 * 2 + 20.0 * 1024)
+    want = 2000.0 * 1024 * 2 + 20.0 * 1024
+    assert bench.traffic_for("ffn_skinny_kernel<1, 16, 0>", want * 1.3) == pytest.approx(want)
 
 
 def test_summaries_are_ignored_once_the_kernels_change(tmp_path, monkeypatch):
@@ -67,26 +67,31 @@ def test_summaries_are_ignored_once_the_kernels_change(tmp_path, monkeypatch):
     for name in ("t.json", "m.json"):
         with open(tmp_path / name, "w") as f:
             json.dump(stale, f)
-    assert bench.traffic_for("ffn_lds_kernel<0>") is None
+    assert bench.traffic_for("ffn_lds_kernel<0>", 2.0) is None
     assert bench.mfma_for("ffn_lds_kernel<0>", 2756608) is None
     # the same data under the current sources' hash is used
     stale["source_sha256"] = bench.kernel_source_hash()
     for name in ("t.json", "m.json"):
         with open(tmp_path / name, "w") as f:
             json.dump(stale, f)
-    assert bench.traffic_for("ffn_lds_kernel<0>") == pytest.approx(2.0)
+    assert bench.traffic_for("ffn_lds_kernel<0>", 2.0) == pytest.approx(2.0)
     assert bench.mfma_for("ffn_lds_kernel<0>", 2756608)["mfma_busy_frac"] == 0.5
 
 
-def test_traffic_lookup_refuses_a_kernel_seen_with_several_grids(tmp_path, monkeypatch):
+def test_traffic_lookup_takes_the_grid_nearest_the_algorithmic_bytes(tmp_path, monkeypatch):
+    """One kernel, two launch grids (two workloads): the entry nearest the launch's
+    algorithmic bytes is taken, and none when no entry is within a factor of 2."""
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "t.json"))
     k = "void moe::ffn_lds_kernel<0>(args)"
     t = {"source_sha256": bench.kernel_source_hash(),
          "kernels": {k: {"1": {"read_bytes": 1.0, "write_bytes": 1.0},
-                         "2": {"read_bytes": 5.0, "write_bytes": 5.0}}}}
+                         "2": {"read_bytes": 500.0, "write_bytes": 500.0}}}}
     with open(tmp_path / "t.json", "w") as f:
         json.dump(t, f)
-    assert bench.traffic_for("ffn_lds_kernel<0>") is None
+    assert bench.traffic_for("ffn_lds_kernel<0>", 900.0) == pytest.approx(1000.0)
+    assert bench.traffic_for("ffn_lds_kernel<0>", 1.5) == pytest.approx(2.0)
+    assert bench.traffic_for("ffn_lds_kernel<0>", 40.0) is None
+    assert bench.traffic_for("ffn_skinny_kernel", 1000.0) is None
 
 
 def test_mfma_summary_from_counters(tmp_path, monkeypatch):
