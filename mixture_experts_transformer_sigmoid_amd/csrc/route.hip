@@ -20,6 +20,7 @@
 #include <mutex>
 #include <unordered_map>
 
+#include "arrival_slots.h"
 #include "common.h"
 #include "select.h"
 
@@ -399,54 +400,20 @@ void select_launch(const float* z_part, int np, int row_parts, int pstride, cons
                        row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
 }
 
-// The arrival slot of a workspace on the current device (key: the workspace's address).
-// A workspace keeps its slot while it is among the kArrivalSlots most recently used; a
-// slot first used while `s` is being captured into a graph is never given to another
-// workspace, since the graph's launches carry it.
-struct ArrivalTable {
-  std::unordered_map<uintptr_t, int> slot_of;
-  uintptr_t key[kArrivalSlots] = {};
-  uint64_t used_at[kArrivalSlots] = {};
-  bool taken[kArrivalSlots] = {};
-  bool pinned[kArrivalSlots] = {};
-  uint64_t clock = 0;
-};
-
+// The arrival slot of a workspace on the current device (ArrivalSlotTable; pinned when
+// the call is being captured into a graph on `s`).
 hipError_t arrival_slot(const void* ws, hipStream_t s, int* slot) {
   static std::mutex mu;
-  static std::unordered_map<int, ArrivalTable> tables;
+  static std::unordered_map<int, ArrivalSlotTable<kArrivalSlots>> tables;
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   err = hipStreamIsCapturing(s, &cap);
   if (err != hipSuccess) return err;
-  const uintptr_t key = reinterpret_cast<uintptr_t>(ws);
   std::lock_guard<std::mutex> lock(mu);
-  ArrivalTable& tb = tables[dev];
-  ++tb.clock;
-  int i;
-  const auto it = tb.slot_of.find(key);
-  if (it != tb.slot_of.end()) {
-    i = it->second;
-  } else {
-    // a free slot, else the least recently used one that no graph holds
-    i = -1;
-    for (int j = 0; j < kArrivalSlots; ++j) {
-      if (!tb.taken[j]) {
-        i = j;
-        break;
-      }
-      if (!tb.pinned[j] && (i < 0 || tb.used_at[j] < tb.used_at[i])) i = j;
-    }
-    if (i < 0) return hipErrorOutOfMemory;
-    if (tb.taken[i]) tb.slot_of.erase(tb.key[i]);
-    tb.taken[i] = true;
-    tb.key[i] = key;
-    tb.slot_of[key] = i;
-  }
-  tb.used_at[i] = tb.clock;
-  if (cap != hipStreamCaptureStatusNone) tb.pinned[i] = true;
+  const int i = tables[dev].slot(reinterpret_cast<uintptr_t>(ws), cap != hipStreamCaptureStatusNone);
+  if (i < 0) return hipErrorOutOfMemory;
   *slot = i;
   return hipSuccess;
 }

@@ -1,0 +1,112 @@
+"""The router's arrival-slot table (csrc/arrival_slots.h), built with g++ on the host.
+
+Each workspace address gets a slot of the library's per-GPU arrival counters.  The
+properties the router relies on: a workspace keeps its slot while it is among the most
+recently used; two workspaces in use at the same time never share a slot; a slot used
+under graph capture is never given to another workspace; with every slot held by graphs
+a new workspace is refused (-1).  A small driver built on the table (4 slots) reads
+"key pin" lines and prints the slot of each.
+"""
+import os
+import random
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mixture_experts_transformer_sigmoid_amd", "csrc")
+SLOTS = 4
+
+DRIVER = r"""
+#include <stdio.h>
+#include "arrival_slots.h"
+int main() {
+  moe::ArrivalSlotTable<%d> t;
+  unsigned long long key;
+  int pin;
+  while (scanf("%%llu %%d", &key, &pin) == 2) printf("%%d\n", t.slot((uintptr_t)key, pin != 0));
+  return 0;
+}
+""" % SLOTS
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    d = tmp_path_factory.mktemp("arrival")
+    src = d / "driver.cpp"
+    src.write_text(DRIVER)
+    exe = d / "driver"
+    subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-I", CSRC, str(src), "-o", str(exe)],
+                   check=True)
+
+    def run(calls):
+        inp = "".join(f"{k} {int(p)}\n" for k, p in calls)
+        r = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True)
+        assert "runtime error" not in r.stderr, r.stderr
+        return [int(v) for v in r.stdout.split()]
+    return run
+
+
+def test_a_workspace_keeps_its_slot(driver):
+    got = driver([(1000, 0), (2000, 0), (1000, 0), (2000, 0), (1000, 0)])
+    assert got[0] == got[2] == got[4] and got[1] == got[3] and got[0] != got[1]
+
+
+def test_least_recently_used_slot_is_reused(driver):
+    # keys 1..4 fill the slots; key 1 is used again, so key 5 takes key 2's slot
+    got = driver([(1, 0), (2, 0), (3, 0), (4, 0), (1, 0), (5, 0), (2, 0)])
+    assert len(set(got[:4])) == 4
+    assert got[5] == got[1]            # key 5 in key 2's old slot
+    assert got[6] not in (got[5], got[4])   # key 2 back: not the slot of 5 or of 1
+
+
+def test_graph_slots_are_never_reassigned(driver):
+    # keys 1..3 captured (pinned); keys 10, 11, 12 then share the one free slot in turn
+    calls = [(1, 1), (2, 1), (3, 1), (10, 0), (11, 0), (12, 0), (1, 0), (2, 0), (3, 0)]
+    got = driver(calls)
+    pinned = got[:3]
+    assert len(set(pinned)) == 3
+    assert got[3] == got[4] == got[5] and got[3] not in pinned
+    assert got[6:] == pinned
+
+
+def test_every_slot_held_by_graphs_refuses_a_new_workspace(driver):
+    got = driver([(1, 1), (2, 1), (3, 1), (4, 1), (5, 0), (1, 0)])
+    assert len(set(got[:4])) == 4 and got[4] == -1 and got[5] == got[0]
+
+
+def test_random_sequences_keep_live_workspaces_apart(driver):
+    """Over random calls (some captured), with slot ownership tracked call by call: a
+    workspace that still owns a slot gets that slot back; a new one takes a free slot, or
+    else the slot of the least recently used owner that no graph holds; a slot taken under
+    capture never changes owner; -1 only when every slot is held by a graph."""
+    rng = random.Random(7)
+    calls = [(rng.randrange(1, 12), rng.random() < 0.004) for _ in range(4000)]
+    got = driver(calls)
+    owner = [None] * SLOTS          # slot -> key
+    last_use = {}
+    pinned = set()                  # slots held by a graph
+    for n, ((k, p), s) in enumerate(zip(calls, got)):
+        mine = [j for j in range(SLOTS) if owner[j] == k]
+        if mine:
+            assert s == mine[0], (n, k, s, mine)
+        elif s == -1:
+            assert len(pinned) == SLOTS, n
+            continue
+        elif None in owner:
+            assert owner[s] is None, (n, s)
+        else:
+            free = [j for j in range(SLOTS) if j not in pinned]
+            lru = min(free, key=lambda j: last_use[owner[j]])
+            assert s == lru, (n, s, lru)
+        assert s not in pinned or owner[s] == k, (n, s)
+        owner[s] = k
+        last_use[k] = n
+        if p:
+            pinned.add(s)
+    assert len(set(got)) > 1
