@@ -400,13 +400,13 @@ void select_launch(const float* z_part, int np, int row_parts, int pstride, cons
                        row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
 }
 
-// The arrival slot of a workspace on the current device (ArrivalSlotTable; pinned when
-// the call is being captured into a graph on `s`).
+// The arrival slot of a workspace on the device of `s`, where the router will run
+// (ArrivalSlotTable; pinned when the call is being captured into a graph on `s`).
 hipError_t arrival_slot(const void* ws, hipStream_t s, int* slot) {
   static std::mutex mu;
   static std::unordered_map<int, ArrivalSlotTable<kArrivalSlots>> tables;
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  hipDevice_t dev = 0;
+  hipError_t err = hipStreamGetDevice(s, &dev);
   if (err != hipSuccess) return err;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   err = hipStreamIsCapturing(s, &cap);
