@@ -97,6 +97,16 @@ def test_latent_routed_experts_on_the_wide_kernel():
     check(cfg, {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu", seed=71).items()})
 
 
+def test_latent_router_over_several_expert_tiles():
+    """64 experts: each 16-token block of the router spans four expert tiles, and the last
+    of them to finish takes the block's top-k (an arrival count per block).  The latent
+    entry point's own routing and permutation, and every token's output (the kernels'
+    schedule replayed on the host reaches 0.68 of the bar on these inputs)."""
+    cfg = S.with_overrides("tiny_latent", tokens=100, n_experts=64, top_k=8, d_expert=256,
+                           d_shared=256)
+    check(cfg, {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu", seed=71).items()})
+
+
 @pytest.mark.parametrize("T", [12, 600])
 def test_latent_shared_expert_kernel_choice(T):
     """The shared expert runs as a launch of its own (one group of T rows): the skinny

@@ -103,6 +103,41 @@ def test_two_streams_own_workspaces():
     say("  24 calls on two streams: routing equal")
 
 
+def test_layer_on_two_streams_own_workspaces():
+    """The whole layer (moe_forward, 128 tokens, 64 experts) on two streams at once, each
+    with its own workspace and input, 8 calls each queued alternately: every call's output
+    equals the one the same input gives alone, bit for bit."""
+    cfg = _cfg(128, 64)
+    dims = M.dims_for(cfg)
+    base = {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu", seed=85).items()}
+    xs = [base["x"], S.make_inputs(cfg, "cpu", seed=86)["x"].to(DEV)]
+
+    def forward(x, out, ws, stream=None):
+        M.moe_forward(dims, x, base["w_r"], base["b"], base["w1"], base["w3"], base["w2"],
+                      base["ws1"], base["ws3"], base["ws2"], out, ws, stream=stream)
+
+    want = []
+    for x in xs:
+        o = torch.empty(dims.tokens, dims.d_model, dtype=torch.bfloat16, device=DEV)
+        forward(x, o, M.workspace(dims))
+        want.append(o)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [M.workspace(dims), M.workspace(dims)]
+    outs = [[], []]
+    for _ in range(8):
+        for j in range(2):
+            o = torch.empty(dims.tokens, dims.d_model, dtype=torch.bfloat16, device=DEV)
+            with torch.cuda.stream(streams[j]):
+                forward(xs[j], o, wss[j], stream=streams[j])
+            outs[j].append(o)
+    torch.cuda.synchronize()
+    for j in range(2):
+        for i, o in enumerate(outs[j]):
+            assert torch.equal(o.view(torch.int16), want[j].view(torch.int16)), (j, i)
+    say("  16 layer calls on two streams: outputs equal")
+
+
 def test_graph_replays_between_eager_calls():
     """moe_forward (T = 100, 64 experts: four expert tiles per token block) captured in a
     HIP graph on its workspace, then replayed four times with a new input copied in before
