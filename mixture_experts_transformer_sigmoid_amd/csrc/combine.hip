@@ -225,9 +225,10 @@ hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float
 // then the scaling), rounded once to fp32 and then to bf16: the normalised row feeds the
 // router, whose top-k decision would turn on a one-ulp difference in any element, and in
 // fp64 the result does not depend on the summation order to within bf16 rounding.
-// The first kNormVec 8-element pieces of each thread (the whole row up to d = 8192) are
-// requested at once and kept in registers for the scaling pass; loads at clamped in-range
-// addresses, so that none sits behind a branch.  Wider rows loop over the rest.
+// The first kNormVec 8-element pieces of each thread (the whole row up to d = 8192), and
+// the gain values that scale them (two 16-byte loads per piece), are requested at once and
+// kept in registers for the scaling pass; loads at clamped in-range addresses, so that
+// none sits behind a branch.  Wider rows loop over the rest.
 constexpr int kNormVec = 4;
 
 __global__ __launch_bounds__(kCombineThreads) void rmsnorm_kernel(
@@ -239,8 +240,14 @@ __global__ __launch_bounds__(kCombineThreads) void rmsnorm_kernel(
   const uint16_t* row = x + t * d;
   constexpr int kSpan = kCombineThreads * 8;  // elements per pass of the workgroup
   u32x4_t v[kNormVec];
+  f32x4_t gv[kNormVec][2];
 #pragma unroll
-  for (int j = 0; j < kNormVec; ++j) v[j] = load16(row + min(tid * 8 + j * kSpan, d - 8));
+  for (int j = 0; j < kNormVec; ++j) {
+    const int c = min(tid * 8 + j * kSpan, d - 8);
+    v[j] = load16(row + c);
+    gv[j][0] = *reinterpret_cast<const f32x4_t*>(gain + c);
+    gv[j][1] = *reinterpret_cast<const f32x4_t*>(gain + c + 4);
+  }
   auto sumsq = [](const u32x4_t& w, double acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -263,20 +270,26 @@ __global__ __launch_bounds__(kCombineThreads) void rmsnorm_kernel(
 #pragma unroll
   for (int i = 0; i < kCombineThreads / 64; ++i) tot += wsum[i];
   const double inv_rms = 1.0 / sqrt(tot / (double)d + (double)eps);
-  auto scale_store = [&](const u32x4_t& w, int c) {
+  // element 2i of the piece with gain g[i >> 1][(2i) & 3], element 2i + 1 with the next
+  auto scale_store = [&](const u32x4_t& w, const f32x4_t (&g)[2], int c) {
     u32x4_t o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float a = (float)((double)bf16_to_f32(w[i] & 0xffffu) * inv_rms * (double)gain[c + 2 * i]);
-      const float b = (float)((double)bf16_to_f32(w[i] >> 16) * inv_rms * (double)gain[c + 2 * i + 1]);
+      const float ga = g[i >> 1][(2 * i) & 3], gb = g[i >> 1][(2 * i + 1) & 3];
+      const float a = (float)((double)bf16_to_f32(w[i] & 0xffffu) * inv_rms * (double)ga);
+      const float b = (float)((double)bf16_to_f32(w[i] >> 16) * inv_rms * (double)gb);
       o[i] = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
     }
     *reinterpret_cast<u32x4_t*>(out + t * d + c) = o;
   };
 #pragma unroll
   for (int j = 0; j < kNormVec; ++j)
-    if (tid * 8 + j * kSpan < d) scale_store(v[j], tid * 8 + j * kSpan);
-  for (int c = tid * 8 + kNormVec * kSpan; c < d; c += kSpan) scale_store(load16(row + c), c);
+    if (tid * 8 + j * kSpan < d) scale_store(v[j], gv[j], tid * 8 + j * kSpan);
+  for (int c = tid * 8 + kNormVec * kSpan; c < d; c += kSpan) {
+    const f32x4_t g[2] = {*reinterpret_cast<const f32x4_t*>(gain + c),
+                          *reinterpret_cast<const f32x4_t*>(gain + c + 4)};
+    scale_store(load16(row + c), g, c);
+  }
 }
 
 hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, uint16_t* out, int64_t T, int d,
