@@ -103,6 +103,35 @@ def test_two_streams_own_workspaces():
     say("  24 calls on two streams: routing equal")
 
 
+def test_many_calls_in_a_row_agree():
+    """400 routing calls back to back on one workspace at the K2 decode shape of the router
+    (128 tokens, 384 experts: 24 workgroups per token block meet at each count), each into
+    its own output: every call equals the first bit for bit, and the first equals the
+    oracle.  A handoff between workgroups that read a score before it was out would show as
+    a call that differs."""
+    cfg = dict(tokens=128, d_model=7168, n_experts=384, top_k=8, d_expert=64, d_shared=64,
+               routed_scale=2.827, bias="uniform")
+    dims = M.dims_for(cfg)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    inp = {"x": torch.randn(128, 7168, generator=g, device=DEV).to(torch.bfloat16),
+           "w_r": torch.randn(384, 7168, generator=g, device=DEV) / 7168 ** 0.5,
+           "b": torch.rand(384, generator=g, device=DEV) * 0.02 - 0.01}
+    ws = M.workspace(dims)
+    n = 400
+    idx = torch.full((n, 128, 8), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((n, 128, 8), float("nan"), dtype=torch.float32, device=DEV)
+    for i in range(n):
+        M.moe_route(dims, inp["x"], inp["w_r"], inp["b"], idx[i], w[i], None, ws)
+    torch.cuda.synchronize()
+    _check(idx[0], w[0], inp, dims, "first call")
+    same_idx = (idx == idx[0]).all(dim=2).all(dim=1)
+    same_w = (w.view(torch.int32) == w[0].view(torch.int32)).all(dim=2).all(dim=1)
+    bad = torch.nonzero(~(same_idx & same_w)).flatten().tolist()
+    say(f"  {n} calls: {len(bad)} differ from the first")
+    assert not bad, bad[:10]
+
+
 def test_layer_on_two_streams_own_workspaces():
     """The whole layer (moe_forward, 128 tokens, 64 experts) on two streams at once, each
     with its own workspace and input, 8 calls each queued alternately: every call's output
