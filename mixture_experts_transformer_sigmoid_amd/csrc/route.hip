@@ -263,7 +263,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
   }
   __syncthreads();
   if (kCanBeLocal && local) {
-    // lane l holds expert l (lanes from E on: -inf), as load_scores would give them
+    // lane l holds expert l (lanes from E on: -inf)
     for (int i = wave; i < 16; i += kRouterWaves) {
       const int64_t tt = t0 + i;
       if (tt >= T) break;
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_scores_kernel(
   if (last_s == 0) return;
   // every workgroup of the block has counted, so all of its scores are out (the barrier
   // orders every wave's loads after wave 0's acquire): lane l holds experts l, l + 64, ...
-  // (load_scores' order, at clamped addresses)
+  // (loads at clamped addresses; experts from E on get score -inf)
   for (int i = wave; i < 16; i += kRouterWaves) {
     const int64_t tt = t0 + i;
     if (tt >= T) break;

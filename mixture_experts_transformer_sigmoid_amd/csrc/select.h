@@ -79,25 +79,6 @@ __device__ __forceinline__ void select_topk(const float (&score)[EPL], const flo
   }
 }
 
-// A token's scores and sigmoids from rows of [T, E] arrays (loads at clamped in-range
-// addresses; experts past E get score -inf).
-template <int EPL>
-__device__ __forceinline__ void load_scores(const float* sc_row, const float* sg_row, int E,
-                                            int lane, float (&score)[EPL], float (&sig)[EPL]) {
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = min(lane + 64 * i, E - 1);
-    score[i] = sc_row[e];
-    sig[i] = sg_row[e];
-  }
-#pragma unroll
-  for (int i = 0; i < EPL; ++i)
-    if (lane + 64 * i >= E) {
-      score[i] = -INFINITY;
-      sig[i] = 0.0f;
-    }
-}
-
 // Experts per lane for E experts: the smallest instantiated EPL >= ceil(E / 64).
 inline int select_epl(int E) {
   const int epl = (E + 63) / 64;
