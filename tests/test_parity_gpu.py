@@ -564,6 +564,29 @@ def test_tie_break_lower_index():
     assert torch.all(g["idx"] == 3)
 
 
+@pytest.mark.parametrize("T,E,k", [(45, 16, 2), (100, 384, 8), (600, 384, 8), (33, 1000, 8)])
+def test_all_scores_equal_pick_the_lowest_indices(T, E, k):
+    """W_r = 0 and b = 0: every score is sigmoid(0) + 0 = 0.5, a tie between all experts
+    everywhere, so the lower-index rule alone decides (R2): each token takes experts
+    0 .. k-1 in that order, each with gate alpha / k.  Covers the selection from LDS (16
+    experts), in the router's last workgroup per token block (384 and 1000 experts, up to
+    512 tokens) and in the selection kernel above 512 tokens."""
+    cfg = dict(tokens=T, d_model=128, n_experts=E, top_k=k, d_expert=64, d_shared=64,
+               routed_scale=2.827, bias="uniform")
+    dims = M.dims_for(cfg)
+    x = torch.randn(T, 128, device=DEV).to(torch.bfloat16)
+    w_r = torch.zeros(E, 128, dtype=torch.float32, device=DEV)
+    b = torch.zeros(E, dtype=torch.float32, device=DEV)
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    M.moe_route(dims, x, w_r, b, idx, w, None, M.workspace(dims))
+    torch.cuda.synchronize()
+    want = torch.arange(k, dtype=torch.int32, device=DEV).expand(T, k)
+    assert torch.equal(idx, want), idx[:2]
+    g = torch.tensor(2.827 * 0.5, dtype=torch.float32) / torch.tensor(0.5 * k, dtype=torch.float32)
+    assert torch.allclose(w.cpu(), g.expand(T, k), rtol=0, atol=1e-6), w[:2]
+
+
 def test_permute_drops_invalid_entries():
     cfg = S.CONFIGS["tiny"]
     dims = M.dims_for(cfg, tokens=6)
