@@ -34,10 +34,10 @@
  *     finished, in a small counter array the library holds on each GPU (zero at load, and
  *     back to zero at the end of every routing launch).  Each workspace address is given
  *     its own slot of 1024; a workspace keeps its slot while it is among the 1024 most
- *     recently used on that GPU, and forever once a call on it has been captured into a
- *     graph.  So calls that may overlap, having their own workspaces, never share
- *     counters; capturing calls on more than 1024 workspaces of one GPU fails with
- *     MOE_EHIP.
+ *     recently used on that GPU, and, once a call on it has been captured into a graph, until
+ *     moe_workspace_release.  So calls that may overlap, having their own workspaces, never
+ *     share counters; capturing calls on more than 1024 unreleased workspaces of one GPU
+ *     fails with MOE_EHIP.
  *   - Every output is fully overwritten.  tokens == 0 is a valid no-op.
  *   - Errors are status codes, checked on the host BEFORE anything is launched:
  *       MOE_EINVAL       null / misaligned (16 B) pointer, impossible dims
@@ -192,6 +192,16 @@ moe_status moe_forward_noalloc(const moe_dims* dims, const uint16_t* x, const fl
                                const float* bias, const uint16_t* w1, const uint16_t* w3,
                                const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
                                const uint16_t* ws2, uint16_t* out, void* stream);
+
+/* For callers that go through many workspaces over a long run, such as a server that
+ * captures graphs on freshly allocated workspaces: tells the library that the workspace
+ * at `ws` (an address passed to earlier calls) will not be used again, so that its slot of
+ * the router's arrival counts (see the conventions above) may go to another workspace,
+ * including a slot held because a call on `ws` was captured into a graph.  Call it only
+ * when no launch using `ws` is pending and no graph holding such launches will be
+ * replayed.  Host-side bookkeeping only: nothing is launched.  An address the library has
+ * not seen, or NULL, is ignored.  Always MOE_OK. */
+moe_status moe_workspace_release(const void* ws);
 
 /* The MoE half of a transformer block, with the steps either side of the layer fused in
  * ("Kimi K2 · Transformer blocks", MoE transformer block: x_ffn = RMSNorm(x'_n), the

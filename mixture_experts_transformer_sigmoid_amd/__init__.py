@@ -10,7 +10,8 @@ from .binding import (EXPORTS, LIB_PATH, MOE_EHIP, MOE_EINVAL, MOE_ESCRATCH, MOE
                       moe_block_workspace_bytes, moe_combine, moe_dims, moe_expert_down,
                       moe_expert_ffn, moe_expert_gate_up, moe_forward, moe_forward_block,
                       moe_forward_latent, moe_forward_noalloc, moe_latent_workspace_bytes, moe_permute, moe_route,
-                      moe_workspace_bytes, routing_in_workspace, status_str, workspace)
+                      moe_workspace_bytes, moe_workspace_release, routing_in_workspace, status_str,
+                      workspace)
 
 __all__ = ["EXPORTS", "LIB_PATH", "MOE_EHIP", "MOE_EINVAL", "MOE_ESCRATCH", "MOE_EUNSUPPORTED",
            "MOE_EWORKSPACE", "MOE_OK", "NOALLOC_SCRATCH_BYTES", "HSPLIT_MAX_TOP_K", "h_width", "moe_forward_noalloc", "MoeDims", "MoeError", "MoeFp8Weights", "block_workspace", "dims_for",
@@ -19,4 +20,5 @@ __all__ = ["EXPORTS", "LIB_PATH", "MOE_EHIP", "MOE_EINVAL", "MOE_ESCRATCH", "MOE
            "lib", "moe_block_workspace_bytes", "moe_combine", "moe_forward_block",
            "moe_dims", "moe_expert_down", "moe_expert_ffn", "moe_expert_gate_up", "moe_forward",
            "moe_forward_latent", "moe_latent_workspace_bytes", "moe_permute", "moe_route",
-           "moe_workspace_bytes", "routing_in_workspace", "status_str", "workspace"]
+           "moe_workspace_bytes", "moe_workspace_release", "routing_in_workspace", "status_str",
+           "workspace"]

@@ -32,7 +32,8 @@ EXPORTS = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_latent_workspace_bytes", "moe_forward_latent",
            "moe_block_workspace_bytes", "moe_forward_block", "moe_expert_gate_up_fp8",
-           "moe_expert_down_fp8", "moe_forward_fp8", "moe_forward_noalloc")
+           "moe_expert_down_fp8", "moe_forward_fp8", "moe_forward_noalloc",
+           "moe_workspace_release")
 
 
 class MoeDims(ctypes.Structure):
@@ -89,6 +90,7 @@ def lib():
         "moe_combine": [D, _P, _P, _P, _P, _P, _P],
         "moe_forward": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
         "moe_forward_noalloc": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+        "moe_workspace_release": [_P],
         "moe_block_workspace_bytes": [D, ctypes.POINTER(ctypes.c_size_t)],
         "moe_forward_block": [D, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               _S, _P],
@@ -221,6 +223,12 @@ def moe_forward(dims, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, ws, str
     _check(lib().moe_forward(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w1),
                              _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out), wp,
                              wn, _stream(stream)))
+
+
+def moe_workspace_release(ws):
+    """The workspace will not be used again: its slot of the router's arrival counts may go
+    to another workspace (moe.h, moe_workspace_release)."""
+    _check(lib().moe_workspace_release(_ptr(ws)))
 
 
 def moe_forward_noalloc(dims, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, out, stream=None):

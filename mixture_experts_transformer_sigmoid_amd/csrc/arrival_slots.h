@@ -7,7 +7,8 @@
 // gets a slot of its own: a slot stays with its workspace while that workspace is among
 // the kSlots most recently used, and forever once a call on it has been captured into a
 // graph (the graph's launches carry the slot number, so it may never be handed to another
-// workspace).  One table per GPU; the caller serialises access.
+// workspace) until the caller releases the workspace.  One table per GPU; the caller
+// serialises access.
 #pragma once
 
 #include <stdint.h>
@@ -19,8 +20,8 @@ namespace moe {
 template <int kSlots>
 class ArrivalSlotTable {
  public:
-  // The slot of workspace `key`; `pin` (the call is being captured) keeps it for good.
-  // Returns -1 when every slot is held by a graph and `key` has none.
+  // The slot of workspace `key`; `pin` (the call is being captured) keeps it until the
+  // workspace is released.  Returns -1 when every slot is held by a graph and `key` has none.
   int slot(uintptr_t key, bool pin) {
     ++clock_;
     int i;
@@ -48,6 +49,16 @@ class ArrivalSlotTable {
     return i;
   }
 
+  // Workspace `key` will not be used again: its slot, pinned or not, becomes free.
+  void release(uintptr_t key) {
+    const auto it = slot_of_.find(key);
+    if (it == slot_of_.end()) return;
+    const int i = it->second;
+    slot_of_.erase(it);
+    taken_[i] = false;
+    pinned_[i] = false;
+  }
+
  private:
   std::unordered_map<uintptr_t, int> slot_of_;
   uintptr_t key_[kSlots] = {};
@@ -56,5 +67,8 @@ class ArrivalSlotTable {
   bool pinned_[kSlots] = {};
   uint64_t clock_ = 0;
 };
+
+// Frees the slot of workspace `ws` on every GPU (defined with the router; host only).
+void arrival_release(const void* ws);
 
 }  // namespace moe

@@ -5,6 +5,7 @@
 #include <mutex>
 
 #include "../../include/moe.h"
+#include "arrival_slots.h"
 #include "common.h"
 
 // Fixed device scratch of moe_forward_noalloc: each GPU the library runs on holds its own
@@ -401,6 +402,11 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
   (void)hipGetLastError();
   return forward_impl(d, x, nullptr, w_router, bias, w1, w3, w2, ws1, ws3, ws2, nullptr, out, ws,
                       (hipStream_t)stream);
+}
+
+moe_status moe_workspace_release(const void* ws) {
+  if (ws != nullptr) moe::arrival_release(ws);
+  return MOE_OK;
 }
 
 moe_status moe_forward_noalloc(const moe_dims* dims, const uint16_t* x, const float* w_router,

@@ -400,25 +400,33 @@ void select_launch(const float* z_part, int np, int row_parts, int pstride, cons
                        row_parts, pstride, bias, T, E, k, alpha, logits, idx, w);
 }
 
+// The slot tables, one per GPU, and the lock that serialises them.
+std::mutex g_slot_mu;
+std::unordered_map<int, ArrivalSlotTable<kArrivalSlots>> g_slot_tables;
+
 // The arrival slot of a workspace on the device of `s`, where the router will run
 // (ArrivalSlotTable; pinned when the call is being captured into a graph on `s`).
 hipError_t arrival_slot(const void* ws, hipStream_t s, int* slot) {
-  static std::mutex mu;
-  static std::unordered_map<int, ArrivalSlotTable<kArrivalSlots>> tables;
   hipDevice_t dev = 0;
   hipError_t err = hipStreamGetDevice(s, &dev);
   if (err != hipSuccess) return err;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   err = hipStreamIsCapturing(s, &cap);
   if (err != hipSuccess) return err;
-  std::lock_guard<std::mutex> lock(mu);
-  const int i = tables[dev].slot(reinterpret_cast<uintptr_t>(ws), cap != hipStreamCaptureStatusNone);
+  std::lock_guard<std::mutex> lock(g_slot_mu);
+  const int i =
+      g_slot_tables[dev].slot(reinterpret_cast<uintptr_t>(ws), cap != hipStreamCaptureStatusNone);
   if (i < 0) return hipErrorOutOfMemory;
   *slot = i;
   return hipSuccess;
 }
 
 }  // namespace
+
+void arrival_release(const void* ws) {
+  std::lock_guard<std::mutex> lock(g_slot_mu);
+  for (auto& t : g_slot_tables) t.second.release(reinterpret_cast<uintptr_t>(ws));
+}
 
 hipError_t launch_router_small(const uint16_t* x, const RouterNorm* norm, const float* w_r,
                                const float* bias, int64_t T, int d, int E, int k, float alpha,

@@ -18,6 +18,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "mixture_experts_transformer_sigmoid_amd", "csrc")
 SLOTS = 4
 
+# lines "key pin": pin 0 or 1 asks for the slot (printed); pin 2 releases the workspace
+# (prints -2)
 DRIVER = r"""
 #include <stdio.h>
 #include "arrival_slots.h"
@@ -25,7 +27,14 @@ int main() {
   moe::ArrivalSlotTable<%d> t;
   unsigned long long key;
   int pin;
-  while (scanf("%%llu %%d", &key, &pin) == 2) printf("%%d\n", t.slot((uintptr_t)key, pin != 0));
+  while (scanf("%%llu %%d", &key, &pin) == 2) {
+    if (pin == 2) {
+      t.release((uintptr_t)key);
+      printf("-2\n");
+    } else {
+      printf("%%d\n", t.slot((uintptr_t)key, pin != 0));
+    }
+  }
   return 0;
 }
 """ % SLOTS
@@ -78,6 +87,19 @@ def test_graph_slots_are_never_reassigned(driver):
 def test_every_slot_held_by_graphs_refuses_a_new_workspace(driver):
     got = driver([(1, 1), (2, 1), (3, 1), (4, 1), (5, 0), (1, 0)])
     assert len(set(got[:4])) == 4 and got[4] == -1 and got[5] == got[0]
+
+
+def test_released_workspaces_free_their_slots(driver):
+    # four captured workspaces hold every slot; releasing one lets a new workspace in, in
+    # that slot (not pinned: a later workspace may take it over); releasing an unknown
+    # workspace changes nothing; the other captured workspaces keep their slots
+    calls = [(1, 1), (2, 1), (3, 1), (4, 1), (5, 0), (2, 2), (5, 0), (99, 2), (6, 0), (1, 0),
+             (3, 0), (4, 0)]
+    got = driver(calls)
+    assert got[4] == -1 and got[5] == -2
+    assert got[6] == got[1]            # key 5 in key 2's released slot
+    assert got[8] == got[1]            # key 6 takes it over from key 5
+    assert got[9:] == [got[0], got[2], got[3]]
 
 
 def test_random_sequences_keep_live_workspaces_apart(driver):

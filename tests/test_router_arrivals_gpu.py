@@ -218,3 +218,31 @@ def test_graph_replays_between_eager_calls():
         forward(inps[j]["x"], other, ws_graph)               # eager, the graph's workspace
         torch.cuda.synchronize()
         assert torch.equal(other.view(torch.int16), want[j][0].view(torch.int16)), f"eager {i}"
+
+
+def test_released_workspace_and_graph():
+    """A call captured in a graph pins its workspace's slot; after the graph is destroyed
+    and the workspace released (moe_workspace_release), calls on other workspaces and on
+    the released one (which takes a slot again) still route as the oracle does."""
+    cfg = _cfg(100, 64)
+    dims = M.dims_for(cfg)
+    inp = {k: v.to(DEV) for k, v in S.make_inputs(cfg, "cpu", seed=95).items()}
+    ws = M.workspace(dims)
+    idx = torch.empty(100, 8, dtype=torch.int32, device=DEV)
+    w = torch.empty(100, 8, dtype=torch.float32, device=DEV)
+    M.moe_route(dims, inp["x"], inp["w_r"], inp["b"], idx, w, None, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.moe_route(dims, inp["x"], inp["w_r"], inp["b"], idx, w, None, ws)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    _check(idx, w, inp, dims, "graph replay")
+    del g
+    M.moe_workspace_release(ws)
+    M.moe_workspace_release(ws)          # a second release is ignored
+    for j, space in enumerate((M.workspace(dims), ws, M.workspace(dims))):
+        i2, w2 = _route(dims, inp, space)
+        torch.cuda.synchronize()
+        _check(i2, w2, inp, dims, f"after release, call {j}")
