@@ -127,12 +127,14 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* c
  *     if the shared expert is present (d_shared > 0, ws1/ws3 non-NULL), Ts = T rows of
  *     the shared expert for tokens 0..T-1.  Rows p >= offsets[E] of the routed block are
  *     left untouched.  g, u are fp32 accumulations of bf16 products.
- *   H = I: h rounded to bf16.  H = 2I when top_k <= MOE_HSPLIT_MAX_TOP_K: h in two bf16
- *     parts, columns [0, I) = bf16(h), [I, 2I) = bf16(h - bf16(h)) (16 significant bits;
- *     with so few slots per token a single rounding of h would take most of the output's
- *     error budget).  moe_expert_down reads h in the same form.  The FP8 entry points
- *     always use H = I. */
+ *   H = I: h rounded to bf16.  H = 2I when top_k <= MOE_HSPLIT_MAX_TOP_K or d_expert <=
+ *     MOE_HSPLIT_MAX_D_EXPERT: h in two bf16 parts, columns [0, I) = bf16(h), [I, 2I) =
+ *     bf16(h - bf16(h)) (16 significant bits; with so few slots per token, or so few terms
+ *     per output of the down projection, a single rounding of h would take most of the
+ *     output's error budget).  moe_expert_down reads h in the same form.  The FP8 entry
+ *     points always use H = I. */
 #define MOE_HSPLIT_MAX_TOP_K 2
+#define MOE_HSPLIT_MAX_D_EXPERT 128
 moe_status moe_expert_gate_up(const moe_dims* dims, const uint16_t* x, const int32_t* perm_rows,
                               const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                               const uint16_t* ws1, const uint16_t* ws3, uint16_t* h, void* ws,

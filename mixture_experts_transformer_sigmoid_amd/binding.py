@@ -18,14 +18,16 @@ LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = range(6)
 # moe.h's MOE_NOALLOC_SCRATCH_BYTES: the fixed device scratch of moe_forward_noalloc
 NOALLOC_SCRATCH_BYTES = 128 << 20
-# moe.h's MOE_HSPLIT_MAX_TOP_K: up to this top_k the bf16 entry points keep h in two bf16
-# parts, rows of 2I
+# moe.h's MOE_HSPLIT_MAX_TOP_K and MOE_HSPLIT_MAX_D_EXPERT: up to this top_k, or up to this
+# expert width, the bf16 entry points keep h in two bf16 parts, rows of 2I
 HSPLIT_MAX_TOP_K = 2
+HSPLIT_MAX_D_EXPERT = 128
 
 
 def h_width(dims) -> int:
     """Columns per row of h for the bf16 entry points (moe_expert_gate_up / _down)."""
-    return (2 if int(dims.top_k) <= HSPLIT_MAX_TOP_K else 1) * int(dims.d_expert)
+    two = int(dims.top_k) <= HSPLIT_MAX_TOP_K or int(dims.d_expert) <= HSPLIT_MAX_D_EXPERT
+    return (2 if two else 1) * int(dims.d_expert)
 
 # every exported symbol of include/moe.h
 EXPORTS = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",

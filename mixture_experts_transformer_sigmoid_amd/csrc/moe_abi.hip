@@ -64,10 +64,12 @@ size_t router_wsplit_bytes(const moe_dims& d) {
   return 3 * (size_t)moe::router_part_rows(d.n_experts) * d.d_model * 2;
 }
 
-bool hsplit(const moe_dims& d) { return d.top_k <= moe::kHsplitMaxTopK; }
+bool hsplit(const moe_dims& d) {
+  return d.top_k <= moe::kHsplitMaxTopK || d.d_expert <= MOE_HSPLIT_MAX_D_EXPERT;
+}
 
 // Columns of h per row: I, or 2I when h is kept in two bf16 parts (bf16 weights, few slots
-// per token).
+// per token or narrow experts).
 size_t h_width(const moe_dims& d) { return (hsplit(d) ? 2 : 1) * (size_t)d.d_expert; }
 
 struct Layout {

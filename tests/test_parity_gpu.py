@@ -439,8 +439,9 @@ def test_single_expert():
 def test_expert_count_not_a_multiple_of_four(E, T, k):
     # the router GEMM has 3E outputs per token: rows of its fp32 output are neither a
     # whole number of 4-feature groups nor 16-byte aligned (T = 600 takes the wide kernel).
-    # k <= 2 keeps h in two bf16 parts: with a single bf16 rounding of h the schedule
-    # itself exceeds the bar at E = 7, T = 600 (tests/test_precision_schedule.py).
+    # I = 64 keeps h in two bf16 parts at every k: with a single bf16 rounding of h the
+    # schedule itself exceeds the bar at E = 7, T = 600, k <= 2
+    # (tests/test_precision_schedule.py).
     cfg = dict(tokens=T, d_model=128, n_experts=E, top_k=k, d_expert=64, d_shared=64,
                routed_scale=2.827, bias="uniform")
     full_check(cfg, to_dev(S.make_inputs(cfg, "cpu", seed=20 + E)), intermediates=True)
@@ -452,8 +453,9 @@ def test_router_selection_in_place_boundary(E, T):
     from LDS; 17 experts need a second expert tile, and the last workgroup of each token
     block to finish selects from the scores in memory.  Both sides of the boundary, with a
     ragged last block of 16 tokens, every token compared (top-8, so k is at its largest).
-    I = 256: at I = 128 and top-8 the kernels' schedule replayed on the host reaches 0.86 to
-    1.21 of the output bar over 200-300 tokens; here 0.64 to 0.76."""
+    I = 256, where h is rounded once to bf16 (at I = 128 that single rounding would reach
+    0.86 to 1.21 of the output bar over 200-300 tokens, so the kernels keep h in two parts
+    there); here the kernels' schedule replayed on the host reaches 0.64 to 0.76."""
     cfg = dict(tokens=T, d_model=256, n_experts=E, top_k=8, d_expert=256, d_shared=256,
                routed_scale=2.827, bias="uniform")
     full_check(cfg, to_dev(S.make_inputs(cfg, "cpu", seed=60 + E + T)), intermediates=True)

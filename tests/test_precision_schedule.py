@@ -9,9 +9,10 @@ as the reference.
 
 Pins: the rounding points against torch's own bf16 casts on a small layer.  Limits: the
 replay against the exact oracle on seeded inputs of the shapes the GPU tests use, which
-records where the schedule itself stays inside max |err| <= 2e-2 * RMS(out) and where it
-does not (few slots per token, narrow experts: the final rounding and the rounding of h
-then leave no margin).
+records where the schedule with h rounded once stays inside max |err| <= 2e-2 * RMS(out)
+and where it does not (few slots per token, narrow experts: the final rounding and the
+rounding of h then leave no margin), and that the two-part h the kernels use on exactly
+those shapes brings each back inside.
 """
 import math
 
@@ -149,6 +150,12 @@ SHAPES = {
     "d 128, E 1024, I 64, 4096 tokens, k 8": (
         dict(tokens=4096, d_model=128, n_experts=1024, top_k=8, d_expert=64, d_shared=64,
              routed_scale=2.827, bias="uniform"), 0, None, (0.020, 0.030)),
+    "d 128, E 1024, I 128, 4096 tokens, k 8": (
+        dict(tokens=4096, d_model=128, n_experts=1024, top_k=8, d_expert=128, d_shared=128,
+             routed_scale=2.827, bias="uniform"), 0, None, (0.020, 0.030)),
+    "d 128, E 1024, I 256, 4096 tokens, k 8": (
+        dict(tokens=4096, d_model=128, n_experts=1024, top_k=8, d_expert=256, d_shared=256,
+             routed_scale=2.827, bias="uniform"), 0, None, (0.010, 0.020)),
 }
 
 
@@ -162,15 +169,34 @@ def test_kernel_schedule_limits(name):
     assert lo <= ratio < hi, ratio
 
 
-@pytest.mark.parametrize("name", [n for n in SHAPES if SHAPES[n][0]["top_k"] <= 2])
-def test_two_part_h_holds_the_bar_at_few_slots(name):
-    """With at most two slots per token the kernels keep h in two bf16 parts (16
-    significant bits); the replay of that schedule is inside the bar with margin on every
-    shape where the single rounding is not."""
+def _two_part(cfg):
+    """The kernels' rule for h in two bf16 parts (the binding's h_width)."""
+    return cfg["top_k"] <= 2 or cfg["d_expert"] <= 128
+
+
+def test_two_part_rule_matches_the_binding():
+    from mixture_experts_transformer_sigmoid_amd import binding as B
+    for cfg, *_ in SHAPES.values():
+        dims = B.dims_for(cfg)
+        assert B.h_width(dims) == (2 if _two_part(cfg) else 1) * cfg["d_expert"]
+
+
+@pytest.mark.parametrize("name", [n for n in SHAPES if _two_part(SHAPES[n][0])])
+def test_two_part_h_holds_the_bar(name):
+    """With at most two slots per token, or experts at most 128 wide, the kernels keep h
+    in two bf16 parts (16 significant bits); the replay of that schedule is inside the bar
+    on every such shape, also where the single rounding is not."""
     cfg, seed, bias, _ = SHAPES[name]
     ratio = _replay_ratio(cfg, seed, bias, mo.KERNEL_BF16_POINTS_TWO_PART)
     print(f"{name}: two-part-h replay max|err| / RMS = {ratio:.4f}")
-    assert ratio < 0.018, ratio
+    assert ratio < 0.0185, ratio
+
+
+def test_no_shape_left_outside_the_bar():
+    """Every shape whose single-rounding replay misses the bar is one where the kernels
+    use two parts."""
+    for name, (cfg, _, _, (lo, _)) in SHAPES.items():
+        assert lo < 0.020 or _two_part(cfg), name
 
 
 def test_two_part_h_replay_against_torch():
