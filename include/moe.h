@@ -169,7 +169,13 @@ moe_status moe_combine(const moe_dims* dims, const float* y_routed, const int32_
                        void* stream);
 
 /* The whole layer: route, permute, gate/up, down, combine; out [T, d] bf16.
- * Shared expert used iff d_shared > 0 (then ws1, ws3, ws2 must be non-NULL). */
+ * Shared expert used iff d_shared > 0 (then ws1, ws3, ws2 must be non-NULL).
+ * Inside the call the expert outputs (routed rows and the shared expert's) are kept in
+ * the workspace as 24-bit floats: each fp32 result of the down projection with its 8
+ * lowest mantissa bits cleared (16 significant bits, toward zero), 3 bytes per value
+ * instead of 4.  That is 2^-15 of each value at most, against the 2^-9 of the output's
+ * own bf16 rounding.  The output is bit-identical to moe_combine applied to
+ * moe_expert_down's fp32 rows cut the same way. */
 moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_router,
                        const float* bias, const uint16_t* w1, const uint16_t* w3,
                        const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
@@ -183,7 +189,7 @@ moe_status moe_forward(const moe_dims* dims, const uint16_t* x, const float* w_r
  * the module's load until the process ends).  The call itself allocates nothing.
  *   - Limit: moe_workspace_bytes(dims) <= MOE_NOALLOC_SCRATCH_BYTES, else MOE_ESCRATCH
  *     before anything is launched.  At the K2 shape (d 7168, 384 experts, top-8, I 2048,
- *     shared expert) that admits up to 450 tokens.
+ *     shared expert) that admits up to 512 tokens.
  *   - The array of the CURRENT device is used: `stream` must belong to it.
  *   - Every call on one GPU shares that GPU's array.  Calls that overlap on one GPU (on
  *     different streams, or from different host threads without ordering) race on it and
@@ -255,7 +261,8 @@ typedef struct moe_fp8_weights {
 
 /* moe_expert_gate_up / moe_expert_down / moe_forward with FP8 expert weights (`w` is a
  * host pointer to the struct of device pointers); same workspace (moe_workspace_bytes),
- * outputs and semantics otherwise. */
+ * outputs and semantics otherwise (moe_forward_fp8 keeps 24-bit expert rows inside the
+ * call as moe_forward does). */
 moe_status moe_expert_gate_up_fp8(const moe_dims* dims, const uint16_t* x,
                                   const int32_t* perm_rows, const int32_t* offsets,
                                   const moe_fp8_weights* w, uint16_t* h, void* ws,

@@ -3,9 +3,9 @@
 // y_shared; the weighted sum over the k slots in fp32 as in the moe_infer of
 // "Kimi K3 · Latent up-projection".  fp32 accumulation in slot order, one bf16 rounding.
 //
-// Each thread owns 8 consecutive features of one token (32-byte fp32 loads, one 16-byte
-// bf16 store), a block 1,024 features; a token's k expert rows are gathered through
-// inv_perm.
+// Each thread owns 8 consecutive features of one token (32-byte fp32 loads, or 24 bytes
+// of packed 24-bit floats; one 16-byte bf16 store), a block 1,024 features; a token's k
+// expert rows are gathered through inv_perm.
 #include "common.h"
 
 namespace moe {
@@ -16,10 +16,28 @@ constexpr int kCombineThreads = 256;
 // none idle); at the K2 prefill shape 414 us against 437 us with 256 threads per block
 constexpr int kGatherThreads = 128;
 
-template <int KMAX>
+// Features c .. c + 7 of expert row `row` (fp32 rows of d, or with Y24 packed 24-bit rows
+// of 3 d bytes).
+template <bool Y24>
+__device__ __forceinline__ void load_y8(const void* y, int64_t row, int d, int c, f32x4_t& a,
+                                        f32x4_t& b) {
+  if constexpr (Y24) {
+    const F24x4* src = reinterpret_cast<const F24x4*>(static_cast<const uint8_t*>(y) +
+                                                      (row * d + c) * 3);
+    a = unpack_f24x4(src[0]);
+    b = unpack_f24x4(src[1]);
+  } else {
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(y) +
+                                                          row * d + c);
+    a = src[0];
+    b = src[1];
+  }
+}
+
+template <int KMAX, bool Y24>
 __global__ __launch_bounds__(kGatherThreads) void combine_kernel(
-    const float* __restrict__ y_routed, const int32_t* __restrict__ inv,
-    const float* __restrict__ topk_w, const float* __restrict__ y_shared,
+    const void* __restrict__ y_routed, const int32_t* __restrict__ inv,
+    const float* __restrict__ topk_w, const void* __restrict__ y_shared,
     const uint16_t* __restrict__ residual, uint16_t* __restrict__ out, int64_t T, int d, int k) {
   const int nchunk = (d / 8 + kGatherThreads - 1) / kGatherThreads;
   const int64_t t = blockIdx.x / nchunk;
@@ -42,9 +60,7 @@ __global__ __launch_bounds__(kGatherThreads) void combine_kernel(
 #pragma unroll
   for (int s = 0; s < KMAX; ++s) {
     if (p[s] >= 0 && p[s] < slots) {
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y_routed + (int64_t)p[s] * d + c);
-      ra[s] = src[0];
-      rb[s] = src[1];
+      load_y8<Y24>(y_routed, p[s], d, c, ra[s], rb[s]);
     } else {
       ra[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       rb[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -55,11 +71,7 @@ __global__ __launch_bounds__(kGatherThreads) void combine_kernel(
   // is waited for (issued after the sums, they would cost a second round trip)
   f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
   u32x4_t v = {0u, 0u, 0u, 0u};
-  if (y_shared != nullptr) {
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y_shared + t * d + c);
-    sa = src[0];
-    sb = src[1];
-  }
+  if (y_shared != nullptr) load_y8<Y24>(y_shared, t, d, c, sa, sb);
   if (residual != nullptr) v = load16(residual + t * d + c);
   f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -209,14 +221,18 @@ hipError_t launch_combine_rmsnorm(const float* y_routed, const int32_t* inv, con
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float* topk_w,
-                          const float* y_shared, const uint16_t* residual, uint16_t* out,
-                          int64_t T, int d, int k, hipStream_t s) {
+hipError_t launch_combine(const void* y_routed, const int32_t* inv, const float* topk_w,
+                          const void* y_shared, const uint16_t* residual, uint16_t* out,
+                          int64_t T, int d, int k, hipStream_t s, bool y24) {
   if (T <= 0) return hipSuccess;
   const int64_t nchunk = (d / 8 + kGatherThreads - 1) / kGatherThreads;
   dim3 grid((unsigned)(nchunk * T));
-  hipLaunchKernelGGL(combine_kernel<kMaxTopK>, grid, dim3(kGatherThreads), 0, s, y_routed, inv,
-                     topk_w, y_shared, residual, out, T, d, k);
+  if (y24)
+    hipLaunchKernelGGL((combine_kernel<kMaxTopK, true>), grid, dim3(kGatherThreads), 0, s,
+                       y_routed, inv, topk_w, y_shared, residual, out, T, d, k);
+  else
+    hipLaunchKernelGGL((combine_kernel<kMaxTopK, false>), grid, dim3(kGatherThreads), 0, s,
+                       y_routed, inv, topk_w, y_shared, residual, out, T, d, k);
   return hipGetLastError();
 }
 

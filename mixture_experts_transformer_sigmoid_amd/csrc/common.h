@@ -90,6 +90,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Expert output rows inside the layer: 24-bit floats, the upper three bytes of an fp32
+// (its mantissa cut to 15 bits, rounding toward zero: 16 significant bits, fp32's exponent
+// range).  Four consecutive values pack little-endian into 12 bytes, so a row of N (a
+// multiple of 4) takes 3N bytes and each group of four starts on a 4-byte boundary (one
+// dwordx3 access).  Packing is three byte permutes per four values.
+struct __attribute__((aligned(4))) F24x4 {
+  uint32_t w[3];
+};
+
+__device__ __forceinline__ F24x4 pack_f24x4(f32x4_t v) {
+  const uint32_t a = __float_as_uint(v[0]), b = __float_as_uint(v[1]),
+                 c = __float_as_uint(v[2]), d = __float_as_uint(v[3]);
+  F24x4 r;
+  // v_perm_b32: byte selector i picks byte i of {hi:lo} (0-3 lo, 4-7 hi)
+  r.w[0] = __builtin_amdgcn_perm(b, a, 0x05030201u);  // a1 a2 a3 b1
+  r.w[1] = __builtin_amdgcn_perm(c, b, 0x06050302u);  // b2 b3 c1 c2
+  r.w[2] = __builtin_amdgcn_perm(d, c, 0x07060503u);  // c3 d1 d2 d3
+  return r;
+}
+
+__device__ __forceinline__ f32x4_t unpack_f24x4(F24x4 r) {
+  f32x4_t v;
+  v[0] = __uint_as_float(r.w[0] << 8);
+  v[1] = __uint_as_float(((r.w[0] >> 24) | (r.w[1] << 8)) << 8);
+  v[2] = __uint_as_float(((r.w[1] >> 16) | (r.w[2] << 16)) << 8);
+  v[3] = __uint_as_float(r.w[2] & 0xffffff00u);
+  return v;
+}
+
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations, then meets
 // the other waves.  Unlike __syncthreads() it does not drain the wave's outstanding
 // global loads (on CDNA a release fence waits for vmcnt(0)), so register prefetches of
@@ -242,10 +271,12 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
 
 // tiles_ready: the tile list already holds this shape's tiles for the same offsets (built
 // by the permutation or by the gate/up launch just before), so the launch skips building it.
+// y24: y_routed / y_shared hold rows of packed 24-bit floats (3 d bytes each, F24x4 groups)
+// instead of fp32 rows.
 hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
-                       const uint16_t* w2, const uint16_t* ws2, float* y_routed,
-                       float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s,
-                       bool tiles_ready = false);
+                       const uint16_t* w2, const uint16_t* ws2, void* y_routed, void* y_shared,
+                       Tile* tiles, int32_t* ntiles, hipStream_t s, bool tiles_ready = false,
+                       bool y24 = false);
 
 // FP8 (E4M3) expert weights with one fp32 scale per 128 x 128 block; device pointers.
 struct Fp8Weights {
@@ -271,13 +302,15 @@ hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32
                               bool tiles_ready = false);
 
 hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
-                           const Fp8Weights& w, float* y_routed, float* y_shared, Tile* tiles,
-                           int32_t* ntiles, hipStream_t s, bool tiles_ready = false);
+                           const Fp8Weights& w, void* y_routed, void* y_shared, Tile* tiles,
+                           int32_t* ntiles, hipStream_t s, bool tiles_ready = false,
+                           bool y24 = false);
 
 // residual (bf16 [T, d]) may be null; when given it is added before the bf16 rounding.
-hipError_t launch_combine(const float* y_routed, const int32_t* inv, const float* topk_w,
-                          const float* y_shared, const uint16_t* residual, uint16_t* out,
-                          int64_t T, int d, int k, hipStream_t s);
+// y24: the expert rows are packed 24-bit floats (as launch_down writes them with y24).
+hipError_t launch_combine(const void* y_routed, const int32_t* inv, const float* topk_w,
+                          const void* y_shared, const uint16_t* residual, uint16_t* out,
+                          int64_t T, int d, int k, hipStream_t s, bool y24 = false);
 
 // out[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps) * gain), fp64 arithmetic.
 hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, uint16_t* out, int64_t T, int d,

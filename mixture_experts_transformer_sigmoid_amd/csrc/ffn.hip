@@ -546,9 +546,9 @@ hipError_t launch_gate_up(const FfnShape& sh, const uint16_t* x, const int32_t* 
 }
 
 hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
-                       const uint16_t* w2, const uint16_t* ws2, float* y_routed,
-                       float* y_shared, Tile* tiles, int32_t* ntiles, hipStream_t s,
-                       bool tiles_ready) {
+                       const uint16_t* w2, const uint16_t* ws2, void* y_routed, void* y_shared,
+                       Tile* tiles, int32_t* ntiles, hipStream_t s, bool tiles_ready,
+                       bool y24) {
   const bool wide = use_wide(sh, kWideRowsBf16);
   const int BM = wide ? kWideBM : kSkinnyBM;
   if (!tiles_ready) {
@@ -564,8 +564,8 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.B3 = nullptr;
   a.S1 = ws2;
   a.S3 = nullptr;
-  a.Y = y_routed;
-  a.Ys = y_shared;
+  a.Y = static_cast<float*>(y_routed);
+  a.Ys = static_cast<float*>(y_shared);
   a.tiles = tiles;
   a.ntiles = ntiles;
   a.k = sh.k;
@@ -574,14 +574,25 @@ hipError_t launch_down(const FfnShape& sh, const uint16_t* h, const int32_t* off
   a.K = sh.hsplit ? 2 * sh.I : sh.I;
   a.wk = sh.hsplit ? sh.I : 0;
   a.E = sh.E;
-  if (wide)
-    launch_wide<kF32>(grid_for(sh, BM, kWideBNDown, a.N), s, a);
-  else if (sh.hsplit)
-    hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32, true>),
-                       grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32>),
-                       grid_for(sh, BM, 64 * kSkinnyNF, a.N), dim3(256), 0, s, a);
+  const dim3 gw = grid_for(sh, BM, kWideBNDown, a.N), gs = grid_for(sh, BM, 64 * kSkinnyNF, a.N);
+  if (wide) {
+    if (y24) launch_wide<kF24>(gw, s, a);
+    else launch_wide<kF32>(gw, s, a);
+  } else if (sh.hsplit) {
+    if (y24)
+      hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF24, true>), gs, dim3(256),
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32, true>), gs, dim3(256),
+                         0, s, a);
+  } else {
+    if (y24)
+      hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF24>), gs, dim3(256), 0, s,
+                         a);
+    else
+      hipLaunchKernelGGL((ffn_skinny_kernel<kSkinnyNF, kSkinnyKU, kF32>), gs, dim3(256), 0, s,
+                         a);
+  }
   return hipGetLastError();
 }
 

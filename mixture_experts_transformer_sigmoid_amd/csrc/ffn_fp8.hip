@@ -531,8 +531,8 @@ hipError_t launch_gate_up_fp8(const FfnShape& sh, const uint16_t* x, const int32
 }
 
 hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t* offsets,
-                           const Fp8Weights& w, float* y_routed, float* y_shared, Tile* tiles,
-                           int32_t* ntiles, hipStream_t s, bool tiles_ready) {
+                           const Fp8Weights& w, void* y_routed, void* y_shared, Tile* tiles,
+                           int32_t* ntiles, hipStream_t s, bool tiles_ready, bool y24) {
   const bool wide = use_wide(sh, kWideRowsFp8);
   const int BM = wide ? kF8LdsBM : kSkinnyBM;
   if (!tiles_ready) {
@@ -542,16 +542,25 @@ hipError_t launch_down_fp8(const FfnShape& sh, const uint16_t* h, const int32_t*
   FfnArgs a = fp8_args(sh, w, false, tiles, ntiles);
   a.A = h;
   a.a_rows = sh.T * sh.k + (sh.shared ? sh.T : 0);
-  a.Y = y_routed;
-  a.Ys = y_shared;
+  a.Y = static_cast<float*>(y_routed);
+  a.Ys = static_cast<float*>(y_shared);
   a.N = sh.d;
   a.K = sh.I;
-  if (wide)
-    hipLaunchKernelGGL(ffn_lds_fp8_kernel<kF32>, grid_for(sh, BM, kF8LdsFeatDown, a.N),
-                       dim3(64 * kF8LdsWaves), 0, s, a);
-  else
-    hipLaunchKernelGGL((ffn_skinny_fp8_kernel<kSkinnyF8DnNF, kSkinnyF8DnKB, kF32>),
-                       grid_for(sh, BM, 64 * kSkinnyF8DnNF, a.N), dim3(256), 0, s, a);
+  const dim3 gw = grid_for(sh, BM, kF8LdsFeatDown, a.N),
+             gs = grid_for(sh, BM, 64 * kSkinnyF8DnNF, a.N);
+  if (wide) {
+    if (y24)
+      hipLaunchKernelGGL(ffn_lds_fp8_kernel<kF24>, gw, dim3(64 * kF8LdsWaves), 0, s, a);
+    else
+      hipLaunchKernelGGL(ffn_lds_fp8_kernel<kF32>, gw, dim3(64 * kF8LdsWaves), 0, s, a);
+  } else {
+    if (y24)
+      hipLaunchKernelGGL((ffn_skinny_fp8_kernel<kSkinnyF8DnNF, kSkinnyF8DnKB, kF24>), gs,
+                         dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((ffn_skinny_fp8_kernel<kSkinnyF8DnNF, kSkinnyF8DnKB, kF32>), gs,
+                         dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ enum Epi : int {
   kF32 = 1,      // fp32 rows into Y (grouped rows) or Ys (the last group's rows)
   kBF16 = 2,     // bf16 rows into C
   kAddBF16 = 3,  // bf16(acc + R[row]) into C, R fp32 with the same layout
+  kF24 = 4,      // packed 24-bit float rows (3 N bytes, F24x4 groups) into Y / Ys
 };
 
 struct FfnArgs {
@@ -27,8 +28,8 @@ struct FfnArgs {
   const uint16_t* S1;     // shared weights [N, K] (ws1, or ws2 for down)
   const uint16_t* S3;     // shared ws3 (gate/up)
   uint16_t* C;            // gate/up: h [rows, N] bf16
-  float* Y;               // down: y_routed [T*k, N] fp32
-  float* Ys;              // down: y_shared [T, N] fp32
+  float* Y;               // down: y_routed [T*k, N] fp32 (kF24: 3 N bytes per row)
+  float* Ys;              // down: y_shared [T, N] fp32 (kF24: 3 N bytes per row)
   const Tile* tiles;
   const int32_t* ntiles;
   int32_t k;              // slots per token (gate/up gather: token = slot / k)
@@ -116,6 +117,15 @@ __device__ __forceinline__ void store_gateup(const FfnArgs& a, int64_t p, int nn
   }
 }
 
+// Four outputs (features nn .. nn + 3, nn a multiple of 4) of grouped row p as packed
+// 24-bit floats: routed rows into Y, the shared expert's into Ys, 3 N bytes per row.
+__device__ __forceinline__ void store_f24_row4(const FfnArgs& a, int64_t p, int nn, f32x4_t v) {
+  const int64_t N = a.N;
+  uint8_t* row = p < a.routed_rows ? reinterpret_cast<uint8_t*>(a.Y) + p * 3 * N
+                                   : reinterpret_cast<uint8_t*>(a.Ys) + (p - a.routed_rows) * 3 * N;
+  *reinterpret_cast<F24x4*>(row + 3 * nn) = pack_f24x4(v);
+}
+
 // Store four consecutive outputs (features nn .. nn+3) of grouped row p.  Every output
 // row is a whole number of 4-feature groups: N is a multiple of 64 for every bf16 output
 // (d, I and the latent width are), and the fp32 outputs are the down GEMM's (N = d) and
@@ -131,6 +141,8 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
     float* yrow = p < a.routed_rows ? a.Y + p * N
                                     : a.Ys + (p - a.routed_rows) * (a.ldc ? a.ldc : N) + col0;
     *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
+  } else if (EPI == kF24) {
+    store_f24_row4(a, p, nn, v);
   } else {
     if (EPI == kAddBF16) v += *reinterpret_cast<const f32x4_t*>(a.R + p * N + nn);
     u32x2_t packed;
@@ -148,7 +160,8 @@ __device__ __forceinline__ void store4(const FfnArgs& a, int64_t p, int nn, f32x
 // fragment at a time in its own part of the (by then idle) activation buffers (32 rows of
 // its outputs in fp32, the SwiGLU already applied: 16 KiB at most) and reads it back along
 // the rows, so that one store instruction covers whole rows: with four fragments 2 x 512 B
-// (fp32, 128 outputs) or 4 x 128 B (bf16 h, 64 outputs), with two 4 x 256 B or 8 x 64 B.
+// (fp32, 128 outputs) or 4 x 128 B (bf16 h, 64 outputs), with two 4 x 256 B or 8 x 64 B
+// (24-bit rows: 4 x 192 B).
 //
 // Staging layout: row r (0..31) holds FW / 4 pieces of 4 outputs; piece p sits in slot
 // r (FW / 4) + (p ^ (r & 7)), so the 8 lanes that the LDS serves together (8 rows, one
@@ -161,6 +174,8 @@ __device__ __forceinline__ void store_row4(const FfnArgs& a, int64_t p, int nn, 
     float* yrow = p < a.routed_rows ? a.Y + p * N
                                     : a.Ys + (p - a.routed_rows) * (a.ldc ? a.ldc : N) + col0;
     *reinterpret_cast<f32x4_t*>(yrow + nn) = v;
+  } else if constexpr (EPI == kF24) {
+    store_f24_row4(a, p, nn, v);
   } else {
     if constexpr (EPI == kAddBF16) v += *reinterpret_cast<const f32x4_t*>(a.R + p * N + nn);
     u32x2_t packed;

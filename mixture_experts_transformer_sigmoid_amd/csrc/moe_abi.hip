@@ -105,7 +105,9 @@ Layout layout(const moe_dims& d) {
   L.tiles = take(max_tiles * sizeof(Tile));
   L.ntiles = take(4);
   L.h = take(rows * h_width(d) * 2);
-  L.y = take(rows * (size_t)d.d_model * 4);
+  // the layer's expert outputs, routed rows then the shared expert's, as packed 24-bit
+  // floats (3 bytes per value)
+  L.y = take(rows * (size_t)d.d_model * 3);
   L.total = off;
   return L;
 }
@@ -177,19 +179,22 @@ moe_status gate_up_impl(const moe_dims& d, const uint16_t* x, const int32_t* per
                                         tiles_ready));
 }
 
+// y24: y_routed / y_shared are the layer's packed 24-bit rows (the workspace's y region),
+// else the caller's fp32 rows.
 moe_status down_impl(const moe_dims& d, const uint16_t* h, const int32_t* offsets,
-                     const uint16_t* w2, const uint16_t* ws2, float* y_routed,
-                     float* y_shared, void* ws, hipStream_t s, bool tiles_ready = false) {
+                     const uint16_t* w2, const uint16_t* ws2, void* y_routed, void* y_shared,
+                     void* ws, hipStream_t s, bool tiles_ready = false, bool y24 = false) {
   const Layout L = layout(d);
   return hip_status(moe::launch_down(ffn_shape(d), h, offsets, w2, ws2, y_routed, y_shared,
                                      at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles), s,
-                                     tiles_ready));
+                                     tiles_ready, y24));
 }
 
-moe_status combine_impl(const moe_dims& d, const float* y_routed, const int32_t* inv,
-                        const float* w, const float* y_shared, uint16_t* out, hipStream_t s) {
+moe_status combine_impl(const moe_dims& d, const void* y_routed, const int32_t* inv,
+                        const float* w, const void* y_shared, uint16_t* out, hipStream_t s,
+                        bool y24 = false) {
   return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, nullptr, out, d.tokens,
-                                        d.d_model, d.top_k, s));
+                                        d.d_model, d.top_k, s, y24));
 }
 
 bool shared_ptrs_ok(const moe_dims& d, const void* a, const void* b) {
@@ -319,15 +324,16 @@ moe_status forward_impl(const moe_dims& d, const uint16_t* x, const moe::RouterN
   int32_t* perm = at<int32_t>(ws, L.perm);
   int32_t* inv = at<int32_t>(ws, L.inv);
   uint16_t* h = at<uint16_t>(ws, L.h);
-  float* y_routed = at<float>(ws, L.y);
-  float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
+  uint8_t* y_routed = at<uint8_t>(ws, L.y);
+  uint8_t* y_shared =
+      has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model * 3 : nullptr;
   const moe::TileSpec ts = moe::ffn_tile_spec(ffn_shape(d));
   const uint16_t* x_in = nullptr;
   MOE_TRY(route_permute(d, x, norm, w_router, bias, ws, route_bufs(L), &ts, s, &x_in));
   MOE_TRY(gate_up_impl(d, x_in, perm, offsets, w1, w3, ws1, ws3, h, ws, s, true));
-  MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s, true));
+  MOE_TRY(down_impl(d, h, offsets, w2, ws2, y_routed, y_shared, ws, s, true, true));
   return hip_status(moe::launch_combine(y_routed, inv, w, y_shared, residual, out, d.tokens,
-                                        d.d_model, d.top_k, s));
+                                        d.d_model, d.top_k, s, true));
 }
 
 // ---------------------------------------------------------------------- FP8 weights
@@ -481,8 +487,9 @@ moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float*
   int32_t* perm = at<int32_t>(ws, L.perm);
   int32_t* inv = at<int32_t>(ws, L.inv);
   uint16_t* h = at<uint16_t>(ws, L.h);
-  float* y_routed = at<float>(ws, L.y);
-  float* y_shared = has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model : nullptr;
+  uint8_t* y_routed = at<uint8_t>(ws, L.y);
+  uint8_t* y_shared =
+      has_shared(d) ? y_routed + (size_t)d.tokens * d.top_k * d.d_model * 3 : nullptr;
   const moe::Fp8Weights fw = fp8_of(*w);
   const moe::TileSpec ts = moe::ffn_tile_spec_fp8(ffn_shape_fp8(d));
   const uint16_t* x_in = nullptr;
@@ -492,8 +499,8 @@ moe_status moe_forward_fp8(const moe_dims* dims, const uint16_t* x, const float*
                                              s, true)));
   MOE_TRY(hip_status(moe::launch_down_fp8(ffn_shape_fp8(d), h, offsets, fw, y_routed, y_shared,
                                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
-                                          s, true)));
-  return combine_impl(d, y_routed, inv, gw, y_shared, out, s);
+                                          s, true, true)));
+  return combine_impl(d, y_routed, inv, gw, y_shared, out, s, true);
 }
 
 moe_status moe_block_workspace_bytes(const moe_dims* dims, size_t* bytes) {

@@ -256,6 +256,17 @@ def permute(topk_idx, n_experts):
             perm.astype(np.int32), inv.astype(np.int32))
 
 
+def cut_sig16(v):
+    """Keep 16 significant bits of each value and drop the rest (rounding toward zero), as
+    a 24-bit float row holds an fp32 result: sign, 8-bit exponent and the top 15 stored
+    mantissa bits.  From the definition, in float64: with |v| = m 2^e, m in [0.5, 1), the
+    kept value is trunc(m 2^16) 2^(e - 16).  Zero, NaN and infinities pass unchanged."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    out = np.ldexp(np.trunc(m * 65536.0) / 65536.0, e)
+    return np.where(np.isfinite(v), out, v)
+
+
 # ------------------------------------------------------------------------------- FFN
 def swiglu(x_rows, w1, w3, w2, bf16_points=()):
     """One SwiGLU expert on a set of rows: g = x W1, u = x W3, a = g sigma(g), h = a u,
@@ -282,18 +293,21 @@ def swiglu(x_rows, w1, w3, w2, bf16_points=()):
 #   "h"           the SwiGLU hidden row, before the down projection
 #   "h2"          the same row kept as two bf16 parts, bf16(h) + bf16(h - bf16(h))
 #   "expert_out"  each expert's output row E_i
+#   "y24"         each expert's output row and the shared expert's output cut to 16
+#                 significant bits toward zero (cut_sig16; the 24-bit rows of the layer)
 #   "y_routed"    the gate-weighted sum over the k slots
 #   "y_shared"    the shared expert's output
 #   "out"         the layer output
 # PAGE_BF16_POINTS: where a bf16 copy of the module rounds ("Kimi K3 · Latent
 # up-projection", moe_infer: expert outputs in the module dtype, weighted sum taken in
 # fp32 and cast back; the shared output added in the module dtype).
-# KERNEL_BF16_POINTS: the HIP path's schedule (h is the down GEMM's bf16 operand; expert
-# outputs, the weighted sum and the shared output stay fp32; one final rounding), and
-# KERNEL_BF16_POINTS_TWO_PART the same with h in two bf16 parts (top_k <= 2).
+# KERNEL_BF16_POINTS: the HIP layer's schedule (h is the down GEMM's bf16 operand; expert
+# outputs and the shared output kept with 16 significant bits; the weighted sum in fp32;
+# one final rounding), and KERNEL_BF16_POINTS_TWO_PART the same with h in two bf16 parts
+# (top_k <= 2 or I <= 128).
 PAGE_BF16_POINTS = ("h", "expert_out", "y_routed", "y_shared", "out")
-KERNEL_BF16_POINTS = ("h", "out")
-KERNEL_BF16_POINTS_TWO_PART = ("h2", "out")
+KERNEL_BF16_POINTS = ("h", "y24", "out")
+KERNEL_BF16_POINTS_TWO_PART = ("h2", "y24", "out")
 
 
 def _expert_getter(w1, w3, w2):
@@ -347,6 +361,8 @@ def moe_sparse(x, w_r, b, top_k, alpha=ALPHA_K2, *, get_expert=None, w1=None, w3
         out_e = swiglu(x[rows[[i for i, _ in pairs]]], w1e, w3e, w2e, bf16_points)
         if "expert_out" in bf16_points:
             out_e = round_bf16(out_e)
+        elif "y24" in bf16_points:
+            out_e = cut_sig16(out_e)
         for n, pr in enumerate(pairs):
             per_slot[pr] = out_e[n]
     d = next(iter(per_slot.values())).shape[0] if per_slot else _f64(w_r).shape[1]
@@ -356,6 +372,8 @@ def moe_sparse(x, w_r, b, top_k, alpha=ALPHA_K2, *, get_expert=None, w1=None, w3
             y_r[i] = y_r[i] + gates[i, j] * per_slot[(i, int(j))]
     if shared is not None:
         y_s = swiglu(x[rows], *shared, bf16_points)
+        if "y24" in bf16_points:
+            y_s = cut_sig16(y_s)
     else:
         y_s = np.zeros_like(y_r)
     if "y_routed" in bf16_points:

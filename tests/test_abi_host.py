@@ -264,8 +264,8 @@ def test_noalloc_host_checks():
     assert L.moe_forward_noalloc(ctypes.byref(d), None, P, P, P, P, P, P, P, P, P, None) == M.MOE_EINVAL
     assert L.moe_forward_noalloc(ctypes.byref(d), P, P, P, Q, P, P, P, P, P, P, None) == M.MOE_EINVAL
     # the largest K2 batch that fits, and the first that does not
-    assert M.moe_workspace_bytes(_k2(450)) <= B.NOALLOC_SCRATCH_BYTES < M.moe_workspace_bytes(_k2(451))
-    big = _k2(451)
+    assert M.moe_workspace_bytes(_k2(512)) <= B.NOALLOC_SCRATCH_BYTES < M.moe_workspace_bytes(_k2(513))
+    big = _k2(513)
     assert L.moe_forward_noalloc(ctypes.byref(big), P, P, P, P, P, P, P, P, P, P, None) == M.MOE_ESCRATCH
     assert "MOE_NOALLOC_SCRATCH_BYTES" in M.status_str(M.MOE_ESCRATCH)
     z = _k2(0)

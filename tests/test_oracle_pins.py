@@ -436,6 +436,22 @@ def test_round_bf16_against_torch_and_ties():
     assert s[0] == np.inf and s[1] == -np.inf and np.isnan(s[2])
 
 
+def test_cut_sig16_against_fp32_bit_masking():
+    """cut_sig16 on fp32 values equals clearing the 8 lowest stored mantissa bits of the
+    fp32 pattern (what a 24-bit float keeps of it), over normal fp32 values of both signs
+    and every magnitude; plus hand cases of the grid at 1.0 (spacing 2^-15)."""
+    rng = np.random.default_rng(23)
+    v = (rng.standard_normal(200_000) * np.exp(rng.uniform(-80, 80, 200_000))).astype(np.float32)
+    v = v[np.abs(v) >= np.finfo(np.float32).tiny]
+    masked = (v.view(np.uint32) & np.uint32(0xFFFFFF00)).view(np.float32).astype(np.float64)
+    assert np.array_equal(mo.cut_sig16(v.astype(np.float64)), masked)
+    t = mo.cut_sig16(np.array([1 + 2.0 ** -15, 1 + 2.0 ** -16, 1 + 2.0 ** -15 + 2.0 ** -16,
+                               -(1 + 2.0 ** -16), 2 - 2.0 ** -20, 0.0, -0.0]))
+    assert list(t) == [1 + 2.0 ** -15, 1.0, 1 + 2.0 ** -15, -1.0, 2 - 2.0 ** -15, 0.0, 0.0]
+    s = mo.cut_sig16(np.array([np.inf, -np.inf, np.nan]))
+    assert s[0] == np.inf and s[1] == -np.inf and np.isnan(s[2])
+
+
 def _block(L, x_res, gain, eps=1e-6, **kw):
     args = dict(w1=L["w1"], w3=L["w3"], w2=L["w2"], ws1=L["ws1"], ws3=L["ws3"], ws2=L["ws2"])
     args.update(kw)

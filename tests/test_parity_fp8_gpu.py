@@ -69,11 +69,17 @@ def run_split(cfg, inp):
     M.moe_expert_down_fp8(dims, h, offs, w, y, ys, ws)
     out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
     M.moe_combine(dims, y, inv, gw, ys, out)
+    # the layer keeps its expert rows as 24-bit floats (the low 8 mantissa bits cleared):
+    # the same combine over those values is what moe_forward_fp8 must return
+    out24 = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y24 = (y.view(torch.int32) & -256).view(torch.float32)
+    ys24 = (ys.view(torch.int32) & -256).view(torch.float32) if ys is not None else None
+    M.moe_combine(dims, y24, inv, gw, ys24, out24)
     fw = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
     M.moe_forward_fp8(dims, inp["x"], inp["w_r"], inp["b"], w, fw, ws)
     torch.cuda.synchronize()
     return dict(idx=idx, w=gw, counts=counts, offs=offs, perm=perm, inv=inv, h=h, y=y, ys=ys,
-                out=out, fw=fw)
+                out=out, out24=out24, fw=fw)
 
 
 def check_bound(got, want, lim, what):
@@ -95,7 +101,8 @@ def full_check(cfg, inp, sample=None, seed=0, intermediates=True, inter_tokens=2
     for name in ("h", "y", "ys", "out", "fw"):
         if g[name] is not None:
             assert bool(torch.isfinite(g[name].float()).all()), f"{name}: elements never written"
-    assert torch.equal(g["fw"].view(torch.int16), g["out"].view(torch.int16)), "forward != split"
+    assert torch.equal(g["fw"].view(torch.int16), g["out24"].view(torch.int16)), \
+        "forward != split with 24-bit expert rows"
     again = run_split(cfg, inp)
     assert torch.equal(again["out"].view(torch.int16), g["out"].view(torch.int16)), "not deterministic"
     x = f64(inp["x"])

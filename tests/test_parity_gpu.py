@@ -68,6 +68,26 @@ def run_split(cfg, inp, dims=None):
                 y_r=y_r, y_s=y_s, out=out, dims=dims)
 
 
+def trunc24(y):
+    """The layer entry points keep expert outputs as 24-bit floats: each fp32 value with
+    its 8 lowest mantissa bits cleared (16 significant bits, toward zero).  In place."""
+    if y is not None:
+        y.view(torch.int32).bitwise_and_(-256)
+    return y
+
+
+def split_as_forward(g, dims):
+    """What moe_forward must return for the split path's routing and expert outputs:
+    moe_combine over the fp32 rows of moe_expert_down cut to the 24-bit values that the
+    layer's own rows hold (the same GEMMs, the same sums in the same order)."""
+    out = torch.full((dims.tokens, dims.d_model), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y_r = trunc24(g["y_r"].clone())
+    y_s = trunc24(g["y_s"].clone()) if g.get("y_s") is not None else None
+    M.moe_combine(dims, y_r, g["inv"], g["w"], y_s, out)
+    torch.cuda.synchronize()
+    return out
+
+
 def run_forward(cfg, inp, dims=None, keep_ws=False):
     dims = dims or M.dims_for(cfg)
     ws = M.workspace(dims)
@@ -310,7 +330,9 @@ def full_check(cfg, inp, dims=None, sample=None, intermediates=False, seed=0):
             16 if dims.d_model <= 1024 else 2)
         check_intermediates(g, inp, dims, toks[:n_int])
     fw, ws = run_forward(cfg, inp, dims, keep_ws=True)
-    assert torch.equal(fw.view(torch.int16), g["out"].view(torch.int16)), "forward != split path"
+    assert torch.equal(fw.view(torch.int16), split_as_forward(g, dims).view(torch.int16)), \
+        "forward != split path with 24-bit expert rows"
+    check_out(f64(fw)[toks], o["out"], f"forward out ({toks.size} of {T} tokens)")
     # the fused call's own routing and permutation, left at the front of its workspace
     rw = M.routing_in_workspace(dims, ws)
     for mine, theirs in (("idx", "topk_idx"), ("w", "topk_w"), ("counts", "counts"),

@@ -22,7 +22,8 @@ import mixture_experts_transformer_sigmoid_amd as M
 import synth_inputs as S
 from oracle import moe_oracle as O
 from test_parity_gpu import (DEV, GAP, assert_all_written, check_intermediates, check_out,
-                             check_routing, f64, run_forward, run_split, say, to_dev)
+                             check_routing, f64, run_forward, run_split, say, split_as_forward,
+                             to_dev, trunc24)
 
 pytestmark = pytest.mark.gpu
 
@@ -82,7 +83,8 @@ def check_e1024(cfg, seed):
     # h within one bf16 ulp of bf16(silu(g) u), Y within the fp32 accumulation bound
     check_intermediates(g, inp, dims, toks[:16])
     fw = run_forward(cfg, inp, dims)
-    assert torch.equal(fw.view(torch.int16), g["out"].view(torch.int16)), "forward != split path"
+    assert torch.equal(fw.view(torch.int16), split_as_forward(g, dims).view(torch.int16)), \
+        "forward != split path with 24-bit expert rows"
 
 
 # ------------------------------------------------------------------ largest T
@@ -130,7 +132,11 @@ def large_case(cfg, inp, n_route, n_out, getter, shared):
                      tokens=pick, routing=ref)
     out_rows = f64(g["out"].index_select(0, torch.from_numpy(rows[pick]).to(DEV)))
     check_out(out_rows, o["out"])
-    out_split = g["out"]
+    # the split path's expert rows cut to 24 bits in place (no second copy at this size),
+    # combined again: what the layer's own 24-bit rows must give
+    out_split = torch.full_like(g["out"], float("nan"))
+    M.moe_combine(dims, trunc24(g["y_r"]), g["inv"], g["w"], trunc24(g["y_s"]), out_split)
+    torch.cuda.synchronize()
     for name in ("h", "y_r", "y_s", "z"):
         g[name] = None
     del g

@@ -1,9 +1,10 @@
 """The oracle's bf16-points diagnostic mode, and what the HIP path's precision schedule can
 hold (no GPU).
 
-The HIP path rounds the SwiGLU hidden row h to bf16 (the down GEMM's MFMA operand) and
-the layer output once; everything between stays fp32.  moe_sparse(..., bf16_points=
-KERNEL_BF16_POINTS) replays that schedule in float64.  It is a diagnostic: it attributes
+The HIP layer rounds the SwiGLU hidden row h to bf16 (the down GEMM's MFMA operand),
+keeps each expert's output row with 16 significant bits (its 24-bit rows) and rounds the
+layer output once; the sums stay fp32.  moe_sparse(..., bf16_points=KERNEL_BF16_POINTS)
+replays that schedule in float64.  It is a diagnostic: it attributes
 differences between the GPU and the exact oracle, and it never replaces the exact oracle
 as the reference.
 
@@ -35,6 +36,13 @@ def _bf(t):
     return t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
 
 
+def _cut16(t):
+    """16 significant bits toward zero, with torch's frexp (the rounding itself is pinned
+    against fp32 bit masking in tests/test_oracle_pins.py)."""
+    m, e = torch.frexp(t)
+    return torch.ldexp(torch.trunc(m * 65536.0) / 65536.0, e)
+
+
 def _layer(seed, T=40, d=64, E=6, I=32, k=2):
     rng = np.random.default_rng(seed)
     r = lambda *s: rng.standard_normal(s)  # noqa: E731
@@ -62,12 +70,16 @@ def _torch_schedule(L, points):
         ye = mlp(L["w1"][e], L["w3"][e], L["w2"][e])
         if "expert_out" in points:
             ye = _bf(ye)
+        elif "y24" in points:
+            ye = _cut16(ye)
         g = torch.zeros(x.shape[0], dtype=torch.float64)
         for j in range(L["k"]):
             hit = torch.from_numpy(r["topk_idx"][:, j] == e)
             g[hit] = torch.from_numpy(r["topk_w"][:, j])[hit]
         y_r = y_r + g[:, None] * ye
     y_s = mlp(L["ws1"], L["ws3"], L["ws2"])
+    if "y24" in points:
+        y_s = _cut16(y_s)
     if "y_routed" in points:
         y_r = _bf(y_r)
     if "y_shared" in points:
@@ -84,7 +96,7 @@ def _oracle_schedule(L, points):
 
 
 @pytest.mark.parametrize("points", [(), mo.KERNEL_BF16_POINTS, mo.PAGE_BF16_POINTS, ("h",),
-                                    ("expert_out",), ("y_routed", "y_shared")])
+                                    ("expert_out",), ("y24",), ("y_routed", "y_shared")])
 def test_bf16_points_against_torch_casts(points):
     L = _layer(41)
     got = _oracle_schedule(L, points)

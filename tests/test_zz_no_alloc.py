@@ -79,7 +79,7 @@ def test_noalloc_k2_decode(k2_weights):
 
 def test_noalloc_rejects_beyond_scratch():
     cfg = S.CONFIGS["k2_decode"]
-    dims = M.dims_for(cfg, tokens=451)
+    dims = M.dims_for(cfg, tokens=513)
     x = torch.empty((8, 16), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(M.MoeError) as ei:
         M.moe_forward_noalloc(dims, x, x, x, x, x, x, x, x, x, x)
