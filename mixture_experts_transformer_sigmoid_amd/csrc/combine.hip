@@ -108,14 +108,15 @@ __global__ __launch_bounds__(kGatherThreads) void combine_kernel(
 
 // Latent variant: u_hat[t] = RMSNorm(sum_slot G * Y[inv[t, slot]]) with unit gain, eps as
 // given ("Kimi K3 · Latent up-projection": the routed sum on the latent width is
-// normalised before the up-projection).  One workgroup per token; each thread keeps up
-// to CPT 4-wide fp32 chunks of the sum, the sum of squares is reduced in a fixed tree
+// normalised before the up-projection).  Y holds the routed rows as packed 24-bit floats
+// (3 L bytes each).  One workgroup per token; each thread keeps up to CPT 4-wide fp32
+// chunks of the sum, the sum of squares is reduced in a fixed tree
 // order (deterministic), and the row is scaled by 1/sqrt(mean + eps).  u_hat is the
 // up-projection's MFMA operand: rounded to bf16 once (rows of L), or with TWO in two bf16
 // parts, [bf16(u_hat) | bf16(rest)] (rows of 2L).
 template <int KMAX, int CPT, bool TWO>
 __global__ __launch_bounds__(kCombineThreads) void combine_rmsnorm_kernel(
-    const float* __restrict__ y_routed, const int32_t* __restrict__ inv,
+    const void* __restrict__ y_routed, const int32_t* __restrict__ inv,
     const float* __restrict__ topk_w, uint16_t* __restrict__ out, int64_t T, int L, int k,
     float eps) {
   __shared__ float wsum[kCombineThreads / 64];
@@ -146,8 +147,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rmsnorm_kernel(
   for (int j = 0; j < CPT; ++j) {
     const int c = min(tid + kCombineThreads * j, nch - 1);
 #pragma unroll
-    for (int s = 0; s < KMAX; ++s)
-      v[j][s] = *reinterpret_cast<const f32x4_t*>(y_routed + (int64_t)max(p[s], 0) * L + 4 * c);
+    for (int s = 0; s < KMAX; ++s) {
+      const int64_t e = (int64_t)max(p[s], 0) * L + 4 * c;  // first element of the piece
+      v[j][s] = unpack_f24x4(
+          *reinterpret_cast<const F24x4*>(static_cast<const uint8_t*>(y_routed) + e * 3));
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   f32x4_t acc[CPT];
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rmsnorm_kernel(
 
 }  // namespace
 
-hipError_t launch_combine_rmsnorm(const float* y_routed, const int32_t* inv, const float* topk_w,
+hipError_t launch_combine_rmsnorm(const void* y_routed, const int32_t* inv, const float* topk_w,
                                   uint16_t* out, int64_t T, int L, int k, float eps,
                                   bool two_part, hipStream_t s) {
   if (T <= 0) return hipSuccess;

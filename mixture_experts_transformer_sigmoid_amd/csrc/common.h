@@ -318,7 +318,8 @@ hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, uint16_t* out, i
 
 // u = RMSNorm(sum_slot topk_w * y_routed[inv]) over L features (L <= 8192): out[t] =
 // bf16(u) (rows of L), or with two_part [bf16(u) | bf16(u - bf16(u))] (rows of 2L).
-hipError_t launch_combine_rmsnorm(const float* y_routed, const int32_t* inv, const float* topk_w,
+// y_routed rows are packed 24-bit floats (3 L bytes each), as launch_down writes them with y24.
+hipError_t launch_combine_rmsnorm(const void* y_routed, const int32_t* inv, const float* topk_w,
                                   uint16_t* out, int64_t T, int L, int k, float eps,
                                   bool two_part, hipStream_t s);
 constexpr int kMaxLatent = 8192;

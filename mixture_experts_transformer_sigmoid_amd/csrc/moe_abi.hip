@@ -249,7 +249,7 @@ LatentLayout latent_layout(const moe_dims& d, int32_t L) {
   P.lat = take(T * (size_t)L * 2);
   P.h = take(slots * h_width(d) * 2);
   P.hs = take(has_shared(d) ? T * h_width(d) * 2 : 0);
-  P.y = take(slots * (size_t)L * 4);
+  P.y = take(slots * (size_t)L * 3);  // the routed experts' rows, packed 24-bit floats
   P.uhat = take(T * (size_t)L * 2 * (L <= moe::kLatentTwoPartMaxL ? 2 : 1));  // one or two parts
   P.ys = take(has_shared(d) ? T * (size_t)d.d_model * 4 : 0);
   P.total = off;
@@ -683,7 +683,7 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
   int32_t* ntiles = at<int32_t>(ws, P.ntiles);
   uint16_t* lat = at<uint16_t>(ws, P.lat);
   uint16_t* h = at<uint16_t>(ws, P.h);
-  float* y = at<float>(ws, P.y);
+  uint8_t* y = at<uint8_t>(ws, P.y);
   uint16_t* uhat = at<uint16_t>(ws, P.uhat);
   // router on the full-width input ("Kimi K3 · Latent up-projection": the gate scores
   // hidden_states before the down-projection), and the permutation
@@ -698,7 +698,7 @@ moe_status moe_forward_latent(const moe_dims* dims, int32_t d_latent, const uint
   MOE_TRY(hip_status(moe::launch_gate_up(rsh, lat, perm, offsets, w1, w3, nullptr, nullptr, h,
                                          tiles, ntiles, s)));
   MOE_TRY(hip_status(
-      moe::launch_down(rsh, h, offsets, w2, nullptr, y, nullptr, tiles, ntiles, s, true)));
+      moe::launch_down(rsh, h, offsets, w2, nullptr, y, nullptr, tiles, ntiles, s, true, true)));
   // gate-weighted sum over the slots, RMSNorm (eps from the config), bf16
   const bool uhat2 = L <= moe::kLatentTwoPartMaxL;
   MOE_TRY(hip_status(
